@@ -1,0 +1,153 @@
+"""Workload shapes for block top-k sparse decode attention.
+
+The shapes stand in for the decode workloads the Kinetics pages measure
+(rebuttal page "Kinetics: Rethinking Test-Time Scaling Law", "W2 & Q2:
+Real-world latency benchmarks": Qwen3 decode against a 32K-token KV cache,
+Best-of-N batches; answer Q4: budgets of 1024 tokens as (block, top-k) =
+(16,64), (32,32), (64,16)).  Head layouts follow the Qwen3 8B / 14B / 32B
+attention shapes (32/8, 40/8, 64/8 query/KV heads, head_dim 128).
+
+No arithmetic of the method lives here: only sizes, seeds and byte counts
+used to report bandwidth.
+"""
+from dataclasses import dataclass, field, replace
+from typing import List
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    hq: int
+    hkv: int
+    ctx_len: int
+    block: int
+    topk: int
+    dtype: str            # "f32" or "bf16"
+    seed: int
+    head_dim: int = 128
+    heavy_blocks: int = 0  # blocks per pair whose keys are pushed toward q
+    t_cap: int = 0         # cache capacity in tokens (0: equal to ctx_len)
+
+    @property
+    def gqa(self) -> int:
+        return self.hq // self.hkv
+
+    @property
+    def cap(self) -> int:
+        return self.t_cap or self.ctx_len
+
+    @property
+    def nb(self) -> int:
+        return (self.ctx_len + self.block - 1) // self.block
+
+    @property
+    def nb_cap(self) -> int:
+        return (self.cap + self.block - 1) // self.block
+
+    @property
+    def esize(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def pairs(self) -> int:
+        return self.batch * self.hkv
+
+    @property
+    def k_eff(self) -> int:
+        return min(self.topk, self.nb)
+
+    # ---- algorithmic bytes (what the method has to move, per call) ----
+    def bytes_summary_scan(self) -> int:
+        return self.pairs * self.nb * self.head_dim * self.esize
+
+    def kept_tokens(self) -> int:
+        """Tokens of the kept blocks that lie inside the context, per pair
+        (the blocks are the top k; for the byte model take the last block as
+        partial only when it must be kept, i.e. when every block is kept)."""
+        if self.k_eff >= self.nb:
+            return self.ctx_len
+        return self.k_eff * self.block
+
+    def bytes_gather(self) -> int:
+        return self.pairs * self.kept_tokens() * self.head_dim * self.esize * 2
+
+    def bytes_q_out(self) -> int:
+        return self.batch * self.hq * self.head_dim * self.esize * 2
+
+    def bytes_update(self) -> int:
+        """Newest-block summary update of one decode step: read the newest
+        block's keys (at most one block) and write one summary row."""
+        newest = self.ctx_len - (self.nb - 1) * self.block
+        return self.pairs * (newest + 1) * self.head_dim * self.esize
+
+    def bytes_sparse_step(self) -> int:
+        return (self.bytes_summary_scan() + self.bytes_gather() + self.bytes_q_out()
+                + self.bytes_update())
+
+    def bytes_dense(self) -> int:
+        return (self.pairs * self.ctx_len * self.head_dim * self.esize * 2
+                + self.bytes_q_out())
+
+    def cache_bytes(self) -> int:
+        return 2 * self.pairs * self.cap * self.head_dim * self.esize
+
+    def summary_bytes(self) -> int:
+        return self.pairs * self.nb_cap * self.head_dim * self.esize
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "batch": self.batch, "hq": self.hq, "hkv": self.hkv,
+                "head_dim": self.head_dim, "ctx_len": self.ctx_len, "block": self.block,
+                "topk_blocks": self.topk, "budget_tokens": self.topk * self.block,
+                "dtype": self.dtype, "heavy_blocks": self.heavy_blocks, "seed": self.seed}
+
+    def scaled(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+TINY = Workload("tiny-gqa4-ctx4096-f32", batch=1, hq=8, hkv=2, ctx_len=4096, block=16, topk=32,
+                dtype="f32", seed=1001)
+QWEN3_8B = Workload("qwen3-8b-longcot-b32-ctx32k", batch=32, hq=32, hkv=8, ctx_len=32768,
+                    block=16, topk=64, dtype="bf16", seed=1002)
+QWEN3_14B = Workload("qwen3-14b-b64-ctx32k-heavy", batch=64, hq=40, hkv=8, ctx_len=32768,
+                     block=32, topk=64, dtype="bf16", seed=1003, heavy_blocks=4)
+QWEN3_32B = Workload("qwen3-32b-b32-ctx64k", batch=32, hq=64, hkv=8, ctx_len=65536, block=64,
+                     topk=64, dtype="bf16", seed=1004)
+
+MAIN = [TINY, QWEN3_8B, QWEN3_14B, QWEN3_32B]
+
+SWEEP_BATCH = (8, 32, 128)
+SWEEP_CTX = (8192, 32768, 131072)
+SWEEP_BLOCK = (16, 32, 64)
+SWEEP_BUDGET = (256, 1024, 4096, 8192)
+
+
+def sweep() -> List[Workload]:
+    """Budget / length sweep on the Qwen3-32B head layout (64q/8kv, d=128,
+    bf16): every (batch, ctx, block, token budget) point in row-major order,
+    then the keep-every-block (dense-equivalent) point of each
+    (batch, ctx, block)."""
+    pts = []
+    p = 0
+    for b in SWEEP_BATCH:
+        for L in SWEEP_CTX:
+            for B in SWEEP_BLOCK:
+                for budget in SWEEP_BUDGET:
+                    pts.append(Workload(f"sweep-b{b}-ctx{L}-blk{B}-budget{budget}", batch=b, hq=64,
+                                        hkv=8, ctx_len=L, block=B, topk=budget // B,
+                                        dtype="bf16", seed=5000 + p))
+                    p += 1
+    for b in SWEEP_BATCH:
+        for L in SWEEP_CTX:
+            for B in SWEEP_BLOCK:
+                pts.append(Workload(f"sweep-b{b}-ctx{L}-blk{B}-allblocks", batch=b, hq=64, hkv=8,
+                                    ctx_len=L, block=B, topk=L // B, dtype="bf16", seed=5000 + p))
+                p += 1
+    return pts
+
+
+def by_name(name: str) -> Workload:
+    for w in MAIN + sweep():
+        if w.name == name:
+            return w
+    raise KeyError(name)

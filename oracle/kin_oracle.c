@@ -1,0 +1,460 @@
+/*
+ * kin_oracle.c -- plain, slow CPU oracle for block top-k sparse decode
+ * attention, in fp64.
+ *
+ * TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg may load this library.  It
+ * shares no source, header, table or helper with the HIP library: it has
+ * its own dtype codes, its own bf16 rounding and its own loops.
+ *
+ * What it computes (sources are the pages this project follows):
+ *   - "Kinetics: Memory-Aware Test-Time Scaling" (skill summary page),
+ *     section "Implementation", module BlockTopKAttention: the attention
+ *     scores are q.k / sqrt(head_dim), a block is ranked by the mean score
+ *     of its tokens, torch.topk keeps the best blocks, everything else is
+ *     masked to a huge negative number before softmax, and the output is
+ *     softmax(scores) . V.
+ *   - "Kinetics: Rethinking Test-Time Scaling Law" (OpenReview rebuttal
+ *     page), answer Q4 "KV block size and grouping strategy": the blocks
+ *     are KV blocks of a fixed size and the KV budget is
+ *     (block size) x (top-k blocks), e.g. (16,64), (32,32), (64,16) for a
+ *     budget of 1024 tokens; answer "W2. Alternative sparse attention
+ *     variants": Block-TopK keeps the whole KV cache and retrieves from it
+ *     at every decode step.
+ *   - Same rebuttal, "W2 & Q2: Real-world latency benchmarks": the method
+ *     runs as batched decode against a 32K-token KV cache, one new query
+ *     per sequence per step.
+ *
+ * Readings of points the pages leave open (each is listed with its reason
+ * in the design notes of the repository):
+ *   R1 block representative = mean key of the block.  For one query this
+ *      is exactly the page's "mean score per block" (q.mean(k) = mean(q.k)).
+ *   R2 GQA: one selection per (sequence, KV head); the group's score of a
+ *      block is the SUM over its query heads of q_h . s_j.  Query head h
+ *      reads KV head floor(h / gqa).
+ *   R3 the 1/sqrt(d) factor is applied in the softmax only; it does not
+ *      change the ranking, so the selection score omits it.
+ *   R4 summaries are stored in the cache dtype: fp64 mean, rounded to fp32
+ *      (RNE), and for bf16 caches rounded again fp32 -> bf16 (RNE).
+ *   R5 selection scores are fp64; ties go to the LOWER block index; the
+ *      kept indices are returned ascending, padded with -1 when k > nb.
+ *   R6 a partial last block (ctx_len % block != 0) is averaged over its
+ *      valid tokens only; tokens at or beyond ctx_len never take part.
+ *   R7 the new token is already appended: the query attends to [0, ctx_len).
+ *   R8 masking to -1e9 is read as exclusion (exp(-1e9) is 0 in fp64).
+ *
+ * Layouts (row-major, contiguous):
+ *   q, out      [batch][hkv*gqa][head_dim]
+ *   K, V        [batch][hkv][t_cap][head_dim]
+ *   S           [batch][hkv][nb_cap][head_dim], nb_cap = ceil(t_cap/block)
+ *   scores      [batch][hkv][nb_cap]          (fp64)
+ *   idx         [batch][hkv][k]               (int32)
+ * dtype 0 = IEEE binary32, dtype 1 = bfloat16 (upper half of a binary32).
+ *
+ * Every entry point returns 0 on success and a negative number when an
+ * argument is out of range.  Threads split work by (sequence, KV head)
+ * pair only; the arithmetic inside a pair is a plain sequential loop.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define KOR_F32 0
+#define KOR_BF16 1
+
+/* ------------------------------------------------------------------ */
+/* element access                                                      */
+/* ------------------------------------------------------------------ */
+
+/* Exact value of element i of an fp32 or bf16 array, as a double. */
+static double kor_get(const void *base, int dtype, size_t i)
+{
+    if (dtype == KOR_F32)
+        return (double)((const float *)base)[i];
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* binary32 -> bfloat16 with round-to-nearest, ties to even: keep the top
+ * 16 bits, and add one unit in their last place when the dropped 16 bits
+ * are above half, or exactly half with an odd kept part.  A carry out of
+ * the mantissa moves into the exponent, which is the correct result
+ * (up to and including overflow to infinity).  Inputs are finite. */
+static uint16_t kor_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint32_t keep = u >> 16;
+    uint32_t drop = u & 0xFFFFu;
+    if (drop > 0x8000u || (drop == 0x8000u && (keep & 1u)))
+        keep += 1u;
+    return (uint16_t)keep;
+}
+
+/* Store the double x as element i of an fp32 or bf16 array: first the C
+ * conversion double -> float (round to nearest even), then for bf16 the
+ * second rounding above. */
+static void kor_put(void *base, int dtype, size_t i, double x)
+{
+    float f = (float)x;
+    if (dtype == KOR_F32)
+        ((float *)base)[i] = f;
+    else
+        ((uint16_t *)base)[i] = kor_bf16_rne(f);
+}
+
+/* ------------------------------------------------------------------ */
+/* a tiny thread pool over (sequence, KV head) pairs                    */
+/* ------------------------------------------------------------------ */
+
+typedef void (*kor_pair_fn)(const void *ctx, int pair);
+
+typedef struct {
+    kor_pair_fn fn;
+    const void *ctx;
+    int npairs, nthreads, tid;
+} kor_job;
+
+static void *kor_worker(void *arg)
+{
+    const kor_job *job = (const kor_job *)arg;
+    for (int p = job->tid; p < job->npairs; p += job->nthreads)
+        job->fn(job->ctx, p);
+    return NULL;
+}
+
+static void kor_run_pairs(int npairs, int nthreads, kor_pair_fn fn, const void *ctx)
+{
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > npairs)
+        nthreads = npairs;
+    if (nthreads <= 1) {
+        for (int p = 0; p < npairs; ++p)
+            fn(ctx, p);
+        return;
+    }
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    kor_job *jobs = (kor_job *)malloc(sizeof(kor_job) * (size_t)nthreads);
+    char *live = (char *)calloc((size_t)nthreads, 1);
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t].fn = fn;
+        jobs[t].ctx = ctx;
+        jobs[t].npairs = npairs;
+        jobs[t].nthreads = nthreads;
+        jobs[t].tid = t;
+        if (pthread_create(&th[t], NULL, kor_worker, &jobs[t]) == 0)
+            live[t] = 1;
+        else
+            kor_worker(&jobs[t]); /* no thread: do its share here */
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (live[t])
+            pthread_join(th[t], NULL);
+    free(live);
+    free(th);
+    free(jobs);
+}
+
+static int kor_nblocks(int len, int block) { return (len + block - 1) / block; }
+
+/* ------------------------------------------------------------------ */
+/* O1: block summaries (mean key per block), reading R1, R4, R6         */
+/* ------------------------------------------------------------------ */
+
+typedef struct {
+    const void *K;
+    void *S;          /* rounded summaries in dtype, or NULL */
+    double *S64;      /* unrounded fp64 means, or NULL */
+    int dtype, hkv, t_cap, d, ctx_len, block, nb_cap, j0, j1;
+} kor_sum_ctx;
+
+static void kor_sum_pair(const void *vctx, int pair)
+{
+    const kor_sum_ctx *c = (const kor_sum_ctx *)vctx;
+    const size_t kbase = (size_t)pair * (size_t)c->t_cap * (size_t)c->d;
+    const size_t sbase = (size_t)pair * (size_t)c->nb_cap * (size_t)c->d;
+    for (int j = c->j0; j < c->j1; ++j) {
+        int t0 = j * c->block;
+        int n = c->ctx_len - t0;
+        if (n > c->block)
+            n = c->block;
+        for (int ch = 0; ch < c->d; ++ch) {
+            double sum = 0.0;
+            for (int t = t0; t < t0 + n; ++t) /* ascending token order */
+                sum += kor_get(c->K, c->dtype, kbase + (size_t)t * c->d + ch);
+            double mean = sum / (double)n;
+            size_t o = sbase + (size_t)j * c->d + ch;
+            if (c->S)
+                kor_put(c->S, c->dtype, o, mean);
+            if (c->S64)
+                c->S64[o] = mean;
+        }
+    }
+}
+
+/* Recompute, from scratch, every block that intersects
+ * [t_begin, t_end) and [0, ctx_len).  S (dtype) and/or S64 (fp64, the
+ * unrounded means) may be NULL.  Blocks outside the range are untouched. */
+int kor_block_summary(const void *K, void *S, double *S64, int dtype, int batch, int hkv,
+                      int t_cap, int head_dim, int ctx_len, int block, int t_begin, int t_end,
+                      int nthreads)
+{
+    if (!K || (!S && !S64) || batch < 1 || hkv < 1 || head_dim < 1 || block < 1)
+        return -1;
+    if (dtype != KOR_F32 && dtype != KOR_BF16)
+        return -2;
+    if (ctx_len < 1 || ctx_len > t_cap || t_begin < 0 || t_end < t_begin || t_end > t_cap)
+        return -3;
+    if (t_end > ctx_len)
+        t_end = ctx_len;
+    if (t_begin >= t_end)
+        return 0;
+    kor_sum_ctx c = {K, S, S64, dtype, hkv, t_cap, head_dim, ctx_len, block,
+                     kor_nblocks(t_cap, block), t_begin / block, (t_end - 1) / block + 1};
+    kor_run_pairs(batch * hkv, nthreads, kor_sum_pair, &c);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* O2: block scores, reading R2, R3, R5                                  */
+/* ------------------------------------------------------------------ */
+
+typedef struct {
+    const void *q, *S;
+    double *scores;
+    int dtype, hkv, gqa, d, nb_cap, nb;
+} kor_score_ctx;
+
+static void kor_score_pair(const void *vctx, int pair)
+{
+    const kor_score_ctx *c = (const kor_score_ctx *)vctx;
+    const int b = pair / c->hkv, g = pair % c->hkv;
+    const int hq = c->hkv * c->gqa;
+    for (int j = 0; j < c->nb; ++j) {
+        double sigma = 0.0;
+        for (int h = g * c->gqa; h < (g + 1) * c->gqa; ++h) {
+            size_t qo = ((size_t)b * hq + h) * c->d;
+            size_t so = ((size_t)pair * c->nb_cap + j) * c->d;
+            for (int ch = 0; ch < c->d; ++ch)
+                sigma += kor_get(c->q, c->dtype, qo + ch) * kor_get(c->S, c->dtype, so + ch);
+        }
+        if (sigma == 0.0) /* -0.0 and +0.0 are one score */
+            sigma = 0.0;
+        c->scores[(size_t)pair * c->nb_cap + j] = sigma;
+    }
+}
+
+/* scores[b][g][j] = sum over the group's heads h and channels c of
+ * q[b][h][c] * S[b][g][j][c], for j < nb = ceil(ctx_len / block). */
+int kor_block_score(const void *q, const void *S, double *scores, int dtype, int batch, int hkv,
+                    int gqa, int head_dim, int nb_cap, int nb, int nthreads)
+{
+    if (!q || !S || !scores || batch < 1 || hkv < 1 || gqa < 1 || head_dim < 1)
+        return -1;
+    if (dtype != KOR_F32 && dtype != KOR_BF16)
+        return -2;
+    if (nb < 1 || nb > nb_cap)
+        return -3;
+    kor_score_ctx c = {q, S, scores, dtype, hkv, gqa, head_dim, nb_cap, nb};
+    kor_run_pairs(batch * hkv, nthreads, kor_score_pair, &c);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* O3: top-k selection, reading R5                                      */
+/* ------------------------------------------------------------------ */
+
+typedef struct {
+    double s;
+    int j;
+} kor_cand;
+
+/* higher score first; equal scores: lower block index first */
+static int kor_cand_cmp(const void *pa, const void *pb)
+{
+    const kor_cand *a = (const kor_cand *)pa, *b = (const kor_cand *)pb;
+    if (a->s > b->s)
+        return -1;
+    if (a->s < b->s)
+        return 1;
+    return (a->j > b->j) - (a->j < b->j);
+}
+
+static int kor_int_cmp(const void *pa, const void *pb)
+{
+    int a = *(const int *)pa, b = *(const int *)pb;
+    return (a > b) - (a < b);
+}
+
+typedef struct {
+    const double *scores;
+    int32_t *idx;
+    double *gap;
+    int nb_cap, nb, k;
+} kor_topk_ctx;
+
+static void kor_topk_pair(const void *vctx, int pair)
+{
+    const kor_topk_ctx *c = (const kor_topk_ctx *)vctx;
+    const double *s = c->scores + (size_t)pair * c->nb_cap;
+    kor_cand *cand = (kor_cand *)malloc(sizeof(kor_cand) * (size_t)c->nb);
+    int *keep = (int *)malloc(sizeof(int) * (size_t)c->nb);
+    double amax = 0.0;
+    for (int j = 0; j < c->nb; ++j) {
+        cand[j].s = s[j];
+        cand[j].j = j;
+        if (fabs(s[j]) > amax)
+            amax = fabs(s[j]);
+    }
+    qsort(cand, (size_t)c->nb, sizeof(kor_cand), kor_cand_cmp);
+    int keff = c->k < c->nb ? c->k : c->nb;
+    for (int i = 0; i < keff; ++i)
+        keep[i] = cand[i].j;
+    qsort(keep, (size_t)keff, sizeof(int), kor_int_cmp);
+    int32_t *out = c->idx + (size_t)pair * c->k;
+    for (int i = 0; i < c->k; ++i)
+        out[i] = i < keff ? keep[i] : -1;
+    if (c->gap) {
+        /* margin certificate: distance between the last kept and the first
+         * dropped score, relative to the largest |score| of the pair */
+        double g;
+        if (keff >= c->nb)
+            g = INFINITY;
+        else if (amax == 0.0)
+            g = 0.0;
+        else
+            g = (cand[keff - 1].s - cand[keff].s) / amax;
+        c->gap[pair] = g;
+    }
+    free(cand);
+    free(keep);
+}
+
+/* idx[b][g][0..k): the min(k, nb) blocks with the largest scores (ties to
+ * the lower index), ascending, then -1.  gap (may be NULL): per pair
+ * (score of the last kept - score of the first dropped) / max |score|,
+ * +inf when every block is kept. */
+int kor_block_topk(const double *scores, int32_t *idx, double *gap, int batch, int hkv,
+                   int nb_cap, int nb, int k, int nthreads)
+{
+    if (!scores || !idx || batch < 1 || hkv < 1)
+        return -1;
+    if (nb < 1 || nb > nb_cap || k < 1)
+        return -3;
+    kor_topk_ctx c = {scores, idx, gap, nb_cap, nb, k};
+    kor_run_pairs(batch * hkv, nthreads, kor_topk_pair, &c);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* O4: exact softmax attention over the kept tokens, reading R3, R6-R8  */
+/* ------------------------------------------------------------------ */
+
+typedef struct {
+    const void *q, *K, *V;
+    const int32_t *idx; /* NULL: dense, every token in [0, ctx_len) */
+    double *out;
+    int dtype, hkv, gqa, d, t_cap, ctx_len, block, k;
+} kor_attn_ctx;
+
+static void kor_attn_pair(const void *vctx, int pair)
+{
+    const kor_attn_ctx *c = (const kor_attn_ctx *)vctx;
+    const int b = pair / c->hkv, g = pair % c->hkv;
+    const int hq = c->hkv * c->gqa;
+    const size_t kv = (size_t)pair * c->t_cap * c->d;
+
+    /* the kept token list, in ascending block order */
+    int ntok = 0;
+    size_t cap = c->idx ? (size_t)c->k * (size_t)c->block : (size_t)c->ctx_len;
+    int *tok = (int *)malloc(sizeof(int) * cap);
+    if (!c->idx) {
+        for (int t = 0; t < c->ctx_len; ++t)
+            tok[ntok++] = t;
+    } else {
+        const int32_t *sel = c->idx + (size_t)pair * c->k;
+        for (int i = 0; i < c->k; ++i) {
+            if (sel[i] < 0)
+                continue;
+            for (int t = sel[i] * c->block; t < (sel[i] + 1) * c->block && t < c->ctx_len; ++t)
+                tok[ntok++] = t;
+        }
+    }
+    double *z = (double *)malloc(sizeof(double) * (size_t)(ntok > 0 ? ntok : 1));
+    const double scale = 1.0 / sqrt((double)c->d);
+
+    for (int h = g * c->gqa; h < (g + 1) * c->gqa; ++h) {
+        const size_t qo = ((size_t)b * hq + h) * c->d;
+        double *o = c->out + qo;
+        double m = -INFINITY;
+        for (int i = 0; i < ntok; ++i) {
+            double dot = 0.0;
+            for (int ch = 0; ch < c->d; ++ch)
+                dot += kor_get(c->q, c->dtype, qo + ch) *
+                       kor_get(c->K, c->dtype, kv + (size_t)tok[i] * c->d + ch);
+            z[i] = dot * scale;
+            if (z[i] > m)
+                m = z[i];
+        }
+        double den = 0.0;
+        for (int ch = 0; ch < c->d; ++ch)
+            o[ch] = 0.0;
+        for (int i = 0; i < ntok; ++i) {
+            double p = exp(z[i] - m);
+            den += p;
+            for (int ch = 0; ch < c->d; ++ch)
+                o[ch] += p * kor_get(c->V, c->dtype, kv + (size_t)tok[i] * c->d + ch);
+        }
+        for (int ch = 0; ch < c->d; ++ch)
+            o[ch] = ntok > 0 ? o[ch] / den : 0.0;
+    }
+    free(z);
+    free(tok);
+}
+
+/* out[b][h][:] (fp64, unrounded) = softmax attention of query head h over
+ * the tokens of its KV head's kept blocks (idx, k entries per pair, -1
+ * entries skipped), or over every token in [0, ctx_len) when idx is NULL. */
+int kor_decode_attention(const void *q, const void *K, const void *V, const int32_t *idx, int k,
+                         double *out, int dtype, int batch, int hkv, int gqa, int head_dim,
+                         int t_cap, int ctx_len, int block, int nthreads)
+{
+    if (!q || !K || !V || !out || batch < 1 || hkv < 1 || gqa < 1 || head_dim < 1 || block < 1)
+        return -1;
+    if (dtype != KOR_F32 && dtype != KOR_BF16)
+        return -2;
+    if (ctx_len < 1 || ctx_len > t_cap || (idx && k < 1))
+        return -3;
+    if (idx) {
+        const int nb = kor_nblocks(ctx_len, block);
+        for (size_t i = 0; i < (size_t)batch * hkv * k; ++i)
+            if (idx[i] >= nb)
+                return -4;
+    }
+    kor_attn_ctx c = {q, K, V, idx, out, dtype, hkv, gqa, head_dim, t_cap, ctx_len, block, k};
+    kor_run_pairs(batch * hkv, nthreads, kor_attn_pair, &c);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* helpers for the tests                                                */
+/* ------------------------------------------------------------------ */
+
+/* Round n doubles to dtype with the same two-step rule as the summaries. */
+int kor_round(const double *x, void *out, size_t n, int dtype)
+{
+    if (!x || !out)
+        return -1;
+    if (dtype != KOR_F32 && dtype != KOR_BF16)
+        return -2;
+    for (size_t i = 0; i < n; ++i)
+        kor_put(out, dtype, i, x[i]);
+    return 0;
+}
+
+int kor_version(void) { return 1; }
