@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Benchmark: block top-k sparse decode attention, one layer, one MI355X.
+
+A step is one whole sparse decode step of one layer for a batch of
+sequences, run through the C ABI of libkin.so back to back on one stream:
+newest-block summary update -> block scores -> top-k -> sparse attention
+(+ split combine).  Steps rotate over several independent layers (each with
+its own cache, summaries and queries) so that consecutive steps never find
+the previous step's bytes in the 256 MB Infinity Cache, as in a real decode
+where the other layers run in between.  Inputs are resident in HBM before
+the timed region starts.
+
+Prints ONE JSON line (rank 0).  value = queries/s/layer = batch / step time.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from block_top_sparse_amd import binding as kb  # noqa: E402
+from block_top_sparse_amd import synth, workloads  # noqa: E402
+from block_top_sparse_amd.buffers import LayerBuffers  # noqa: E402
+
+METRIC = "sparse decode-attn queries/s/layer + achieved HBM GB/s vs peak (1 GPU)"
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def make_layers(w, n_layers, with_dense):
+    layers = []
+    for l in range(n_layers):
+        inp = synth.make_inputs(w, device="cuda", seed=w.seed + 7919 * l)
+        bufs = LayerBuffers(w, with_dense=with_dense)
+        kb.kin_block_summary_update(bufs.desc, inp["K"], bufs.S, 0, w.ctx_len)  # prefill
+        layers.append((inp, bufs))
+        torch.cuda.synchronize()
+        log(f"layer {l}: cache {w.cache_bytes() / 2**30:.2f} GiB ready")
+    return layers
+
+
+def sparse_step(w, inp, bufs, ev=None):
+    d, L = bufs.desc, w.ctx_len
+    if ev is not None:
+        ev[0].record()
+    kb.kin_block_summary_update(d, inp["K"], bufs.S, L - 1, L)
+    if ev is not None:
+        ev[1].record()
+    kb.kin_block_score(d, inp["q"], bufs.S, bufs.scores)
+    if ev is not None:
+        ev[2].record()
+    kb.kin_block_topk(d, bufs.scores, bufs.k, bufs.idx)
+    if ev is not None:
+        ev[3].record()
+    kb.kin_sparse_decode_attn(d, inp["q"], inp["K"], inp["V"], bufs.idx, bufs.k, bufs.out,
+                              bufs.ws)
+    if ev is not None:
+        ev[4].record()
+
+
+def dense_step(w, inp, bufs, ev=None):
+    kb.kin_dense_decode_attn(bufs.desc, inp["q"], inp["K"], inp["V"], bufs.out_dense,
+                             bufs.ws_dense)
+
+
+def time_steps(fn, layers, steps, warmup, n_events=0):
+    """fn(inp, bufs, events_or_None); returns (ms per step, per-stage ms)."""
+    for s in range(warmup):
+        fn(*layers[s % len(layers)], None)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_events)] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for s in range(steps):
+        fn(*layers[s % len(layers)], evs[s] if n_events else None)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    stage_ms = []
+    if n_events:
+        for i in range(n_events - 1):
+            stage_ms.append(sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)) / steps)
+    return total_ms / steps, stage_ms
+
+
+def cpu_baseline(w, layer, max_seqs):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    newest-block summary update + scores + selection + attention for the
+    first `max_seqs` sequences of one layer (all their KV heads), summaries
+    prebuilt outside the timed region."""
+    import oracle
+
+    inp, bufs = layer
+    n = min(max_seqs, w.batch)
+    nthreads = oracle.default_threads()
+    q = inp["q"][:n].cpu()
+    K = inp["K"][:n].cpu()
+    V = inp["V"][:n].cpu()
+    S, _ = oracle.block_summary(K, w.block, w.ctx_len, nthreads=nthreads)
+    t0 = time.perf_counter()
+    S, _ = oracle.block_summary(K, w.block, w.ctx_len, t_begin=w.ctx_len - 1, t_end=w.ctx_len,
+                                S=S, nthreads=nthreads)
+    sc = oracle.block_score(q, S, w.gqa, w.nb, nthreads=nthreads)
+    idx, _ = oracle.block_topk(sc, w.nb, w.topk, nthreads=nthreads)
+    oracle.decode_attention(q, K, V, w.gqa, w.ctx_len, w.block, idx=idx, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "queries/s/layer", "cores": nthreads, "kind": "oracle",
+            "sample": f"{n} of {w.batch} sequences x {w.hkv} KV heads of one layer "
+                      f"(summary update + scores + top-k + attention, fp64), {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=workloads.QWEN3_8B.name)
+    ap.add_argument("--layers", type=int, default=0, help="layers rotated (0: auto)")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=32)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the path shards by sequence or KV head with no "
+              "exchange, and multi-GPU runs are not part of this build (use --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    w = workloads.by_name(args.workload)
+    torch.cuda.set_device(0)
+    n_layers = args.layers or max(2, min(8, math.ceil(2**30 / w.bytes_sparse_step())))
+    cap_layers = max(1, int(150 * 2**30 // (w.cache_bytes() + w.summary_bytes())))
+    n_layers = min(n_layers, cap_layers)
+    log(f"workload {w.name}: {n_layers} layers rotated, step bytes "
+        f"{w.bytes_sparse_step() / 2**20:.1f} MiB")
+    layers = make_layers(w, n_layers, with_dense=not args.no_dense)
+
+    ms, stages = time_steps(lambda i, b, e: sparse_step(w, i, b, e), layers, args.steps,
+                            args.warmup, n_events=5)
+    step_bytes = w.bytes_sparse_step()
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    stage_names = ["summary_update", "block_score", "block_topk", "sparse_attn"]
+    stages_us = {n: round(t * 1000, 2) for n, t in zip(stage_names, stages)}
+
+    # dominant kernel: the longest of the two streaming stages
+    plan_ws = kb.kin_sparse_ws_bytes(layers[0][1].desc, w.topk)
+    if stages[1] >= stages[3]:
+        kern, kms = "k_block_score", stages[1]
+        kbytes = w.bytes_summary_scan() + w.batch * w.hq * w.head_dim * w.esize
+    else:
+        kern = "k_attn_bf16" if w.dtype == "bf16" else "k_attn_f32"
+        if plan_ws:
+            kern += " + k_combine"
+        kms = stages[3]
+        kbytes = w.bytes_gather() + w.bytes_q_out()
+    achieved = kbytes / (kms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": kern, "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": None, "bytes_per_launch": kbytes, "avg_us": round(kms * 1000, 2)}
+
+    res = {"metric": METRIC, "value": round(w.batch / (ms * 1e-3), 1), "unit": "queries/s/layer",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": w.dtype, "data": "synthetic",
+           "config": dict(w.describe(), layers_rotated=n_layers),
+           "step_bytes": step_bytes, "hbm_gbs": round(gbs, 1),
+           "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "stages_us": stages_us,
+           "roofline": roofline}
+
+    if not args.no_dense:
+        dms, _ = time_steps(lambda i, b, e: dense_step(w, i, b), layers,
+                            max(5, args.steps // 5), 2)
+        dbytes = w.bytes_dense()
+        res["dense"] = {"queries_per_s": round(w.batch / (dms * 1e-3), 1),
+                        "ms_per_step": round(dms, 5),
+                        "hbm_gbs": round(dbytes / (dms * 1e-3) / 1e9, 1)}
+        res["speedup_vs_dense"] = round(dms / ms, 2)
+
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, layers[0], args.cpu_seqs)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

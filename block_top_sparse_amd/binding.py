@@ -1,0 +1,160 @@
+"""Python binding of libkin.so (include/kin.h): argument marshalling only.
+
+Every function has the name of the C entry point it calls and takes torch
+device tensors (or None) plus an optional stream (a torch.cuda.Stream, a raw
+hipStream_t handle, or None for torch's current stream).  Nothing here
+computes: every step runs in the HIP kernels of libkin.so.  A non-zero
+status raises KinError with the library's own message.  If libkin.so has not
+been built the first call raises; there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkin.so")
+
+KIN_F32, KIN_BF16 = 0, 1
+_STATUS = {0: "KIN_OK", -1: "KIN_ERR_NULL", -2: "KIN_ERR_SHAPE", -3: "KIN_ERR_DTYPE",
+           -4: "KIN_ERR_ALIGN", -5: "KIN_ERR_UNSUPPORTED", -6: "KIN_ERR_WORKSPACE",
+           -7: "KIN_ERR_HIP"}
+_DT = {torch.float32: KIN_F32, torch.bfloat16: KIN_BF16}
+
+
+class KinError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class kin_desc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("hkv", ctypes.c_int32), ("gqa", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("t_cap", ctypes.c_int32),
+                ("ctx_len", ctypes.c_int32), ("block", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+    def __repr__(self):
+        return "kin_desc(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+def make_desc(batch, hkv, gqa, t_cap, ctx_len, block, dtype, head_dim=128) -> kin_desc:
+    dt = _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return kin_desc(batch, hkv, gqa, head_dim, t_cap, ctx_len, block, dt)
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                              "(or python block_top_sparse_amd/build.py) first")
+        L = ctypes.CDLL(LIB_PATH)
+        D, P, I, Z = ctypes.POINTER(kin_desc), ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        sig = {
+            "kin_block_summary_update": (I, [D, P, P, I, I, P]),
+            "kin_block_score": (I, [D, P, P, P, P]),
+            "kin_block_topk": (I, [D, P, I, P, P]),
+            "kin_sparse_decode_attn": (I, [D, P, P, P, P, I, P, P, Z, P]),
+            "kin_dense_decode_attn": (I, [D, P, P, P, P, P, Z, P]),
+            "kin_sparse_decode_step": (I, [D, P, P, P, P, P, I, P, P, P, Z, P]),
+            "kin_sparse_ws_bytes": (Z, [D, I]),
+            "kin_dense_ws_bytes": (Z, [D]),
+            "kin_status_str": (ctypes.c_char_p, [I]),
+            "kin_last_error": (ctypes.c_char_p, []),
+            "kin_version": (I, []),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def exported_names():
+    return ["kin_block_summary_update", "kin_block_score", "kin_block_topk",
+            "kin_sparse_decode_attn", "kin_dense_decode_attn", "kin_sparse_decode_step",
+            "kin_sparse_ws_bytes", "kin_dense_ws_bytes", "kin_status_str", "kin_last_error",
+            "kin_version"]
+
+
+def _p(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _s(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _check(rc):
+    if rc != 0:
+        raise KinError(rc, lib().kin_last_error().decode())
+
+
+def kin_block_summary_update(desc, K, S, t_begin, t_end, stream=None):
+    _check(lib().kin_block_summary_update(ctypes.byref(desc), _p(K), _p(S), t_begin, t_end,
+                                          _s(stream)))
+
+
+def kin_block_score(desc, q, S, scores, stream=None):
+    _check(lib().kin_block_score(ctypes.byref(desc), _p(q), _p(S), _p(scores), _s(stream)))
+
+
+def kin_block_topk(desc, scores, k, idx, stream=None):
+    _check(lib().kin_block_topk(ctypes.byref(desc), _p(scores), k, _p(idx), _s(stream)))
+
+
+def kin_sparse_decode_attn(desc, q, K, V, idx, k, out, ws=None, stream=None):
+    _check(lib().kin_sparse_decode_attn(ctypes.byref(desc), _p(q), _p(K), _p(V), _p(idx), k,
+                                        _p(out), _p(ws), _nbytes(ws), _s(stream)))
+
+
+def kin_dense_decode_attn(desc, q, K, V, out, ws=None, stream=None):
+    _check(lib().kin_dense_decode_attn(ctypes.byref(desc), _p(q), _p(K), _p(V), _p(out), _p(ws),
+                                       _nbytes(ws), _s(stream)))
+
+
+def kin_sparse_decode_step(desc, q, K, V, S, scores, k, idx, out, ws=None, stream=None):
+    _check(lib().kin_sparse_decode_step(ctypes.byref(desc), _p(q), _p(K), _p(V), _p(S),
+                                        _p(scores), k, _p(idx), _p(out), _p(ws), _nbytes(ws),
+                                        _s(stream)))
+
+
+def kin_sparse_ws_bytes(desc, k) -> int:
+    n = lib().kin_sparse_ws_bytes(ctypes.byref(desc), k)
+    if n == ctypes.c_size_t(-1).value:
+        raise KinError(-2, lib().kin_last_error().decode())
+    return n
+
+
+def kin_dense_ws_bytes(desc) -> int:
+    n = lib().kin_dense_ws_bytes(ctypes.byref(desc))
+    if n == ctypes.c_size_t(-1).value:
+        raise KinError(-2, lib().kin_last_error().decode())
+    return n
+
+
+def kin_status_str(status) -> str:
+    return lib().kin_status_str(status).decode()
+
+
+def kin_last_error() -> str:
+    return lib().kin_last_error().decode()
+
+
+def kin_version() -> int:
+    return lib().kin_version()

@@ -1,0 +1,246 @@
+// kin_abi.hip -- the C ABI of libkin.so (declared in include/kin.h):
+// argument checks on the host, workspace sizing, launches on the caller's
+// stream.  Nothing here allocates device memory or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "kin_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+kin_status fail(kin_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+kin_status ok() {
+    g_last_error[0] = '\0';
+    return KIN_OK;
+}
+
+// compute-unit count per device, read once
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_num_cu[kMaxDevices];
+
+int num_cu() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int n = g_num_cu[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+        n = 256;
+    g_num_cu[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Validate a descriptor and derive the geometry.
+kin_status check_desc(const kin_desc *d, kin::Geo *g) {
+    if (!d) return fail(KIN_ERR_NULL, "desc is NULL");
+    if (d->dtype != KIN_F32 && d->dtype != KIN_BF16)
+        return fail(KIN_ERR_DTYPE, "dtype %d is not KIN_F32 (0) or KIN_BF16 (1)", d->dtype);
+    if (d->batch < 1 || d->hkv < 1 || d->gqa < 1)
+        return fail(KIN_ERR_SHAPE, "batch %d, hkv %d and gqa %d must be >= 1", d->batch, d->hkv,
+                    d->gqa);
+    if (d->block < 1)
+        return fail(KIN_ERR_SHAPE, "block %d must be >= 1", d->block);
+    if (d->t_cap < 1 || d->ctx_len < 1 || d->ctx_len > d->t_cap)
+        return fail(KIN_ERR_SHAPE, "need 1 <= ctx_len (%d) <= t_cap (%d)", d->ctx_len, d->t_cap);
+    if (d->head_dim != kin::kHeadDim)
+        return fail(KIN_ERR_UNSUPPORTED, "head_dim %d: only %d is built", d->head_dim,
+                    kin::kHeadDim);
+    if (d->block != 16 && d->block != 32 && d->block != 64 && d->block != 128)
+        return fail(KIN_ERR_UNSUPPORTED, "block %d: only 16, 32, 64 and 128 are built", d->block);
+    if (d->gqa > kin::kMaxGqa)
+        return fail(KIN_ERR_UNSUPPORTED, "gqa %d: at most %d query heads per KV head", d->gqa,
+                    kin::kMaxGqa);
+    const long long pairs = (long long)d->batch * d->hkv;
+    if (pairs > 65535 || (long long)d->batch * d->hkv * d->gqa > (1LL << 30))
+        return fail(KIN_ERR_UNSUPPORTED, "batch x hkv = %lld pairs: at most 65535", pairs);
+    g->batch = d->batch;
+    g->hkv = d->hkv;
+    g->gqa = d->gqa;
+    g->hq = d->hkv * d->gqa;
+    g->t_cap = d->t_cap;
+    g->ctx_len = d->ctx_len;
+    g->block = d->block;
+    g->dtype = d->dtype;
+    g->nb = (d->ctx_len + d->block - 1) / d->block;
+    g->nb_cap = (d->t_cap + d->block - 1) / d->block;
+    g->pairs = (int)pairs;
+    return KIN_OK;
+}
+
+#define KIN_REQUIRE_PTR(p)                                                     \
+    do {                                                                       \
+        if (!(p)) return fail(KIN_ERR_NULL, "%s is NULL", #p);                 \
+        if (!aligned16(p)) return fail(KIN_ERR_ALIGN, "%s is not 16-byte aligned", #p); \
+    } while (0)
+
+kin_status launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(KIN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kin_status kin_block_summary_update(const kin_desc *desc, const void *K, void *S,
+                                    int32_t t_begin, int32_t t_end, kin_stream stream) {
+    kin::Geo g;
+    kin_status st = check_desc(desc, &g);
+    if (st != KIN_OK) return st;
+    KIN_REQUIRE_PTR(K);
+    KIN_REQUIRE_PTR(S);
+    if (t_begin < 0 || t_end < t_begin || t_end > g.t_cap)
+        return fail(KIN_ERR_SHAPE, "need 0 <= t_begin (%d) <= t_end (%d) <= t_cap (%d)", t_begin,
+                    t_end, g.t_cap);
+    const int te = t_end < g.ctx_len ? t_end : g.ctx_len;
+    if (t_begin >= te) return ok();  // nothing inside [0, ctx_len)
+    const int j0 = t_begin / g.block, j1 = (te - 1) / g.block + 1;
+    return launched(kin::launch_block_summary(g, K, S, j0, j1, (hipStream_t)stream),
+                    "kin_block_summary_update");
+}
+
+kin_status kin_block_score(const kin_desc *desc, const void *q, const void *S, double *scores,
+                           kin_stream stream) {
+    kin::Geo g;
+    kin_status st = check_desc(desc, &g);
+    if (st != KIN_OK) return st;
+    KIN_REQUIRE_PTR(q);
+    KIN_REQUIRE_PTR(S);
+    KIN_REQUIRE_PTR(scores);
+    if (g.nb > kin::kMaxBlocks)
+        return fail(KIN_ERR_UNSUPPORTED, "%d blocks: at most %d", g.nb, kin::kMaxBlocks);
+    return launched(kin::launch_block_score(g, q, S, scores, (hipStream_t)stream),
+                    "kin_block_score");
+}
+
+kin_status kin_block_topk(const kin_desc *desc, const double *scores, int32_t k, int32_t *idx,
+                          kin_stream stream) {
+    kin::Geo g;
+    kin_status st = check_desc(desc, &g);
+    if (st != KIN_OK) return st;
+    KIN_REQUIRE_PTR(scores);
+    KIN_REQUIRE_PTR(idx);
+    if (k < 1) return fail(KIN_ERR_SHAPE, "k = %d: need k >= 1", k);
+    if (g.nb > kin::kMaxBlocks)
+        return fail(KIN_ERR_UNSUPPORTED, "%d blocks: at most %d", g.nb, kin::kMaxBlocks);
+    return launched(kin::launch_block_topk(g, scores, k, idx, (hipStream_t)stream),
+                    "kin_block_topk");
+}
+
+static kin_status attention(const kin_desc *desc, const void *q, const void *K, const void *V,
+                            const int32_t *idx, int32_t k, void *out, void *ws,
+                            size_t ws_bytes, kin_stream stream, bool dense) {
+    kin::Geo g;
+    kin_status st = check_desc(desc, &g);
+    if (st != KIN_OK) return st;
+    KIN_REQUIRE_PTR(q);
+    KIN_REQUIRE_PTR(K);
+    KIN_REQUIRE_PTR(V);
+    KIN_REQUIRE_PTR(out);
+    if (!dense) {
+        KIN_REQUIRE_PTR(idx);
+        if (k < 1) return fail(KIN_ERR_SHAPE, "k = %d: need k >= 1", k);
+    }
+    const kin::AttnPlan p = kin::plan_attention(g, dense ? 0 : k, dense, num_cu());
+    if (p.ws_bytes > 0) {
+        if (!ws) return fail(KIN_ERR_NULL, "ws is NULL but %zu bytes are needed", p.ws_bytes);
+        if (!aligned16(ws)) return fail(KIN_ERR_ALIGN, "ws is not 16-byte aligned");
+        if (ws_bytes < p.ws_bytes)
+            return fail(KIN_ERR_WORKSPACE, "ws has %zu bytes, %zu needed", ws_bytes, p.ws_bytes);
+    }
+    return launched(kin::launch_attention(g, p, q, K, V, dense ? nullptr : idx, k, out, ws,
+                                          (hipStream_t)stream),
+                    dense ? "kin_dense_decode_attn" : "kin_sparse_decode_attn");
+}
+
+kin_status kin_sparse_decode_attn(const kin_desc *desc, const void *q, const void *K,
+                                  const void *V, const int32_t *idx, int32_t k, void *out,
+                                  void *ws, size_t ws_bytes, kin_stream stream) {
+    return attention(desc, q, K, V, idx, k, out, ws, ws_bytes, stream, false);
+}
+
+kin_status kin_dense_decode_attn(const kin_desc *desc, const void *q, const void *K,
+                                 const void *V, void *out, void *ws, size_t ws_bytes,
+                                 kin_stream stream) {
+    return attention(desc, q, K, V, nullptr, 0, out, ws, ws_bytes, stream, true);
+}
+
+kin_status kin_sparse_decode_step(const kin_desc *desc, const void *q, const void *K,
+                                  const void *V, void *S, double *scores, int32_t k,
+                                  int32_t *idx, void *out, void *ws, size_t ws_bytes,
+                                  kin_stream stream) {
+    // check everything before enqueueing anything
+    kin::Geo g;
+    kin_status st = check_desc(desc, &g);
+    if (st != KIN_OK) return st;
+    KIN_REQUIRE_PTR(q);
+    KIN_REQUIRE_PTR(K);
+    KIN_REQUIRE_PTR(V);
+    KIN_REQUIRE_PTR(S);
+    KIN_REQUIRE_PTR(scores);
+    KIN_REQUIRE_PTR(idx);
+    KIN_REQUIRE_PTR(out);
+    if (k < 1) return fail(KIN_ERR_SHAPE, "k = %d: need k >= 1", k);
+    if (g.nb > kin::kMaxBlocks)
+        return fail(KIN_ERR_UNSUPPORTED, "%d blocks: at most %d", g.nb, kin::kMaxBlocks);
+    const kin::AttnPlan p = kin::plan_attention(g, k, false, num_cu());
+    if (p.ws_bytes > 0) {
+        if (!ws) return fail(KIN_ERR_NULL, "ws is NULL but %zu bytes are needed", p.ws_bytes);
+        if (!aligned16(ws)) return fail(KIN_ERR_ALIGN, "ws is not 16-byte aligned");
+        if (ws_bytes < p.ws_bytes)
+            return fail(KIN_ERR_WORKSPACE, "ws has %zu bytes, %zu needed", ws_bytes, p.ws_bytes);
+    }
+    hipStream_t s = (hipStream_t)stream;
+    const int jn = (g.ctx_len - 1) / g.block;
+    hipError_t e = kin::launch_block_summary(g, K, S, jn, jn + 1, s);
+    if (e == hipSuccess) e = kin::launch_block_score(g, q, S, scores, s);
+    if (e == hipSuccess) e = kin::launch_block_topk(g, scores, k, idx, s);
+    if (e == hipSuccess) e = kin::launch_attention(g, p, q, K, V, idx, k, out, ws, s);
+    return launched(e, "kin_sparse_decode_step");
+}
+
+size_t kin_sparse_ws_bytes(const kin_desc *desc, int32_t k) {
+    kin::Geo g;
+    if (check_desc(desc, &g) != KIN_OK || k < 1) return (size_t)-1;
+    return kin::plan_attention(g, k, false, num_cu()).ws_bytes;
+}
+
+size_t kin_dense_ws_bytes(const kin_desc *desc) {
+    kin::Geo g;
+    if (check_desc(desc, &g) != KIN_OK) return (size_t)-1;
+    return kin::plan_attention(g, 0, true, num_cu()).ws_bytes;
+}
+
+const char *kin_status_str(kin_status status) {
+    switch (status) {
+    case KIN_OK: return "KIN_OK";
+    case KIN_ERR_NULL: return "KIN_ERR_NULL";
+    case KIN_ERR_SHAPE: return "KIN_ERR_SHAPE";
+    case KIN_ERR_DTYPE: return "KIN_ERR_DTYPE";
+    case KIN_ERR_ALIGN: return "KIN_ERR_ALIGN";
+    case KIN_ERR_UNSUPPORTED: return "KIN_ERR_UNSUPPORTED";
+    case KIN_ERR_WORKSPACE: return "KIN_ERR_WORKSPACE";
+    case KIN_ERR_HIP: return "KIN_ERR_HIP";
+    }
+    return "KIN_ERR_UNKNOWN";
+}
+
+const char *kin_last_error(void) { return g_last_error; }
+
+int32_t kin_version(void) { return KIN_VERSION; }
+
+}  // extern "C"

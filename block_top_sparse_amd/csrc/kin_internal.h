@@ -1,0 +1,68 @@
+// kin_internal.h -- shared between the ABI layer and the kernel files of
+// libkin.so.  Not installed; the public interface is include/kin.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kin.h"
+
+namespace kin {
+
+constexpr int kHeadDim = 128;  // the only head_dim built
+constexpr int kMaxGqa = 16;    // query heads of one group fit one 16-row MFMA tile
+constexpr int kMaxBlocks = 16384;
+constexpr int kChunkBf16 = 32;  // tokens per wave iteration, bf16 attention
+constexpr int kChunkF32 = 64;   // tokens per wave iteration, fp32 attention
+
+// Geometry shared by the launchers (all derived from a validated desc).
+struct Geo {
+    int batch, hkv, gqa, hq, t_cap, ctx_len, block, dtype;
+    int nb, nb_cap, pairs;
+};
+
+// Split-KV plan of one attention call.
+struct AttnPlan {
+    int n_tokens;  // length of each pair's token list (kept blocks x block, or ctx_len)
+    int n_chunks;  // ceil(n_tokens / chunk)
+    int nsplit;    // workgroups per (sequence, KV head)
+    size_t ws_bytes;
+};
+
+AttnPlan plan_attention(const Geo &g, int k, bool dense, int num_cu);
+
+hipError_t launch_block_summary(const Geo &g, const void *K, void *S, int j0, int j1,
+                                hipStream_t s);
+hipError_t launch_block_score(const Geo &g, const void *q, const void *S, double *scores,
+                              hipStream_t s);
+hipError_t launch_block_topk(const Geo &g, const double *scores, int k, int32_t *idx,
+                             hipStream_t s);
+hipError_t launch_attention(const Geo &g, const AttnPlan &p, const void *q, const void *K,
+                            const void *V, const int32_t *idx, int k, void *out, void *ws,
+                            hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// device helpers (bf16 is carried as its raw 16 bits)
+// ---------------------------------------------------------------------------
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// One 16-byte global load of streamed (read-once) data.
+__device__ __forceinline__ u32x4 ld_stream16(const void *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest, ties to even (finite inputs): adding
+// 0x7FFF plus the lowest kept bit carries into the kept half exactly when
+// the dropped half is above one half, or equal to it with an odd kept half.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+}  // namespace kin

@@ -1,0 +1,166 @@
+/*
+ * kin.h -- C ABI of libkin.so: block top-k sparse decode attention for
+ * AMD Instinct MI355X (gfx950), hand-written HIP.
+ *
+ * The method (sources: the skill summary page "Kinetics: Memory-Aware
+ * Test-Time Scaling", section "Implementation", module BlockTopKAttention;
+ * the rebuttal page "Kinetics: Rethinking Test-Time Scaling Law", answers
+ * Q4 "KV block size and grouping strategy", "W2. Alternative sparse
+ * attention variants" and "W2 & Q2: Real-world latency benchmarks"):
+ * at every decode step each sequence brings one new query per head and
+ * attends to its whole retained KV cache.  The cache is cut into KV blocks
+ * of `block` tokens; each block is represented by the mean of its keys; the
+ * query (all heads of one GQA group together) scores every representative,
+ * the k best blocks are kept, and exact softmax(q.k / sqrt(d)) . v runs over
+ * the kept blocks' tokens only.  The KV budget in tokens is block * k.
+ *
+ * Readings of points the pages leave open:
+ *   - representative: the mean key (for one query, q.mean(k) equals the
+ *     page's "mean score per block");
+ *   - one selection per (sequence, KV head), shared by its query heads; the
+ *     group's block score is the SUM of the heads' scores, computed in fp64
+ *     without the 1/sqrt(d) factor (it does not change the order);
+ *   - ties keep the lower block index; indices come out ascending;
+ *   - a partial last block is averaged over its valid tokens;
+ *   - the new token is already in the cache: attention covers [0, ctx_len).
+ *
+ * Shapes and layouts (all row-major, contiguous, device memory):
+ *   hq = hkv * gqa;  query head h reads KV head h / gqa
+ *   nb = ceil(ctx_len / block),  nb_cap = ceil(t_cap / block)
+ *   q, out   [batch][hq][head_dim]            dtype
+ *   K, V     [batch][hkv][t_cap][head_dim]    dtype
+ *   S        [batch][hkv][nb_cap][head_dim]   dtype (block summaries)
+ *   scores   [batch][hkv][nb_cap]             double
+ *   idx      [batch][hkv][k]                  int32
+ * dtype KIN_F32 (binary32) or KIN_BF16 (bfloat16) applies to q, K, V, S
+ * and out alike.  Supported: head_dim 128; block 16, 32, 64 or 128;
+ * 1 <= gqa <= 16; nb <= 16384.
+ *
+ * Conventions for every call:
+ *   - The caller owns every buffer; the library allocates nothing, never
+ *     synchronises, and keeps no state beyond cached device properties and a
+ *     thread-local error message.  Outputs must not alias inputs.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream
+ *     of the current device) in call order; calls return before it runs.
+ *   - Arguments are checked on the host before anything is enqueued; a bad
+ *     argument returns its code, kin_last_error() describes it, and nothing
+ *     runs.  A failed launch returns KIN_ERR_HIP.  Faults inside a kernel
+ *     surface at the caller's next synchronisation, as with any HIP work.
+ *   - Pointers must be 16-byte aligned.  The values read must be finite.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef KIN_H
+#define KIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KIN_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define KIN_API __attribute__((visibility("default")))
+#else
+#define KIN_API
+#endif
+
+typedef void *kin_stream; /* a hipStream_t */
+
+typedef enum kin_dtype {
+    KIN_F32 = 0,
+    KIN_BF16 = 1
+} kin_dtype;
+
+typedef enum kin_status {
+    KIN_OK = 0,
+    KIN_ERR_NULL = -1,        /* a required pointer is NULL */
+    KIN_ERR_SHAPE = -2,       /* a size or range is out of bounds */
+    KIN_ERR_DTYPE = -3,       /* dtype is not KIN_F32 or KIN_BF16 */
+    KIN_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+    KIN_ERR_UNSUPPORTED = -5, /* valid, but not built (e.g. head_dim != 128) */
+    KIN_ERR_WORKSPACE = -6,   /* workspace too small */
+    KIN_ERR_HIP = -7          /* the HIP runtime refused a launch */
+} kin_status;
+
+typedef struct kin_desc {
+    int32_t batch;    /* sequences in the decode batch */
+    int32_t hkv;      /* KV heads */
+    int32_t gqa;      /* query heads per KV head */
+    int32_t head_dim; /* channels per head (128) */
+    int32_t t_cap;    /* cache capacity in tokens per (sequence, KV head) */
+    int32_t ctx_len;  /* valid tokens: [0, ctx_len), 1 <= ctx_len <= t_cap */
+    int32_t block;    /* KV block size in tokens */
+    int32_t dtype;    /* kin_dtype */
+} kin_desc;
+
+/* Block summaries (the block representative: mean key).
+ * Recomputes from scratch every block that intersects [t_begin, t_end) and
+ * [0, ctx_len): S[b][g][j][c] = round(sum_{t in block j, t < ctx_len}
+ * K[b][g][t][c] / n_j), n_j = min(block, ctx_len - j*block), the sum taken
+ * in fp64 in ascending t, rounded fp64 -> fp32 (RNE) and, for bf16, fp32 ->
+ * bf16 (RNE).  After prefill call it with [0, ctx_len); at a decode step,
+ * after appending token ctx_len-1, with [ctx_len-1, ctx_len).  Other blocks
+ * of S are not touched.  Idempotent.
+ * Errors: NULL pointers; 0 <= t_begin <= t_end <= t_cap violated. */
+KIN_API kin_status kin_block_summary_update(const kin_desc *desc, const void *K, void *S,
+                                    int32_t t_begin, int32_t t_end, kin_stream stream);
+
+/* Block scores.  scores[b][g][j] = sum over the group's query heads h
+ * (h / gqa == g) of q[b][h] . S[b][g][j], in fp64, for j < nb; -0.0 is
+ * written as +0.0.  Entries j >= nb are not written.
+ * Errors: NULL pointers, shape. */
+KIN_API kin_status kin_block_score(const kin_desc *desc, const void *q, const void *S, double *scores,
+                           kin_stream stream);
+
+/* Top-k block selection.  idx[b][g][0..k) = the min(k, nb) block indices
+ * with the largest scores, ties to the lower index, in ascending order,
+ * followed by -1 when k > nb.  Only scores[b][g][0..nb) are read.
+ * Errors: NULL pointers; k < 1; nb > 16384 (unsupported). */
+KIN_API kin_status kin_block_topk(const kin_desc *desc, const double *scores, int32_t k, int32_t *idx,
+                          kin_stream stream);
+
+/* Sparse decode attention.  For each query head h of KV head g:
+ * out[b][h] = sum_t softmax_t(q[b][h] . K[b][g][t] / sqrt(head_dim)) V[b][g][t]
+ * over the tokens t < ctx_len of the blocks listed in idx[b][g][0..k)
+ * (entries < 0 or >= nb are skipped).  Accumulation is fp32.
+ * `ws` is scratch of at least kin_sparse_ws_bytes(desc, k) bytes (may be
+ * NULL when that is 0); its contents on entry do not matter.
+ * Errors: NULL pointers, shape, workspace. */
+KIN_API kin_status kin_sparse_decode_attn(const kin_desc *desc, const void *q, const void *K,
+                                  const void *V, const int32_t *idx, int32_t k, void *out,
+                                  void *ws, size_t ws_bytes, kin_stream stream);
+
+/* Dense decode attention over every token in [0, ctx_len): the comparison
+ * the pages measure Block-TopK against.  Same conventions as above. */
+KIN_API kin_status kin_dense_decode_attn(const kin_desc *desc, const void *q, const void *K,
+                                 const void *V, void *out, void *ws, size_t ws_bytes,
+                                 kin_stream stream);
+
+/* One whole sparse decode step, enqueued back to back on `stream`:
+ * summary update of the newest block ([ctx_len-1, ctx_len)), scores, top-k
+ * and sparse attention.  S is updated in place; scores and idx are written
+ * as by the individual calls (they are the step's intermediate results). */
+KIN_API kin_status kin_sparse_decode_step(const kin_desc *desc, const void *q, const void *K,
+                                  const void *V, void *S, double *scores, int32_t k,
+                                  int32_t *idx, void *out, void *ws, size_t ws_bytes,
+                                  kin_stream stream);
+
+/* Workspace sizes in bytes (0 when none is needed); -1 cast to size_t on
+ * a bad descriptor.  Sizes depend on the current device's compute-unit
+ * count: query them on the device the calls will run on. */
+KIN_API size_t kin_sparse_ws_bytes(const kin_desc *desc, int32_t k);
+KIN_API size_t kin_dense_ws_bytes(const kin_desc *desc);
+
+/* Name of a status code, and the detail of the last error on this thread. */
+KIN_API const char *kin_status_str(kin_status status);
+KIN_API const char *kin_last_error(void);
+KIN_API int32_t kin_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KIN_H */

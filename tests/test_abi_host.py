@@ -1,0 +1,112 @@
+"""Host-side checks of libkin.so that need no GPU.
+
+The library loads, exports every entry point include/kin.h declares, and
+rejects bad arguments on the host with the documented status before
+anything is enqueued (each case here fails validation, so no HIP call is
+made).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_top_sparse_amd import binding as kb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kin.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kb.LIB_PATH), reason="libkin.so not built")
+
+FAKE = 0x100000  # an aligned, never dereferenced address: validation fails first
+MISALIGNED = 0x100008
+
+
+def header_entry_points():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"KIN_API\s+[\w\s\*]+?\b(kin_\w+)\s*\(", text)))
+
+
+def test_every_declared_entry_point_is_exported():
+    declared = header_entry_points()
+    assert len(declared) == 11, declared
+    lib = ctypes.CDLL(kb.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(kb.exported_names()) == declared
+
+
+def test_version_and_status_strings():
+    assert kb.kin_version() == 1
+    for code, name in [(0, "KIN_OK"), (-1, "KIN_ERR_NULL"), (-2, "KIN_ERR_SHAPE"),
+                       (-5, "KIN_ERR_UNSUPPORTED"), (-6, "KIN_ERR_WORKSPACE"), (-7, "KIN_ERR_HIP")]:
+        assert kb.kin_status_str(code) == name
+
+
+def _desc(**kw):
+    base = dict(batch=2, hkv=2, gqa=4, t_cap=256, ctx_len=200, block=16, dtype=kb.KIN_BF16)
+    base.update(kw)
+    return kb.make_desc(**base)
+
+
+def _raw(name, *args):
+    return getattr(kb.lib(), name)(*args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), -3),
+    (dict(batch=0), -2),
+    (dict(gqa=0), -2),
+    (dict(ctx_len=0), -2),
+    (dict(ctx_len=300), -2),          # beyond t_cap
+    (dict(head_dim=64), -5),
+    (dict(block=24), -5),
+    (dict(block=8), -5),
+    (dict(gqa=17), -5),
+])
+def test_bad_descriptor_is_rejected(kw, code):
+    d = _desc(**kw)
+    rc = _raw("kin_block_score", ctypes.byref(d), FAKE, FAKE, FAKE, None)
+    assert rc == code, kb.kin_last_error()
+    assert kb.kin_last_error()
+
+
+def test_null_and_misaligned_pointers_are_rejected():
+    d = _desc()
+    assert _raw("kin_block_score", None, FAKE, FAKE, FAKE, None) == -1
+    assert _raw("kin_block_score", ctypes.byref(d), None, FAKE, FAKE, None) == -1
+    assert "q is NULL" in kb.kin_last_error()
+    assert _raw("kin_block_score", ctypes.byref(d), FAKE, MISALIGNED, FAKE, None) == -4
+    assert _raw("kin_block_topk", ctypes.byref(d), FAKE, 4, None, None) == -1
+    assert _raw("kin_sparse_decode_attn", ctypes.byref(d), FAKE, FAKE, FAKE, None, 4, FAKE,
+                None, 0, None) == -1
+    assert _raw("kin_dense_decode_attn", ctypes.byref(d), FAKE, FAKE, None, FAKE, None, 0,
+                None) == -1
+
+
+def test_bad_ranges_and_k_are_rejected():
+    d = _desc()
+    assert _raw("kin_block_summary_update", ctypes.byref(d), FAKE, FAKE, -1, 5, None) == -2
+    assert _raw("kin_block_summary_update", ctypes.byref(d), FAKE, FAKE, 10, 5, None) == -2
+    assert _raw("kin_block_summary_update", ctypes.byref(d), FAKE, FAKE, 0, 257, None) == -2
+    assert _raw("kin_block_topk", ctypes.byref(d), FAKE, 0, FAKE, None) == -2
+    assert _raw("kin_sparse_decode_attn", ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, FAKE,
+                None, 0, None) == -2
+    assert _raw("kin_sparse_decode_step", ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0,
+                FAKE, FAKE, None, 0, None) == -2
+    big = _desc(t_cap=16 * 20000, ctx_len=16 * 20000)
+    assert _raw("kin_block_topk", ctypes.byref(big), FAKE, 4, FAKE, None) == -5
+
+
+def test_workspace_query_rejects_bad_descriptor():
+    with pytest.raises(kb.KinError):
+        kb.kin_sparse_ws_bytes(_desc(gqa=0), 4)
+    with pytest.raises(kb.KinError):
+        kb.kin_dense_ws_bytes(_desc(dtype=9))
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(kb, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(kb, "_lib", None)
+    with pytest.raises(ImportError):
+        kb.kin_version()

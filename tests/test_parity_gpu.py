@@ -1,0 +1,170 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small cases run the whole oracle (several tiles, ragged tails, every block
+size, GQA 1..16, k from 1 past nb, NaN-filled cache tails); the workload
+shapes run at full size with every sequence's selection checked bit-exactly
+and outputs checked on sampled sequences.
+"""
+import zlib
+
+import pytest
+import torch
+
+import oracle
+from block_top_sparse_amd import binding as kb
+from block_top_sparse_amd import synth, workloads
+from block_top_sparse_amd.buffers import LayerBuffers
+from block_top_sparse_amd.workloads import Workload
+
+from parity_util import TOL, bits, check_sequences, gpu_inputs, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kb.lib()  # loud failure if the library is missing
+
+
+SMALL = [
+    # name, batch, hq, hkv, ctx, block, k, dtype, t_cap
+    ("f32-g4-b16", 2, 8, 2, 1000, 16, 9, "f32", 1024),
+    ("f32-g1-b32-k1", 3, 2, 2, 333, 32, 1, "f32", 400),
+    ("f32-g16-b64", 1, 32, 2, 700, 64, 3, "f32", 704),
+    ("bf16-g4-b16", 2, 8, 2, 2000, 16, 17, "bf16", 2048),
+    ("bf16-g5-b32", 2, 10, 2, 1500, 32, 8, "bf16", 1600),
+    ("bf16-g8-b64", 2, 16, 2, 4000, 64, 5, "bf16", 4096),
+    ("bf16-g16-b128", 1, 32, 2, 2100, 128, 4, "bf16", 2176),
+    ("bf16-g1-b16-k1", 2, 3, 3, 99, 16, 1, "bf16", 100),
+    ("bf16-g3-b16-allm1", 2, 6, 2, 250, 16, 15, "bf16", 256),   # k = nb - 1
+    ("bf16-g4-b32-keepall", 2, 8, 2, 290, 32, 10, "bf16", 320),  # k = nb (ragged last block)
+    ("bf16-g4-b16-kpast", 1, 8, 2, 100, 16, 12, "bf16", 128),    # k > nb: -1 padding
+    ("f32-g2-b16-short", 1, 4, 2, 5, 16, 2, "f32", 16),          # one partial block
+    ("bf16-g8-b16-manyblk", 2, 16, 2, 40000, 16, 64, "bf16", 40000),  # nb 2500: 5 keys/thread
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_cases_against_oracle(case):
+    name, b, hq, hkv, L, B, k, dt, cap = case
+    w = Workload(name, batch=b, hq=hq, hkv=hkv, ctx_len=L, block=B, topk=k, dtype=dt, seed=
+                 zlib.crc32(name.encode()) % 10000, t_cap=cap)
+    say(f"case {name}: {w.describe()}")
+    inp = gpu_inputs(w)
+    bufs = run_gpu(w, inp, dense=True)
+    r = check_sequences(w, inp, bufs, range(b), check_dense=True)
+    idx = bufs.idx.cpu()
+    if k > w.nb:
+        assert (idx[:, :, w.nb:] == -1).all()
+    say(f"  ok {r}")
+
+
+def test_tiny_workload_full_parity():
+    w = workloads.TINY
+    say(f"workload {w.name}")
+    inp = gpu_inputs(w)
+    bufs = run_gpu(w, inp, dense=True)
+    r = check_sequences(w, inp, bufs, range(w.batch), check_dense=True)
+    say(f"  ok {r}")
+
+
+def test_keep_all_blocks_equals_dense_bitwise():
+    # with every block kept the token list is [0, ctx_len) in the same order
+    # and the same split plan, so sparse and dense agree to the bit
+    for dt in ("bf16", "f32"):
+        w = Workload(f"keepall-{dt}", batch=2, hq=16, hkv=2, ctx_len=2048, block=32, topk=64,
+                     dtype=dt, seed=71)
+        inp = gpu_inputs(w)
+        bufs = run_gpu(w, inp, dense=True)
+        assert bufs.idx.cpu()[0, 0].tolist() == list(range(64))
+        assert torch.equal(bits(bufs.out), bits(bufs.out_dense)), dt
+        check_sequences(w, inp, bufs, [1], check_dense=True)
+
+
+def test_deterministic_and_stream_ordered():
+    w = Workload("det", batch=4, hq=32, hkv=8, ctx_len=8192, block=16, topk=64, dtype="bf16",
+                 seed=81)
+    inp = gpu_inputs(w)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        a = run_gpu(w, inp, stream=s)
+        out1, idx1 = a.out.clone(), a.idx.clone()
+        a = run_gpu(w, inp, stream=s, bufs=a)
+    assert torch.equal(idx1, a.idx)
+    assert torch.equal(bits(out1), bits(a.out))
+    check_sequences(w, inp, a, [0, 3])
+
+
+def test_decode_steps_update_newest_block():
+    # grow the context one token at a time: the newest-block update must give
+    # the same summaries as a full rebuild, and the fused step entry must
+    # match the oracle at every step
+    w0 = Workload("decode", batch=2, hq=8, hkv=2, ctx_len=600, block=16, topk=6, dtype="bf16",
+                  seed=91, t_cap=700)
+    inp = gpu_inputs(w0.scaled(ctx_len=700))  # rows 600..699 are the tokens to come
+    bufs = LayerBuffers(w0, k=w0.topk)
+    kb.kin_block_summary_update(bufs.desc, inp["K"], bufs.S, 0, w0.ctx_len)
+    for L in range(601, 642):
+        w = w0.scaled(ctx_len=L)
+        d = kb.make_desc(w.batch, w.hkv, w.gqa, w.cap, L, w.block, torch.bfloat16)
+        bufs.desc = d
+        kb.kin_sparse_decode_step(d, inp["q"], inp["K"], inp["V"], bufs.S, bufs.scores, w.topk,
+                                  bufs.idx, bufs.out, bufs.ws)
+        torch.cuda.synchronize()
+        if L % 8 == 1 or L == 641:
+            check_sequences(w, inp, bufs, range(w.batch))
+    full = LayerBuffers(w, k=w.topk)
+    kb.kin_block_summary_update(full.desc, inp["K"], full.S, 0, w.ctx_len)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(full.S[:, :, :w.nb]), bits(bufs.S[:, :, :w.nb]))
+
+
+def test_workspace_too_small_is_rejected():
+    w = workloads.QWEN3_8B.scaled(ctx_len=4096, batch=2)
+    inp = gpu_inputs(w)
+    bufs = LayerBuffers(w)
+    n = kb.kin_sparse_ws_bytes(bufs.desc, w.topk)
+    if n == 0:
+        pytest.skip("no workspace needed for this plan")
+    small = torch.empty(n - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(kb.KinError) as e:
+        kb.kin_sparse_decode_attn(bufs.desc, inp["q"], inp["K"], inp["V"], bufs.idx, w.topk,
+                                  bufs.out, small)
+    assert e.value.status == -6
+
+
+@pytest.mark.parametrize("w", [workloads.QWEN3_8B, workloads.QWEN3_14B, workloads.QWEN3_32B],
+                         ids=lambda w: w.name)
+def test_full_size_workloads(w):
+    say(f"workload {w.name}: generating {w.cache_bytes() / 2**30:.1f} GiB cache")
+    inp = gpu_inputs(w)
+    bufs = run_gpu(w, inp, dense=True)
+    say("  gpu done; checking every sequence's selection")
+    r = check_sequences(w, inp, bufs, range(w.batch), check_out=False)
+    sample = [0, w.batch // 2, w.batch - 1]
+    r2 = check_sequences(w, inp, bufs, sample, check_out=True, check_dense=True)
+    if w.heavy_blocks:
+        heavy = synth.heavy_block_ids(w, device="cuda")
+        idx = bufs.idx.cpu()
+        for b in range(w.batch):
+            for g in range(w.hkv):
+                assert set(heavy[b][g]) <= set(idx[b, g].tolist())
+    say(f"  ok min_gap={r['min_gap']:.3g} {r2}")
+
+
+SWEEP_SAMPLE = ["sweep-b8-ctx131072-blk16-budget8192", "sweep-b128-ctx8192-blk64-budget256",
+                "sweep-b32-ctx32768-blk32-budget1024", "sweep-b8-ctx8192-blk32-allblocks",
+                "sweep-b32-ctx131072-blk64-budget4096"]
+
+
+@pytest.mark.parametrize("name", SWEEP_SAMPLE)
+def test_sweep_points(name):
+    w = workloads.by_name(name)
+    say(f"workload {w.name}: cache {w.cache_bytes() / 2**30:.1f} GiB")
+    inp = gpu_inputs(w)
+    bufs = run_gpu(w, inp)
+    seqs = sorted({0, w.batch // 2, w.batch - 1})
+    r = check_sequences(w, inp, bufs, seqs)
+    say(f"  ok {r}")
