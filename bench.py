@@ -49,22 +49,38 @@ def make_layers(w, n_layers, with_dense):
 
 
 def sparse_step(w, inp, bufs, ev=None):
-    d, L = bufs.desc, w.ctx_len
+    """One decode step of one layer through kin_sparse_decode_step (one
+    kernel when there are enough pairs, else two), events around it."""
     if ev is not None:
         ev[0].record()
-    kb.kin_block_summary_update(d, inp["K"], bufs.S, L - 1, L)
+    kb.kin_sparse_decode_step(bufs.desc, inp["q"], inp["K"], inp["V"], bufs.S, bufs.scores,
+                              bufs.k, bufs.idx, bufs.out, bufs.ws)
     if ev is not None:
         ev[1].record()
-    kb.kin_block_score(d, inp["q"], bufs.S, bufs.scores)
+
+
+def two_kernel_step(w, inp, bufs, ev=None):
+    """The same step as its two fused halves, an event between them."""
+    d = bufs.desc
+    if ev is not None:
+        ev[0].record()
+    kb.kin_decode_update_score(d, inp["q"], inp["K"], bufs.S, bufs.scores)
+    if ev is not None:
+        ev[1].record()
+    kb.kin_decode_select_attend(d, inp["q"], inp["K"], inp["V"], bufs.scores, bufs.k, bufs.idx,
+                                bufs.out, bufs.ws)
     if ev is not None:
         ev[2].record()
+
+
+def unfused_step(w, inp, bufs, ev=None):
+    """The same step as four separate calls (one kernel each, plus combine)."""
+    d, L = bufs.desc, w.ctx_len
+    kb.kin_block_summary_update(d, inp["K"], bufs.S, L - 1, L)
+    kb.kin_block_score(d, inp["q"], bufs.S, bufs.scores)
     kb.kin_block_topk(d, bufs.scores, bufs.k, bufs.idx)
-    if ev is not None:
-        ev[3].record()
     kb.kin_sparse_decode_attn(d, inp["q"], inp["K"], inp["V"], bufs.idx, bufs.k, bufs.out,
                               bufs.ws)
-    if ev is not None:
-        ev[4].record()
 
 
 def dense_step(w, inp, bufs, ev=None):
@@ -129,6 +145,7 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="layers rotated (0: auto)")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32)
     args = ap.parse_args()
 
@@ -147,28 +164,22 @@ def main():
         f"{w.bytes_sparse_step() / 2**20:.1f} MiB")
     layers = make_layers(w, n_layers, with_dense=not args.no_dense)
 
+    # timed region: K steps of kin_sparse_decode_step, an event pair around
+    # each (same stream)
     ms, stages = time_steps(lambda i, b, e: sparse_step(w, i, b, e), layers, args.steps,
-                            args.warmup, n_events=5)
+                            args.warmup, n_events=2)
     step_bytes = w.bytes_sparse_step()
     gbs = step_bytes / (ms * 1e-3) / 1e9
-    stage_names = ["summary_update", "block_score", "block_topk", "sparse_attn"]
-    stages_us = {n: round(t * 1000, 2) for n, t in zip(stage_names, stages)}
-
-    # dominant kernel: the longest of the two streaming stages
-    plan_ws = kb.kin_sparse_ws_bytes(layers[0][1].desc, w.topk)
-    if stages[1] >= stages[3]:
-        kern, kms = "k_block_score", stages[1]
-        kbytes = w.bytes_summary_scan() + w.batch * w.hq * w.head_dim * w.esize
+    num_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    single = w.dtype == "bf16" and w.pairs >= num_cu and w.nb <= 8192 and w.topk <= 2048
+    if single:
+        kern, kbytes, kus = "k_decode_step", step_bytes, stages[0] * 1000
     else:
-        kern = "k_attn_bf16" if w.dtype == "bf16" else "k_attn_f32"
-        if plan_ws:
-            kern += " + k_combine"
-        kms = stages[3]
-        kbytes = w.bytes_gather() + w.bytes_q_out()
-    achieved = kbytes / (kms * 1e-3) / 1e9
+        kern, kbytes, kus = "k_block_score + k_select_attend", step_bytes, stages[0] * 1000
+    achieved = kbytes / (kus * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": kern, "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": None, "bytes_per_launch": kbytes, "avg_us": round(kms * 1000, 2)}
+                "traffic": None, "bytes_per_launch": kbytes, "avg_us": round(kus, 2)}
 
     res = {"metric": METRIC, "value": round(w.batch / (ms * 1e-3), 1), "unit": "queries/s/layer",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -176,8 +187,17 @@ def main():
            "dtype": w.dtype, "data": "synthetic",
            "config": dict(w.describe(), layers_rotated=n_layers),
            "step_bytes": step_bytes, "hbm_gbs": round(gbs, 1),
-           "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "stages_us": stages_us,
-           "roofline": roofline}
+           "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "roofline": roofline}
+
+    if not args.no_unfused:
+        n = max(5, args.steps // 5)
+        tms, tst = time_steps(lambda i, b, e: two_kernel_step(w, i, b, e), layers, n, 2,
+                              n_events=3)
+        res["two_kernel"] = {"ms_per_step": round(tms, 5),
+                             "update_score_us": round(tst[0] * 1000, 2),
+                             "select_attend_us": round(tst[1] * 1000, 2)}
+        ums, _ = time_steps(lambda i, b, e: unfused_step(w, i, b, e), layers, n, 2)
+        res["four_call_ms_per_step"] = round(ums, 5)
 
     if not args.no_dense:
         dms, _ = time_steps(lambda i, b, e: dense_step(w, i, b), layers,

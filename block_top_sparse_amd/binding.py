@@ -60,6 +60,8 @@ def lib():
             "kin_sparse_decode_attn": (I, [D, P, P, P, P, I, P, P, Z, P]),
             "kin_dense_decode_attn": (I, [D, P, P, P, P, P, Z, P]),
             "kin_sparse_decode_step": (I, [D, P, P, P, P, P, I, P, P, P, Z, P]),
+            "kin_decode_update_score": (I, [D, P, P, P, P, P]),
+            "kin_decode_select_attend": (I, [D, P, P, P, P, I, P, P, P, Z, P]),
             "kin_sparse_ws_bytes": (Z, [D, I]),
             "kin_dense_ws_bytes": (Z, [D]),
             "kin_status_str": (ctypes.c_char_p, [I]),
@@ -76,6 +78,7 @@ def lib():
 def exported_names():
     return ["kin_block_summary_update", "kin_block_score", "kin_block_topk",
             "kin_sparse_decode_attn", "kin_dense_decode_attn", "kin_sparse_decode_step",
+            "kin_decode_update_score", "kin_decode_select_attend",
             "kin_sparse_ws_bytes", "kin_dense_ws_bytes", "kin_status_str", "kin_last_error",
             "kin_version"]
 
@@ -132,6 +135,16 @@ def kin_sparse_decode_step(desc, q, K, V, S, scores, k, idx, out, ws=None, strea
     _check(lib().kin_sparse_decode_step(ctypes.byref(desc), _p(q), _p(K), _p(V), _p(S),
                                         _p(scores), k, _p(idx), _p(out), _p(ws), _nbytes(ws),
                                         _s(stream)))
+
+
+def kin_decode_update_score(desc, q, K, S, scores, stream=None):
+    _check(lib().kin_decode_update_score(ctypes.byref(desc), _p(q), _p(K), _p(S), _p(scores),
+                                         _s(stream)))
+
+
+def kin_decode_select_attend(desc, q, K, V, scores, k, idx, out, ws=None, stream=None):
+    _check(lib().kin_decode_select_attend(ctypes.byref(desc), _p(q), _p(K), _p(V), _p(scores), k,
+                                          _p(idx), _p(out), _p(ws), _nbytes(ws), _s(stream)))
 
 
 def kin_sparse_ws_bytes(desc, k) -> int:

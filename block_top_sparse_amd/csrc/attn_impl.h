@@ -1,0 +1,431 @@
+// attn_impl.h -- device side of the decode attention: the kept-token list
+// walk, the bf16 MFMA chunk (loads, scores, online softmax, P.V), the fp32
+// VALU chunk, and the merge of a workgroup's waves.  Shared by the
+// standalone attention kernels, the fused select+attend kernel and the
+// single-kernel decode step.  See attn.hip for the design notes.
+#pragma once
+
+#include "select.h"
+
+#include <math.h>
+
+namespace kin {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kAttnThreads = 256;  // standalone attention: 4 waves
+constexpr int kStepThreads = 512;  // fused select + attention: 8 waves
+constexpr int kStepIdxCap = 2048;  // kept blocks the fused kernel holds in LDS
+
+struct AttnArgs {
+    const void *q, *K, *V;
+    const int32_t *idx;  // global kept-block list (standalone sparse attention)
+    void *out;
+    float *ws_o;   // [batch][hq][nsplit][128] unnormalised partial outputs
+    float *ws_ml;  // [batch][hq][nsplit][2]   (running max in log2 units, sum)
+    int hkv, gqa, t_cap, ctx_len, block, block_shift, nb, k, nsplit, n_chunks;
+    float scale_log2;  // log2(e) / sqrt(head_dim)
+};
+
+// Resolve list position p0 .. p0+15 (16 consecutive positions inside one
+// block) to the first token of that run; valid = false if the slot is
+// empty or past the list.  `sel` may point to global memory or LDS.
+template <bool DENSE>
+__device__ __forceinline__ int run_base(const AttnArgs &a, const int32_t *sel, int p0,
+                                        bool &valid) {
+    if (DENSE) {
+        valid = p0 < a.ctx_len;
+        return p0;
+    }
+    const int slot = p0 >> a.block_shift;
+    const int id = slot < a.k ? sel[slot] : -1;
+    valid = id >= 0 && id < a.nb;
+    return id * a.block + (p0 & (a.block - 1));
+}
+
+// LDS the waves of one workgroup merge through: per wave, per head, the
+// running max, running sum and unnormalised output.
+template <int NW>
+struct MergeLds {
+    float o[NW][kMaxGqa][kHeadDim];
+    float m[NW][kMaxGqa];
+    float l[NW][kMaxGqa];
+};
+
+// Merge the NW waves' (m, l, o) of one workgroup in wave order and write the
+// result (the output when nsplit == 1, else this split's partial).  Uses the
+// first 256 threads: 16 per head, 8 channels each.
+template <int DT, int NW>
+__device__ void merge_waves_and_store(const AttnArgs &a, const MergeLds<NW> &sm, int pair,
+                                      int split) {
+    const int tid = threadIdx.x;
+    const int h = tid >> 4;
+    const int c0 = (tid & 15) * 8;
+    if (tid >= 256 || h >= a.gqa) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.m[w][h]);
+    float wt[NW];
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        wt[w] = (M == -INFINITY) ? 0.f : exp2f(sm.m[w][h] - M);
+        L += wt[w] * sm.l[w][h];
+    }
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) acc += wt[w] * sm.o[w][h][c0 + e];
+        o[e] = acc;
+    }
+    const int b = pair / a.hkv, g = pair % a.hkv;
+    const int hq = a.hkv * a.gqa;
+    const size_t row = (size_t)b * hq + (size_t)g * a.gqa + h;
+    if (a.nsplit == 1) {
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        if (DT == KIN_BF16) {
+            u32x4 w4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                w4[e] = f32_to_bf16_bits(o[2 * e] * inv) | (f32_to_bf16_bits(o[2 * e + 1] * inv) << 16);
+            *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.out) + row * kHeadDim + c0) = w4;
+        } else {
+            f32x4 *p = reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + row * kHeadDim + c0);
+            p[0] = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+            p[1] = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+        }
+    } else {
+        const size_t prow = row * a.nsplit + split;
+        f32x4 *p = reinterpret_cast<f32x4 *>(a.ws_o + prow * kHeadDim + c0);
+        p[0] = f32x4{o[0], o[1], o[2], o[3]};
+        p[1] = f32x4{o[4], o[5], o[6], o[7]};
+        if ((tid & 15) == 0) {
+            a.ws_ml[prow * 2 + 0] = M;
+            a.ws_ml[prow * 2 + 1] = L;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bf16, MFMA
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 16-bit half `n & 1` of dword `n >> 1` of a and b, packed (a low, b high)
+__device__ __forceinline__ uint32_t pick_pair(const u32x4 &a, const u32x4 &b, int n) {
+    const uint32_t x = a[n >> 1], y = b[n >> 1];
+    return (n & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
+}
+
+// The loads of one 32-token chunk held by one lane.
+struct ChunkRegs {
+    u32x4 k[2][4];  // K rows 16*tau + j, channels 32*kk + 8*g4 .. +8
+    u32x4 v[8];     // V rows 16*tau + 4*g4 + r (e = 4*tau + r), channels 8j .. 8j+7
+    uint32_t ok;    // bit e: token of V row e is a kept token inside the context
+};
+
+struct WaveState {
+    f32x4 o[8];   // o[n][r]: head 4*g4 + r, channel 8*j + n
+    float m_run;  // running max of head j (log2 units)
+    float l_run;  // this lane's share of the running sum of head j
+};
+
+template <bool DENSE>
+__device__ __forceinline__ void load_chunk(const AttnArgs &a, const int32_t *sel,
+                                           const uint16_t *Kp, const uint16_t *Vp, int c, int j,
+                                           int g4, ChunkRegs &cr) {
+    cr.ok = 0;
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+        bool valid;
+        const int base = run_base<DENSE>(a, sel, c * kChunkBf16 + 16 * tau, valid);
+        const int tk = base + j;
+        const int rowk = (valid && tk < a.ctx_len) ? tk : 0;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            cr.k[tau][kk] = ld_nt16(Kp + (size_t)rowk * kHeadDim + 32 * kk + 8 * g4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int tv = base + 4 * g4 + r;
+            const bool ok = valid && tv < a.ctx_len;
+            cr.ok |= (ok ? 1u : 0u) << (4 * tau + r);
+            cr.v[4 * tau + r] = ld_nt16(Vp + (size_t)(ok ? tv : 0) * kHeadDim + 8 * j);
+        }
+    }
+}
+
+__device__ __forceinline__ void compute_chunk(const ChunkRegs &cr, const bf16x8 (&qb)[4],
+                                              float scale_log2, int g4, WaveState &st) {
+    float s[8];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cr.k[tau][kk]), qb[kk], acc,
+                                                         0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            s[4 * tau + r] = ((cr.ok >> (4 * tau + r)) & 1u) ? acc[r] * scale_log2 : -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(st.m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(st.m_run - m_use);  // 0 while nothing was seen
+
+    uint32_t pw[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t b0 = f32_to_bf16_bits(exp2f(s[2 * e] - m_use));
+        const uint32_t b1 = f32_to_bf16_bits(exp2f(s[2 * e + 1] - m_use));
+        psum += __uint_as_float(b0 << 16) + __uint_as_float(b1 << 16);
+        pw[e] = b0 | (b1 << 16);
+    }
+    st.l_run = st.l_run * alpha + psum;
+    st.m_run = m_new;
+
+    // rescale O rows (heads 4*g4 + r) by their heads' alpha
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(alpha, 4 * g4 + r);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) st.o[n][r] *= ar;
+    }
+    const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+        const u32x4 vb = {pick_pair(cr.v[0], cr.v[1], n), pick_pair(cr.v[2], cr.v[3], n),
+                          pick_pair(cr.v[4], cr.v[5], n), pick_pair(cr.v[6], cr.v[7], n)};
+        st.o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, as_bf16x8(vb), st.o[n], 0, 0, 0);
+    }
+}
+
+// One wave's share of a pair's chunks [c_beg, c_end), every `step`-th chunk
+// starting at c_beg + first, then its (m, l, o) into merge slot `slot`.
+template <bool DENSE, int NW>
+__device__ void attend_bf16(const AttnArgs &a, const int32_t *sel, int pair, int c_beg,
+                            int c_end, int first, int step, int slot, MergeLds<NW> &sm) {
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 15, g4 = lane >> 4;
+    const int b = pair / a.hkv, gk = pair % a.hkv;
+    const int hq = a.hkv * a.gqa;
+    const uint16_t *Kp = static_cast<const uint16_t *>(a.K) + (size_t)pair * a.t_cap * kHeadDim;
+    const uint16_t *Vp = static_cast<const uint16_t *>(a.V) + (size_t)pair * a.t_cap * kHeadDim;
+
+    // B operand of S^T = K . Q^T: head j, channels 32*kk + 8*g4 .. +8
+    bf16x8 qb[4];
+    {
+        const bool live = j < a.gqa;
+        const uint16_t *qp = static_cast<const uint16_t *>(a.q) +
+                             ((size_t)b * hq + (size_t)gk * a.gqa + (live ? j : 0)) * kHeadDim;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            u32x4 v = *reinterpret_cast<const u32x4 *>(qp + 32 * kk + 8 * g4);
+            if (!live) v = u32x4{0u, 0u, 0u, 0u};
+            qb[kk] = as_bf16x8(v);
+        }
+    }
+    WaveState st;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) st.o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
+
+    // two register buffers: chunk i computes while chunk i + 1 loads.  The
+    // prefetch inside the loop is unconditional (the tail is peeled), so the
+    // wait before a chunk's math covers only that chunk's loads.
+    const int c0 = c_beg + first;
+    const int n = c0 < c_end ? (c_end - c0 + step - 1) / step : 0;
+    ChunkRegs ra, rb;
+    if (n > 0) {
+        load_chunk<DENSE>(a, sel, Kp, Vp, c0, j, g4, ra);
+        int i = 0;
+        for (; i + 2 < n; i += 2) {
+            load_chunk<DENSE>(a, sel, Kp, Vp, c0 + (i + 1) * step, j, g4, rb);
+            compute_chunk(ra, qb, a.scale_log2, g4, st);
+            load_chunk<DENSE>(a, sel, Kp, Vp, c0 + (i + 2) * step, j, g4, ra);
+            compute_chunk(rb, qb, a.scale_log2, g4, st);
+        }
+        if (n - i == 2) {
+            load_chunk<DENSE>(a, sel, Kp, Vp, c0 + (i + 1) * step, j, g4, rb);
+            compute_chunk(ra, qb, a.scale_log2, g4, st);
+            compute_chunk(rb, qb, a.scale_log2, g4, st);
+        } else {
+            compute_chunk(ra, qb, a.scale_log2, g4, st);
+        }
+    }
+
+    float l_tot = st.l_run + __shfl_xor(st.l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (lane < 16) {
+        sm.m[slot][lane] = st.m_run;
+        sm.l[slot][lane] = l_tot;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int n = 0; n < 8; ++n) sm.o[slot][4 * g4 + r][8 * j + n] = st.o[n][r];
+}
+
+// ---------------------------------------------------------------------------
+// fp32, VALU
+// ---------------------------------------------------------------------------
+
+// Order LDS writes of one wave before its following LDS reads (the lanes of
+// a wave run in lockstep and the LDS queue of a wave is in order; this only
+// keeps the compiler from moving accesses across the point).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int NW>
+struct F32Lds {
+    float q[kMaxGqa][kHeadDim];
+    float p[NW][kMaxGqa][kChunkF32];
+    int row[NW][kChunkF32];
+};
+
+// One wave's share of the chunks (64 tokens each) of a pair, fp32.
+template <bool DENSE, int NW>
+__device__ void attend_f32(const AttnArgs &a, const int32_t *sel, int pair, int c_beg, int c_end,
+                           int first, int step, int slot, F32Lds<NW> &fl, MergeLds<NW> &sm) {
+    const int lane = threadIdx.x & 63;
+    const int G = a.gqa;
+    const float *Kp = static_cast<const float *>(a.K) + (size_t)pair * a.t_cap * kHeadDim;
+    const float *Vp = static_cast<const float *>(a.V) + (size_t)pair * a.t_cap * kHeadDim;
+
+    float m_run[kMaxGqa], l_run[kMaxGqa], o0[kMaxGqa], o1[kMaxGqa];
+#pragma unroll
+    for (int h = 0; h < kMaxGqa; ++h) {
+        m_run[h] = -INFINITY;
+        l_run[h] = 0.f;
+        o0[h] = 0.f;
+        o1[h] = 0.f;
+    }
+    for (int c = c_beg + first; c < c_end; c += step) {
+        // this lane's token: list position c*64 + lane
+        const int p = c * kChunkF32 + lane;
+        bool ok;
+        int tok;
+        if (DENSE) {
+            tok = p;
+            ok = p < a.ctx_len;
+        } else {
+            const int slotp = p >> a.block_shift;
+            const int id = slotp < a.k ? sel[slotp] : -1;
+            tok = id * a.block + (p & (a.block - 1));
+            ok = id >= 0 && id < a.nb && tok < a.ctx_len;
+        }
+        const int row = ok ? tok : 0;
+        fl.row[slot][lane] = row;
+
+        float s[kMaxGqa];
+#pragma unroll
+        for (int h = 0; h < kMaxGqa; ++h) s[h] = 0.f;
+        const f32x4 *kr = reinterpret_cast<const f32x4 *>(Kp + (size_t)row * kHeadDim);
+        for (int c4 = 0; c4 < kHeadDim / 4; ++c4) {
+            const f32x4 kv = kr[c4];
+#pragma unroll
+            for (int h = 0; h < kMaxGqa; ++h) {
+                if (h < G) {
+                    s[h] = fmaf(fl.q[h][4 * c4 + 0], kv[0], s[h]);
+                    s[h] = fmaf(fl.q[h][4 * c4 + 1], kv[1], s[h]);
+                    s[h] = fmaf(fl.q[h][4 * c4 + 2], kv[2], s[h]);
+                    s[h] = fmaf(fl.q[h][4 * c4 + 3], kv[3], s[h]);
+                }
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < kMaxGqa; ++h) {
+            if (h >= G) continue;
+            const float z = ok ? s[h] * a.scale_log2 : -INFINITY;
+            float mx = z;
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
+            const float m_new = fmaxf(m_run[h], mx);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = exp2f(m_run[h] - m_use);
+            const float pz = exp2f(z - m_use);
+            l_run[h] = l_run[h] * alpha + pz;
+            o0[h] *= alpha;
+            o1[h] *= alpha;
+            m_run[h] = m_new;
+            fl.p[slot][h][lane] = pz;
+        }
+        wave_lds_sync();  // p / row entries of this wave are complete
+        // p . v: lane owns channels 2*lane, 2*lane+1
+        for (int t = 0; t < kChunkF32; ++t) {
+            const float2 v =
+                reinterpret_cast<const float2 *>(Vp + (size_t)fl.row[slot][t] * kHeadDim)[lane];
+#pragma unroll
+            for (int h = 0; h < kMaxGqa; ++h) {
+                if (h < G) {
+                    const float pt = fl.p[slot][h][t];
+                    o0[h] = fmaf(pt, v.x, o0[h]);
+                    o1[h] = fmaf(pt, v.y, o1[h]);
+                }
+            }
+        }
+        wave_lds_sync();  // every lane is done reading before the next chunk writes
+    }
+#pragma unroll
+    for (int h = 0; h < kMaxGqa; ++h) {
+        if (h >= G) continue;
+        float l = l_run[h];
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) l += __shfl_xor(l, d);
+        if (lane == 0) {
+            sm.m[slot][h] = m_run[h];
+            sm.l[slot][h] = l;
+        }
+        sm.o[slot][h][2 * lane] = o0[h];
+        sm.o[slot][h][2 * lane + 1] = o1[h];
+    }
+}
+
+template <int NW>
+__device__ void load_q_f32(const AttnArgs &a, int pair, F32Lds<NW> &fl) {
+    const int b = pair / a.hkv, gk = pair % a.hkv;
+    const int hq = a.hkv * a.gqa;
+    for (int i = threadIdx.x; i < kMaxGqa * kHeadDim; i += NW * 64) {
+        const int h = i / kHeadDim, c = i % kHeadDim;
+        fl.q[h][c] = h < a.gqa ? static_cast<const float *>(a.q)[((size_t)b * hq + gk * a.gqa + h) *
+                                                                 kHeadDim + c]
+                               : 0.f;
+    }
+}
+
+// Kernel arguments from a validated geometry and plan (host side).
+inline void fill_args(AttnArgs &a, const Geo &g, const AttnPlan &p, const void *q, const void *K,
+                      const void *V, const int32_t *idx, int k, void *out, void *ws) {
+    a.q = q;
+    a.K = K;
+    a.V = V;
+    a.idx = idx;
+    a.out = out;
+    a.ws_o = static_cast<float *>(ws);
+    a.ws_ml = p.nsplit > 1 ? a.ws_o + (size_t)g.batch * g.hq * p.nsplit * kHeadDim : nullptr;
+    a.hkv = g.hkv;
+    a.gqa = g.gqa;
+    a.t_cap = g.t_cap;
+    a.ctx_len = g.ctx_len;
+    a.block = g.block;
+    a.block_shift = __builtin_ctz((unsigned)g.block);
+    a.nb = g.nb;
+    a.k = k;
+    a.nsplit = p.nsplit;
+    a.n_chunks = p.n_chunks;
+    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kHeadDim));
+}
+
+}  // namespace kin

@@ -94,6 +94,24 @@ kin_status launched(hipError_t e, const char *what) {
 
 }  // namespace
 
+// Shared checks of the decode-step entry points.
+static kin_status check_step(const kin_desc *desc, kin::Geo *g) {
+    kin_status st = check_desc(desc, g);
+    if (st != KIN_OK) return st;
+    if (g->nb > kin::kMaxBlocks)
+        return fail(KIN_ERR_UNSUPPORTED, "%d blocks: at most %d", g->nb, kin::kMaxBlocks);
+    return KIN_OK;
+}
+
+static kin_status check_ws(const kin::AttnPlan &p, const void *ws, size_t ws_bytes) {
+    if (p.ws_bytes == 0) return KIN_OK;
+    if (!ws) return fail(KIN_ERR_NULL, "ws is NULL but %zu bytes are needed", p.ws_bytes);
+    if (!aligned16(ws)) return fail(KIN_ERR_ALIGN, "ws is not 16-byte aligned");
+    if (ws_bytes < p.ws_bytes)
+        return fail(KIN_ERR_WORKSPACE, "ws has %zu bytes, %zu needed", ws_bytes, p.ws_bytes);
+    return KIN_OK;
+}
+
 extern "C" {
 
 kin_status kin_block_summary_update(const kin_desc *desc, const void *K, void *S,
@@ -156,12 +174,8 @@ static kin_status attention(const kin_desc *desc, const void *q, const void *K, 
         if (k < 1) return fail(KIN_ERR_SHAPE, "k = %d: need k >= 1", k);
     }
     const kin::AttnPlan p = kin::plan_attention(g, dense ? 0 : k, dense, num_cu());
-    if (p.ws_bytes > 0) {
-        if (!ws) return fail(KIN_ERR_NULL, "ws is NULL but %zu bytes are needed", p.ws_bytes);
-        if (!aligned16(ws)) return fail(KIN_ERR_ALIGN, "ws is not 16-byte aligned");
-        if (ws_bytes < p.ws_bytes)
-            return fail(KIN_ERR_WORKSPACE, "ws has %zu bytes, %zu needed", ws_bytes, p.ws_bytes);
-    }
+    st = check_ws(p, ws, ws_bytes);
+    if (st != KIN_OK) return st;
     return launched(kin::launch_attention(g, p, q, K, V, dense ? nullptr : idx, k, out, ws,
                                           (hipStream_t)stream),
                     dense ? "kin_dense_decode_attn" : "kin_sparse_decode_attn");
@@ -179,13 +193,47 @@ kin_status kin_dense_decode_attn(const kin_desc *desc, const void *q, const void
     return attention(desc, q, K, V, nullptr, 0, out, ws, ws_bytes, stream, true);
 }
 
+kin_status kin_decode_update_score(const kin_desc *desc, const void *q, const void *K, void *S,
+                                   double *scores, kin_stream stream) {
+    kin::Geo g;
+    kin_status st = check_step(desc, &g);
+    if (st != KIN_OK) return st;
+    KIN_REQUIRE_PTR(q);
+    KIN_REQUIRE_PTR(K);
+    KIN_REQUIRE_PTR(S);
+    KIN_REQUIRE_PTR(scores);
+    return launched(kin::launch_update_and_score(g, q, K, S, scores, (hipStream_t)stream),
+                    "kin_decode_update_score");
+}
+
+kin_status kin_decode_select_attend(const kin_desc *desc, const void *q, const void *K,
+                                    const void *V, const double *scores, int32_t k, int32_t *idx,
+                                    void *out, void *ws, size_t ws_bytes, kin_stream stream) {
+    kin::Geo g;
+    kin_status st = check_step(desc, &g);
+    if (st != KIN_OK) return st;
+    KIN_REQUIRE_PTR(q);
+    KIN_REQUIRE_PTR(K);
+    KIN_REQUIRE_PTR(V);
+    KIN_REQUIRE_PTR(scores);
+    KIN_REQUIRE_PTR(idx);
+    KIN_REQUIRE_PTR(out);
+    if (k < 1) return fail(KIN_ERR_SHAPE, "k = %d: need k >= 1", k);
+    const kin::AttnPlan p = kin::plan_step(g, k, num_cu());
+    st = check_ws(p, ws, ws_bytes);
+    if (st != KIN_OK) return st;
+    return launched(kin::launch_select_attend(g, p, q, K, V, scores, k, idx, out, ws,
+                                              (hipStream_t)stream),
+                    "kin_decode_select_attend");
+}
+
 kin_status kin_sparse_decode_step(const kin_desc *desc, const void *q, const void *K,
                                   const void *V, void *S, double *scores, int32_t k,
                                   int32_t *idx, void *out, void *ws, size_t ws_bytes,
                                   kin_stream stream) {
     // check everything before enqueueing anything
     kin::Geo g;
-    kin_status st = check_desc(desc, &g);
+    kin_status st = check_step(desc, &g);
     if (st != KIN_OK) return st;
     KIN_REQUIRE_PTR(q);
     KIN_REQUIRE_PTR(K);
@@ -195,28 +243,30 @@ kin_status kin_sparse_decode_step(const kin_desc *desc, const void *q, const voi
     KIN_REQUIRE_PTR(idx);
     KIN_REQUIRE_PTR(out);
     if (k < 1) return fail(KIN_ERR_SHAPE, "k = %d: need k >= 1", k);
-    if (g.nb > kin::kMaxBlocks)
-        return fail(KIN_ERR_UNSUPPORTED, "%d blocks: at most %d", g.nb, kin::kMaxBlocks);
-    const kin::AttnPlan p = kin::plan_attention(g, k, false, num_cu());
-    if (p.ws_bytes > 0) {
-        if (!ws) return fail(KIN_ERR_NULL, "ws is NULL but %zu bytes are needed", p.ws_bytes);
-        if (!aligned16(ws)) return fail(KIN_ERR_ALIGN, "ws is not 16-byte aligned");
-        if (ws_bytes < p.ws_bytes)
-            return fail(KIN_ERR_WORKSPACE, "ws has %zu bytes, %zu needed", ws_bytes, p.ws_bytes);
-    }
     hipStream_t s = (hipStream_t)stream;
-    const int jn = (g.ctx_len - 1) / g.block;
-    hipError_t e = kin::launch_block_summary(g, K, S, jn, jn + 1, s);
-    if (e == hipSuccess) e = kin::launch_block_score(g, q, S, scores, s);
-    if (e == hipSuccess) e = kin::launch_block_topk(g, scores, k, idx, s);
-    if (e == hipSuccess) e = kin::launch_attention(g, p, q, K, V, idx, k, out, ws, s);
+    const int cu = num_cu();
+    if (kin::step_single_kernel(g, k, cu))
+        return launched(kin::launch_decode_step(g, q, K, V, S, scores, k, idx, out, s),
+                        "kin_sparse_decode_step");
+    const kin::AttnPlan p = kin::plan_step(g, k, cu);
+    st = check_ws(p, ws, ws_bytes);
+    if (st != KIN_OK) return st;
+    hipError_t e = kin::launch_update_and_score(g, q, K, S, scores, s);
+    if (e == hipSuccess) e = kin::launch_select_attend(g, p, q, K, V, scores, k, idx, out, ws, s);
     return launched(e, "kin_sparse_decode_step");
 }
 
 size_t kin_sparse_ws_bytes(const kin_desc *desc, int32_t k) {
     kin::Geo g;
-    if (check_desc(desc, &g) != KIN_OK || k < 1) return (size_t)-1;
-    return kin::plan_attention(g, k, false, num_cu()).ws_bytes;
+    if (check_desc(desc, &g) != KIN_OK) return (size_t)-1;
+    if (k < 1) {
+        fail(KIN_ERR_SHAPE, "k = %d: need k >= 1", k);
+        return (size_t)-1;
+    }
+    const int cu = num_cu();
+    const size_t a = kin::plan_attention(g, k, false, cu).ws_bytes;
+    const size_t b = kin::plan_step(g, k, cu).ws_bytes;
+    return a > b ? a : b;
 }
 
 size_t kin_dense_ws_bytes(const kin_desc *desc) {

@@ -26,6 +26,7 @@ struct AttnPlan {
     int n_tokens;  // length of each pair's token list (kept blocks x block, or ctx_len)
     int n_chunks;  // ceil(n_tokens / chunk)
     int nsplit;    // workgroups per (sequence, KV head)
+    int fused;     // decode step: selection and attention in one kernel
     size_t ws_bytes;
 };
 
@@ -35,11 +36,25 @@ hipError_t launch_block_summary(const Geo &g, const void *K, void *S, int j0, in
                                 hipStream_t s);
 hipError_t launch_block_score(const Geo &g, const void *q, const void *S, double *scores,
                               hipStream_t s);
+// decode step, first half: newest-block summary update + all block scores
+hipError_t launch_update_and_score(const Geo &g, const void *q, const void *K, void *S,
+                                   double *scores, hipStream_t s);
 hipError_t launch_block_topk(const Geo &g, const double *scores, int k, int32_t *idx,
                              hipStream_t s);
 hipError_t launch_attention(const Geo &g, const AttnPlan &p, const void *q, const void *K,
                             const void *V, const int32_t *idx, int k, void *out, void *ws,
                             hipStream_t s);
+// decode step, second half: top-k selection + sparse attention, fused per
+// pair when the plan allows it (plan_step); otherwise separate launches
+AttnPlan plan_step(const Geo &g, int k, int num_cu);
+hipError_t launch_select_attend(const Geo &g, const AttnPlan &p, const void *q, const void *K,
+                                const void *V, const double *scores, int k, int32_t *idx,
+                                void *out, void *ws, hipStream_t s);
+// the whole decode step in one kernel (one workgroup per pair); usable when
+// step_single_kernel() says so (bf16, enough pairs to cover the chip)
+bool step_single_kernel(const Geo &g, int k, int num_cu);
+hipError_t launch_decode_step(const Geo &g, const void *q, const void *K, const void *V, void *S,
+                              double *scores, int k, int32_t *idx, void *out, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // device helpers (bf16 is carried as its raw 16 bits)
@@ -48,9 +63,10 @@ hipError_t launch_attention(const Geo &g, const AttnPlan &p, const void *q, cons
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// One 16-byte global load of streamed (read-once) data.
-__device__ __forceinline__ u32x4 ld_stream16(const void *p) {
-    return *reinterpret_cast<const u32x4 *>(p);
+// One 16-byte global load of data read once (nontemporal hint: streamed
+// through without displacing reusable lines).
+__device__ __forceinline__ u32x4 ld_nt16(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

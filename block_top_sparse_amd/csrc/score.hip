@@ -1,4 +1,5 @@
-// score.hip -- K2: block scores.
+// score.hip -- K2: block scores (and, in the decode-step form, the summary
+// update of the newest block fused in front of them).
 //
 // The group score of block j for (sequence b, KV head g) is
 //     sigma_j = sum_{h : h / gqa == g} q_h . s_j = (sum_h q_h) . s_j
@@ -13,149 +14,121 @@
 // as a pure HBM stream:
 //   - 16 lanes own one block row, 8 channels (16 B of bf16 / 32 B of fp32)
 //     per lane, so one wave load covers 4 whole consecutive rows (1 KiB of
-//     bf16) and a wave keeps TPW x 4 such loads in flight;
+//     bf16); a wave issues all TPW x 4 loads of its rows before any math,
+//     with the nontemporal hint (the rows are read once);
 //   - each lane forms its 8-term fp64 partial in a fixed order, and the 16
 //     partials of 4 blocks are folded with a reduce-scatter butterfly
 //     (xor 8, 4, 2, 1).  The summation tree is the same for every block, so
 //     two blocks with identical summaries get bit-identical scores and a tie
 //     between them is decided by index alone.
-#include "kin_internal.h"
+//
+// Decode-step form (UPDATE): workgroup x = 0 of each pair recomputes the
+// summary of the newest block (ctx_len - 1 lies in it), writes it to S and
+// scores it with the same per-lane math and the same butterfly; every other
+// workgroup scores its range of blocks and leaves the newest block alone.
+#include "score_impl.h"
 
 namespace kin {
 
-template <int DT, int TPW>
+template <int DT, int TPW, bool UPDATE>
 __global__ __launch_bounds__(256) void k_block_score(const void *__restrict__ qv,
-                                                     const void *__restrict__ Sv,
+                                                     const void *__restrict__ Kv, void *Sv,
                                                      double *__restrict__ scores, int hkv,
-                                                     int gqa, int nb_cap, int nb) {
+                                                     int gqa, int t_cap, int nb_cap, int nb,
+                                                     int ctx_len, int block) {
     constexpr int kBlocksPerWave = 16 * TPW;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int sub = lane & 15;  // channel slice: channels 8*sub .. 8*sub+7
     const int grp = lane >> 4;  // which of the 4 rows of a wave load
     const int pair = blockIdx.y;
     const int b = pair / hkv, g = pair % hkv;
-    const int hq = hkv * gqa;
+    const size_t row0 = (size_t)pair * nb_cap;
+    const int newest = nb - 1;
 
-    // (sum over the group's heads of q) for this lane's 8 channels, fp64
-    double qs[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qs[e] = 0.0;
-    for (int h = g * gqa; h < (g + 1) * gqa; ++h) {
-        const size_t qo = ((size_t)b * hq + h) * kHeadDim + 8 * sub;
-        if (DT == KIN_BF16) {
-            const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(qv) + qo);
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                qs[2 * e] += (double)bf16_lo(ww[e]);
-                qs[2 * e + 1] += (double)bf16_hi(ww[e]);
-            }
-        } else {
-            const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(qv) + qo);
-            const float4 a = p[0], c = p[1];
-            const float f[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qs[e] += (double)f[e];
+    if (UPDATE && blockIdx.x == 0) {
+        __shared__ uint32_t row_lds[kHeadDim];
+        if (wave == 0)
+            newest_summary<DT>(Kv, Sv, pair, t_cap, nb_cap, ctx_len, block, row_lds, lane);
+        __syncthreads();
+        if (wave != 0) return;
+        double qs[8];
+        group_query_sum<DT>(qv, b, g, hkv, gqa, sub, qs);
+        // the newest row sits in slot u = 0 of row group 0; the other slots
+        // are zero rows, so the butterfly is the one every block goes through
+        u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+        if (grp == 0) {
+            const uint32_t *r = row_lds + (DT == KIN_BF16 ? 4 : 8) * sub;
+            a = u32x4{r[0], r[1], r[2], r[3]};
+            if (DT != KIN_BF16) c = u32x4{r[4], r[5], r[6], r[7]};
         }
+        double part[4];
+        part[0] = slice_dot<DT>(qs, a, c);
+        part[1] = part[2] = part[3] = slice_dot<DT>(qs, u32x4{0u, 0u, 0u, 0u},
+                                                    u32x4{0u, 0u, 0u, 0u});
+        const double x = fold4(part, lane);
+        if (lane == 0) store_score(scores, row0 + newest, x);
+        return;
     }
 
-    const int wave_j0 = (blockIdx.x * 4 + wave) * kBlocksPerWave;
+    const int wave_j0 = ((blockIdx.x - (UPDATE ? 1 : 0)) * 4 + wave) * kBlocksPerWave;
     if (wave_j0 >= nb) return;
-    const size_t row0 = (size_t)pair * nb_cap;
+    double qs[8];
+    group_query_sum<DT>(qv, b, g, hkv, gqa, sub, qs);
 
+    // every row load of the wave is issued before any arithmetic
+    u32x4 wa[TPW][4], wb[TPW][4];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = min(wave_j0 + 16 * t + 4 * u + grp, nb - 1);
+            load_row_slice<DT>(Sv, row0 + j, sub, wa[t][u], wb[t][u]);
+        }
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-        const int tile_j0 = wave_j0 + 16 * t;
         double part[4];
-        // all 4 row loads of the tile are issued before any arithmetic
-        if (DT == KIN_BF16) {
-            u32x4 w[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int j = min(tile_j0 + 4 * u + grp, nb - 1);
-                w[u] = ld_stream16(static_cast<const uint16_t *>(Sv) + (row0 + j) * kHeadDim +
-                                   8 * sub);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t ww[4] = {w[u][0], w[u][1], w[u][2], w[u][3]};
-                double acc = 0.0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc = fma(qs[2 * e], (double)bf16_lo(ww[e]), acc);
-                    acc = fma(qs[2 * e + 1], (double)bf16_hi(ww[e]), acc);
-                }
-                part[u] = acc;
-            }
-        } else {
-            u32x4 w[4][2];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int j = min(tile_j0 + 4 * u + grp, nb - 1);
-                const float *p = static_cast<const float *>(Sv) + (row0 + j) * kHeadDim + 8 * sub;
-                w[u][0] = ld_stream16(p);
-                w[u][1] = ld_stream16(p + 4);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                float f[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    f[e] = __uint_as_float(w[u][0][e]);
-                    f[4 + e] = __uint_as_float(w[u][1][e]);
-                }
-                double acc = 0.0;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc = fma(qs[e], (double)f[e], acc);
-                part[u] = acc;
-            }
-        }
-        // reduce-scatter over the 16 lanes of a row: after xor 8 each lane
-        // keeps 2 of the 4 blocks, after xor 4 one; xor 2 and xor 1 finish.
-        const bool hi8 = (lane & 8) != 0, hi4 = (lane & 4) != 0;
-        const double send0 = hi8 ? part[0] : part[2];
-        const double send1 = hi8 ? part[1] : part[3];
-        const double r0 = __shfl_xor(send0, 8);
-        const double r1 = __shfl_xor(send1, 8);
-        const double w0 = (hi8 ? part[2] : part[0]) + r0;
-        const double w1 = (hi8 ? part[3] : part[1]) + r1;
-        const double r2 = __shfl_xor(hi4 ? w0 : w1, 4);
-        double x = (hi4 ? w1 : w0) + r2;
-        x += __shfl_xor(x, 2);
-        x += __shfl_xor(x, 1);
-        // lane holds block u = 2*hi8 + hi4 of its row group
-        const int u = (hi8 ? 2 : 0) + (hi4 ? 1 : 0);
-        const int j = tile_j0 + 4 * u + grp;
-        if ((lane & 3) == 0 && j < nb) {
-            if (x == 0.0) x = 0.0;  // one zero: -0.0 becomes +0.0
-            scores[row0 + j] = x;
-        }
+        for (int u = 0; u < 4; ++u) part[u] = slice_dot<DT>(qs, wa[t][u], wb[t][u]);
+        const double x = fold4(part, lane);
+        const int u = ((lane & 8) ? 2 : 0) + ((lane & 4) ? 1 : 0);
+        const int j = wave_j0 + 16 * t + 4 * u + grp;
+        if ((lane & 3) == 0 && j < nb && !(UPDATE && j == newest))
+            store_score(scores, row0 + j, x);
     }
 }
 
-template <int DT>
-static hipError_t launch_tpw(const Geo &g, const void *q, const void *S, double *scores,
-                             hipStream_t s) {
-    // blocks per workgroup = 4 waves x 16 x TPW; keep >= ~4 workgroups per
-    // CU-sized slice of the grid when the problem is small
+template <int DT, bool UPDATE>
+static hipError_t launch_dt(const Geo &g, const void *q, const void *K, void *S, double *scores,
+                            hipStream_t s) {
+    // blocks per workgroup = 4 waves x 16 x TPW; smaller workgroups when the
+    // problem is small so the grid still covers the chip
     const long long total = (long long)g.pairs * g.nb;
-    if (total >= 2048LL * 256) {
-        dim3 grid((g.nb + 255) / 256, g.pairs);
-        k_block_score<DT, 4><<<grid, 256, 0, s>>>(q, S, scores, g.hkv, g.gqa, g.nb_cap, g.nb);
-    } else if (total >= 2048LL * 128) {
-        dim3 grid((g.nb + 127) / 128, g.pairs);
-        k_block_score<DT, 2><<<grid, 256, 0, s>>>(q, S, scores, g.hkv, g.gqa, g.nb_cap, g.nb);
-    } else {
-        dim3 grid((g.nb + 63) / 64, g.pairs);
-        k_block_score<DT, 1><<<grid, 256, 0, s>>>(q, S, scores, g.hkv, g.gqa, g.nb_cap, g.nb);
-    }
+    const int extra = UPDATE ? 1 : 0;
+#define KIN_SCORE_LAUNCH(TPW)                                                                    \
+    k_block_score<DT, TPW, UPDATE><<<dim3((g.nb + 64 * TPW - 1) / (64 * TPW) + extra, g.pairs), \
+                                     256, 0, s>>>(q, K, S, scores, g.hkv, g.gqa, g.t_cap,         \
+                                                  g.nb_cap, g.nb, g.ctx_len, g.block)
+    if (total >= 2048LL * 256)
+        KIN_SCORE_LAUNCH(4);
+    else if (total >= 2048LL * 128)
+        KIN_SCORE_LAUNCH(2);
+    else
+        KIN_SCORE_LAUNCH(1);
+#undef KIN_SCORE_LAUNCH
     return hipGetLastError();
 }
 
 hipError_t launch_block_score(const Geo &g, const void *q, const void *S, double *scores,
                               hipStream_t s) {
-    return g.dtype == KIN_BF16 ? launch_tpw<KIN_BF16>(g, q, S, scores, s)
-                               : launch_tpw<KIN_F32>(g, q, S, scores, s);
+    void *Sm = const_cast<void *>(S);  // not written without UPDATE
+    return g.dtype == KIN_BF16 ? launch_dt<KIN_BF16, false>(g, q, nullptr, Sm, scores, s)
+                               : launch_dt<KIN_F32, false>(g, q, nullptr, Sm, scores, s);
+}
+
+hipError_t launch_update_and_score(const Geo &g, const void *q, const void *K, void *S,
+                                   double *scores, hipStream_t s) {
+    return g.dtype == KIN_BF16 ? launch_dt<KIN_BF16, true>(g, q, K, S, scores, s)
+                               : launch_dt<KIN_F32, true>(g, q, K, S, scores, s);
 }
 
 }  // namespace kin

@@ -1,0 +1,280 @@
+// select.h -- device-side top-k block selection for one (sequence, KV head)
+// pair, run by one whole workgroup of NT threads.
+//
+// The kept set is the k blocks with the largest group scores
+// (torch.topk over the per-block mean scores in BlockTopKAttention, skill
+// summary "Kinetics: Memory-Aware Test-Time Scaling", Implementation; k is
+// counted in blocks, rebuttal "Kinetics: Rethinking Test-Time Scaling Law",
+// Q4 "KV block size and grouping strategy").  Ties keep the lower block
+// index, and the indices are written in ascending order (the order the
+// attention kernel walks the cache).
+//
+// Method: the pair's scores are held in registers (KPT per thread, block
+// j = e * NT + tid).  Each fp64 score maps to an unsigned 64-bit key with
+// the same order (flip all bits of negatives, set the sign bit of the
+// rest).  An MSD radix select finds the k-th largest key: the first pass
+// ranks keys by the distance of their sign+exponent field below the
+// largest one (so one pass fixes the exponent of the k-th key), the later
+// ones take the mantissa 8 bits at a time.  Each pass builds an LDS
+// histogram of the digit among the keys that still match the prefix (one
+// LDS atomic per candidate), then EVERY wave scans the 256 bins itself
+// (a DPP prefix sum, lane broadcasts by readlane), so a pass costs a single
+// barrier: three histogram buffers rotate, and the
+// buffer for pass p+1 is cleared during pass p (its last readers finished
+// before the barrier of pass p-1).  The select stops as soon as the bin
+// holding the k-th key holds exactly the keys still needed; if all 64 bits
+// are used up, the remaining equal keys are exact ties and the lowest
+// indices among them are kept.  The kept flags are compacted in block order
+// with ballot + mbcnt ranks and a scan of the per-wave counts that every
+// wave repeats (one barrier).
+#pragma once
+
+#include "kin_internal.h"
+
+namespace kin {
+
+template <int KPT, int NT>
+struct SelectLds {
+    uint32_t hist[3][256];
+    uint32_t cnt[KPT * (NT / 64)];
+    uint32_t cnt_tie[KPT * (NT / 64)];
+    uint32_t wave_top[NT / 64];  // per wave: largest sign+exponent field of its keys
+};
+
+__device__ __forceinline__ uint64_t order_key(double s) {
+    if (s == 0.0) s = 0.0;  // -0.0 and +0.0 are one score
+    const uint64_t u = (uint64_t)__double_as_longlong(s);
+    return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
+}
+
+__device__ __forceinline__ uint32_t rank_below(uint64_t mask) {
+    // number of set bits of mask in lanes below this one
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Value of v in lane `src` (src uniform across the wave): a scalar read of
+// one lane, no LDS round trip.
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, int src) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, src);
+}
+
+// Inclusive prefix sum over the 64 lanes with DPP moves (row shifts inside
+// each 16-lane row, then row broadcasts of lanes 15 and 31); lanes with no
+// source add the 0 held in `old`.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return v;
+}
+
+// Largest value over the 64 lanes (DPP row shifts, then row broadcasts; the
+// result is read from lane 63).
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
+    return lane_value(v, 63);
+}
+
+// Every wave: the exclusive prefix, in (e, wave) order, of cnt[e * NW + w]
+// at position (e, my_wave), for each e < KPT.  n = KPT * NW entries.
+template <int KPT, int NW>
+__device__ __forceinline__ void offsets_of(const uint32_t *cnt, int wave, int lane,
+                                           uint32_t (&off)[KPT]) {
+    constexpr int N = KPT * NW;
+    uint32_t carry = 0;
+#pragma unroll
+    for (int base = 0; base < N; base += 64) {
+        const int i = base + lane;
+        const uint32_t v = i < N ? cnt[i] : 0u;
+        const uint32_t incl = wave_incl_scan(v);
+        const uint32_t excl = carry + incl - v;
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const int at = e * NW + wave;
+            if (at >= base && at < base + 64) off[e] = lane_value(excl, at - base);
+        }
+        carry += lane_value(incl, 63);
+    }
+}
+
+// Write out[0..k): the min(k, nb) selected block indices ascending, then -1.
+// sc: the pair's scores (nb entries; global memory or LDS).  Every thread of
+// the workgroup calls this; it ends without a barrier, so callers
+// synchronise before other waves read `out`.
+template <int KPT, int NT>
+__device__ void select_topk(const double *__restrict__ sc, int nb, int k, int32_t *out,
+                            SelectLds<KPT, NT> &lds) {
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int keff = min(k, nb);
+
+    for (int i = keff + tid; i < k; i += NT) out[i] = -1;
+    if (keff == nb) {  // every block is kept
+        for (int i = tid; i < nb; i += NT) out[i] = i;
+        return;
+    }
+
+    uint64_t key[KPT];
+    uint32_t top = 0;  // largest sign+exponent field (key >> 52) of this lane
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+        const int j = e * NT + tid;
+        key[e] = j < nb ? order_key(sc[j]) : 0ull;  // 0 is below every finite key
+        top = max(top, (uint32_t)(key[e] >> 52));
+    }
+    top = wave_max(top);
+    if (lane == 0) lds.wave_top[wave] = top;
+    for (int i = tid; i < 256; i += NT) lds.hist[0][i] = 0u;
+    __syncthreads();
+    top = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) top = max(top, lds.wave_top[w]);
+
+    // Pass 1 ranks keys by how far their sign+exponent field lies below the
+    // largest one (digit 255 - distance, clamped at 0): it fixes the
+    // exponent of the k-th key in one pass.  Later passes take the 52
+    // mantissa bits 8 at a time (the last one 4).  Should the k-th key fall
+    // into the clamped bin, the select restarts as a plain 8-bit MSD radix
+    // select over all 64 bits.
+    uint64_t prefix = 0, pmask = 0;
+    uint32_t krem = (uint32_t)keff;
+    bool resolved = false;  // true: every key matching `prefix` is kept
+    bool plain = false;     // restarted as the plain select
+    int buf = 0;
+    int lo = 52, width = 12;  // bit range of the current digit: [lo, lo + width)
+    for (;;) {
+        uint32_t *h = lds.hist[buf];
+        const int nbuf = buf == 2 ? 0 : buf + 1;
+        const bool first_pass = !plain && lo == 52;
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const bool cand = (e * NT + tid < nb) && ((key[e] & pmask) == prefix);
+            uint32_t dig;
+            if (first_pass) {
+                const uint32_t dist = top - (uint32_t)(key[e] >> 52);
+                dig = dist >= 255u ? 0u : 255u - dist;
+            } else {
+                dig = (uint32_t)(key[e] >> lo) & ((1u << width) - 1u);
+            }
+            if (cand) atomicAdd(&h[dig], 1u);
+        }
+        for (int i = tid; i < 256; i += NT) lds.hist[nbuf][i] = 0u;
+        __syncthreads();
+        // every wave: lane l holds bins 255-4l .. 252-4l (descending digits)
+        uint32_t c[4], sum = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            c[r] = h[255 - 4 * lane - r];
+            sum += c[r];
+        }
+        const uint32_t incl = wave_incl_scan(sum);
+        const uint32_t excl = incl - sum;
+        const uint64_t hit = __ballot(excl < krem && krem <= incl);
+        const int src = __builtin_ctzll(hit);
+        uint32_t run = excl, dsel = 0, above = 0, in_bin = 0;
+        bool found = false;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if (!found && run + c[r] >= krem) {
+                dsel = 255u - 4u * lane - r;
+                above = run;
+                in_bin = c[r];
+                found = true;
+            }
+            run += c[r];
+        }
+        dsel = lane_value(dsel, src);
+        above = lane_value(above, src);
+        in_bin = lane_value(in_bin, src);
+        buf = nbuf;
+        if (first_pass && dsel == 0u) {
+            // the k-th key is 255 or more exponent steps below the largest
+            plain = true;
+            lo = 56;
+            width = 8;
+            continue;
+        }
+        krem -= above;
+        if (first_pass) {
+            prefix = (uint64_t)(top - (255u - dsel)) << 52;
+            pmask = 0xFFFull << 52;
+        } else {
+            prefix |= (uint64_t)dsel << lo;
+            pmask |= (uint64_t)((1u << width) - 1u) << lo;
+        }
+        if (in_bin == krem) {
+            resolved = true;
+            break;
+        }
+        if (lo == 0) break;  // all 64 bits used: the rest are exact ties
+        if (first_pass) {
+            lo = 44;
+            width = 8;
+        } else if (lo >= 8) {
+            lo -= 8;
+        } else {
+            width = lo;
+            lo = 0;
+        }
+    }
+
+    // kept: key above the threshold prefix, or equal to it and (resolved, or
+    // among the first krem equal keys in block order)
+    bool keep[KPT];
+    if (resolved) {
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) keep[e] = (e * NT + tid < nb) && key[e] >= prefix;
+    } else {
+        // prefix is now the exact k-th key; rank the ties in block order
+        bool tie[KPT];
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            tie[e] = (e * NT + tid < nb) && key[e] == prefix;
+            const uint64_t m = __ballot(tie[e]);
+            if (lane == 0) lds.cnt_tie[e * NW + wave] = (uint32_t)__popcll(m);
+        }
+        __syncthreads();
+        uint32_t off[KPT];
+        offsets_of<KPT, NW>(lds.cnt_tie, wave, lane, off);
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const uint64_t m = __ballot(tie[e]);
+            const uint32_t r = off[e] + rank_below(m);
+            keep[e] = (e * NT + tid < nb) && (key[e] > prefix || (tie[e] && r < krem));
+        }
+    }
+
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+        const uint64_t m = __ballot(keep[e]);
+        if (lane == 0) lds.cnt[e * NW + wave] = (uint32_t)__popcll(m);
+    }
+    __syncthreads();
+    uint32_t off[KPT];
+    offsets_of<KPT, NW>(lds.cnt, wave, lane, off);
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+        const uint64_t m = __ballot(keep[e]);
+        const uint32_t pos = off[e] + rank_below(m);
+        if (keep[e] && pos < (uint32_t)keff) out[pos] = e * NT + tid;
+    }
+}
+
+// Keys per thread for nb blocks over nt threads, rounded up to an
+// instantiated power of two (nb <= 32 * nt).
+__host__ __device__ inline int select_kpt(int nb, int nt) {
+    const int kpt = (nb + nt - 1) / nt;
+    return kpt <= 1 ? 1 : kpt <= 2 ? 2 : kpt <= 4 ? 4 : kpt <= 8 ? 8 : kpt <= 16 ? 16 : 32;
+}
+
+}  // namespace kin

@@ -139,18 +139,41 @@ KIN_API kin_status kin_dense_decode_attn(const kin_desc *desc, const void *q, co
                                  const void *V, void *out, void *ws, size_t ws_bytes,
                                  kin_stream stream);
 
-/* One whole sparse decode step, enqueued back to back on `stream`:
- * summary update of the newest block ([ctx_len-1, ctx_len)), scores, top-k
- * and sparse attention.  S is updated in place; scores and idx are written
- * as by the individual calls (they are the step's intermediate results). */
+/* The two halves of a decode step, each one fused kernel.
+ * kin_decode_update_score = kin_block_summary_update over
+ * [ctx_len-1, ctx_len) followed by kin_block_score (the newest block's
+ * summary is rebuilt and scored in the same launch as every other block).
+ * kin_decode_select_attend = kin_block_topk followed by
+ * kin_sparse_decode_attn (each pair's workgroup selects its blocks into LDS
+ * and attends over them; idx still receives the selection).  Workspace as
+ * for kin_sparse_decode_attn (kin_sparse_ws_bytes).  Same errors as the
+ * calls they stand for. */
+KIN_API kin_status kin_decode_update_score(const kin_desc *desc, const void *q, const void *K,
+                                           void *S, double *scores, kin_stream stream);
+KIN_API kin_status kin_decode_select_attend(const kin_desc *desc, const void *q, const void *K,
+                                            const void *V, const double *scores, int32_t k,
+                                            int32_t *idx, void *out, void *ws, size_t ws_bytes,
+                                            kin_stream stream);
+
+/* One whole sparse decode step, enqueued on `stream`: summary update of
+ * the newest block ([ctx_len-1, ctx_len)), scores, top-k and sparse
+ * attention, with the same results as those four calls in sequence.  S is
+ * updated in place; scores and idx receive the step's intermediate
+ * results.  With bf16 data and at least as many (sequence, KV head) pairs
+ * as the device has compute units it is ONE kernel (a workgroup per pair
+ * runs all four steps, the scores never leave LDS before the selection);
+ * otherwise it is kin_decode_update_score then kin_decode_select_attend
+ * (two kernels, plus a combine pass when a pair's kept blocks are split
+ * over several workgroups). */
 KIN_API kin_status kin_sparse_decode_step(const kin_desc *desc, const void *q, const void *K,
                                   const void *V, void *S, double *scores, int32_t k,
                                   int32_t *idx, void *out, void *ws, size_t ws_bytes,
                                   kin_stream stream);
 
 /* Workspace sizes in bytes (0 when none is needed); -1 cast to size_t on
- * a bad descriptor.  Sizes depend on the current device's compute-unit
- * count: query them on the device the calls will run on. */
+ * a bad descriptor.  kin_sparse_ws_bytes covers both kin_sparse_decode_attn
+ * and kin_sparse_decode_step.  Sizes depend on the current device's
+ * compute-unit count: query them on the device the calls will run on. */
 KIN_API size_t kin_sparse_ws_bytes(const kin_desc *desc, int32_t k);
 KIN_API size_t kin_dense_ws_bytes(const kin_desc *desc);
 

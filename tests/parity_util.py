@@ -32,17 +32,38 @@ def gpu_inputs(w, tail_fill=float("nan")):
     return synth.make_inputs(w, device="cuda", tail_fill=tail_fill)
 
 
-def run_gpu(w, inp, k=None, dense=False, stream=None, prefill=True, bufs=None):
-    """Prefill summaries, then scores -> top-k -> sparse attention (and dense)."""
+def run_gpu(w, inp, k=None, dense=False, stream=None, prefill=True, bufs=None, fused=False,
+            step=False):
+    """Prefill summaries, then scores -> top-k -> sparse attention (and dense).
+    fused: the decode-step halves instead (newest-block update + scores in
+    one launch, top-k + attention in the next); step: kin_sparse_decode_step
+    (one kernel when there are at least as many pairs as CUs)."""
     bufs = bufs or LayerBuffers(w, k=k, with_dense=dense)
     d = bufs.desc
     bufs.out.fill_(float("nan"))  # every output must be written
-    if prefill:
-        kb.kin_block_summary_update(d, inp["K"], bufs.S, 0, w.ctx_len, stream=stream)
-    kb.kin_block_score(d, inp["q"], bufs.S, bufs.scores, stream=stream)
-    kb.kin_block_topk(d, bufs.scores, bufs.k, bufs.idx, stream=stream)
-    kb.kin_sparse_decode_attn(d, inp["q"], inp["K"], inp["V"], bufs.idx, bufs.k, bufs.out,
-                              bufs.ws, stream=stream)
+    bufs.idx.fill_(-7)
+    bufs.scores.fill_(float("nan"))
+    if fused or step:
+        # summaries of every block but the newest come from the prefill; the
+        # newest is rebuilt by the step itself
+        newest0 = (w.nb - 1) * w.block
+        if prefill and newest0 > 0:
+            kb.kin_block_summary_update(d, inp["K"], bufs.S, 0, newest0, stream=stream)
+        if step:
+            kb.kin_sparse_decode_step(d, inp["q"], inp["K"], inp["V"], bufs.S, bufs.scores,
+                                      bufs.k, bufs.idx, bufs.out, bufs.ws, stream=stream)
+        else:
+            kb.kin_decode_update_score(d, inp["q"], inp["K"], bufs.S, bufs.scores,
+                                       stream=stream)
+            kb.kin_decode_select_attend(d, inp["q"], inp["K"], inp["V"], bufs.scores, bufs.k,
+                                        bufs.idx, bufs.out, bufs.ws, stream=stream)
+    else:
+        if prefill:
+            kb.kin_block_summary_update(d, inp["K"], bufs.S, 0, w.ctx_len, stream=stream)
+        kb.kin_block_score(d, inp["q"], bufs.S, bufs.scores, stream=stream)
+        kb.kin_block_topk(d, bufs.scores, bufs.k, bufs.idx, stream=stream)
+        kb.kin_sparse_decode_attn(d, inp["q"], inp["K"], inp["V"], bufs.idx, bufs.k, bufs.out,
+                                  bufs.ws, stream=stream)
     if dense:
         bufs.out_dense.fill_(float("nan"))
         kb.kin_dense_decode_attn(d, inp["q"], inp["K"], inp["V"], bufs.out_dense, bufs.ws_dense,

@@ -61,6 +61,62 @@ def test_small_cases_against_oracle(case):
     say(f"  ok {r}")
 
 
+FUSED = [
+    # name, batch, hq, hkv, ctx, block, k, dtype, t_cap
+    ("fused-bf16-many-pairs", 40, 32, 8, 4096, 16, 32, "bf16", 4096),   # one workgroup per pair
+    ("fused-bf16-few-pairs", 2, 16, 2, 8000, 16, 100, "bf16", 8192),    # split + combine
+    ("fused-bf16-ragged-b64", 3, 24, 3, 5000, 64, 20, "bf16", 5120),
+    ("fused-bf16-keepall", 2, 8, 2, 1000, 32, 40, "bf16", 1024),        # k > nb
+    ("fused-bf16-g1-k1", 2, 2, 2, 77, 16, 1, "bf16", 80),
+    ("fused-bf16-bigk-fallback", 1, 8, 2, 40000, 16, 2100, "bf16", 40000),  # k > LDS list
+    ("fused-f32-tiny", 1, 8, 2, 4096, 16, 32, "f32", 4096),
+    ("fused-f32-ragged", 2, 12, 2, 999, 32, 7, "f32", 1024),
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=[c[0] for c in FUSED])
+def test_fused_step_halves_against_oracle(case):
+    name, b, hq, hkv, L, B, k, dt, cap = case
+    w = Workload(name, batch=b, hq=hq, hkv=hkv, ctx_len=L, block=B, topk=k, dtype=dt,
+                 seed=zlib.crc32(name.encode()) % 10000, t_cap=cap)
+    say(f"case {name}: {w.describe()}")
+    inp = gpu_inputs(w)
+    bufs = run_gpu(w, inp, fused=True)
+    r = check_sequences(w, inp, bufs, range(b))
+    # the fused halves select exactly what the separate calls select
+    sep = run_gpu(w, inp)
+    assert torch.equal(sep.idx, bufs.idx)
+    assert torch.equal(bits(sep.S[:, :, :w.nb]), bits(bufs.S[:, :, :w.nb]))
+    say(f"  ok {r}")
+
+
+SINGLE = [
+    # name, batch, hq, hkv, ctx, block, k, dtype, t_cap  (>= 256 pairs: one kernel per step)
+    ("step-g4-b16-ragged", 64, 16, 4, 2000, 16, 20, "bf16", 2048),
+    ("step-g5-b32-k1", 32, 40, 8, 1111, 32, 1, "bf16", 1152),
+    ("step-g8-b64-kpast", 32, 64, 8, 700, 64, 15, "bf16", 704),      # k > nb
+    ("step-g1-b16-manyblk", 256, 1, 1, 60000, 16, 100, "bf16", 60000),  # nb 3750
+    ("step-g16-b128-short", 16, 256, 16, 100, 128, 2, "bf16", 128),  # a single partial block
+]
+
+
+@pytest.mark.parametrize("case", SINGLE, ids=[c[0] for c in SINGLE])
+def test_single_kernel_step_against_oracle(case):
+    name, b, hq, hkv, L, B, k, dt, cap = case
+    w = Workload(name, batch=b, hq=hq, hkv=hkv, ctx_len=L, block=B, topk=k, dtype=dt,
+                 seed=zlib.crc32(name.encode()) % 10000, t_cap=cap)
+    say(f"case {name}: {w.describe()}")
+    inp = gpu_inputs(w)
+    bufs = run_gpu(w, inp, step=True)
+    seqs = sorted({0, 1, b // 2, b - 1})
+    r = check_sequences(w, inp, bufs, seqs)
+    sep = run_gpu(w, inp)
+    assert torch.equal(sep.idx, bufs.idx)
+    assert torch.equal(bits(sep.S[:, :, :w.nb]), bits(bufs.S[:, :, :w.nb]))
+    assert torch.equal(sep.scores[:, :, :w.nb], bufs.scores[:, :, :w.nb])
+    say(f"  ok {r}")
+
+
 def test_tiny_workload_full_parity():
     w = workloads.TINY
     say(f"workload {w.name}")
@@ -145,6 +201,14 @@ def test_full_size_workloads(w):
     r = check_sequences(w, inp, bufs, range(w.batch), check_out=False)
     sample = [0, w.batch // 2, w.batch - 1]
     r2 = check_sequences(w, inp, bufs, sample, check_out=True, check_dense=True)
+    # the decode-step forms (the benchmarked path) on the same inputs
+    fused = run_gpu(w, inp, fused=True)
+    assert torch.equal(fused.idx, bufs.idx)
+    check_sequences(w, inp, fused, sample, check_out=True)
+    step = run_gpu(w, inp, step=True)
+    assert torch.equal(step.idx, bufs.idx)
+    assert torch.equal(step.scores[:, :, :w.nb], bufs.scores[:, :, :w.nb])
+    check_sequences(w, inp, step, sample, check_out=True)
     if w.heavy_blocks:
         heavy = synth.heavy_block_ids(w, device="cuda")
         idx = bufs.idx.cpu()
@@ -167,4 +231,45 @@ def test_sweep_points(name):
     bufs = run_gpu(w, inp)
     seqs = sorted({0, w.batch // 2, w.batch - 1})
     r = check_sequences(w, inp, bufs, seqs)
+    fused = run_gpu(w, inp, fused=True)
+    assert torch.equal(fused.idx, bufs.idx)
+    check_sequences(w, inp, fused, seqs)
+    step = run_gpu(w, inp, step=True)
+    assert torch.equal(step.idx, bufs.idx)
+    check_sequences(w, inp, step, seqs)
     say(f"  ok {r}")
+
+
+def _crafted_scores(kind, pairs, nb, gen):
+    if kind == "normal":
+        return torch.randn((pairs, nb), generator=gen, dtype=torch.float64) * 6
+    if kind == "ties":
+        return torch.round(torch.randn((pairs, nb), generator=gen, dtype=torch.float64) * 4) / 8
+    if kind == "equal":
+        return torch.full((pairs, nb), 2.5, dtype=torch.float64)
+    if kind == "wide":  # exponents far apart: the k-th key lies > 255 binades below the max
+        e = torch.randint(-1000, 1000, (pairs, nb), generator=gen).double()
+        s = torch.where(torch.rand((pairs, nb), generator=gen) < 0.5, -1.0, 1.0).double()
+        return s * torch.pow(torch.tensor(2.0, dtype=torch.float64), e)
+    if kind == "zeros":  # +0, -0, denormals and their negatives
+        v = torch.tensor([0.0, -0.0, 5e-324, -5e-324, 1e-310, -1e-310, 1.0], dtype=torch.float64)
+        return v[torch.randint(0, len(v), (pairs, nb), generator=gen)]
+    raise KeyError(kind)
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "equal", "wide", "zeros"])
+@pytest.mark.parametrize("nb", [37, 2048, 8192])
+def test_topk_crafted_scores_bit_exact(kind, nb):
+    gen = torch.Generator().manual_seed(zlib.crc32(f"{kind}-{nb}".encode()))
+    pairs = 24
+    sc = _crafted_scores(kind, pairs, nb, gen).view(4, 6, nb).contiguous()
+    d = kb.make_desc(4, 6, 1, nb * 16, nb * 16, 16, torch.bfloat16)
+    sc_gpu = sc.cuda()
+    for k in sorted({1, 2, 7, 64, nb - 1, nb, nb + 3}):
+        if k < 1:
+            continue
+        idx = torch.full((4, 6, k), -9, dtype=torch.int32, device="cuda")
+        kb.kin_block_topk(d, sc_gpu, k, idx)
+        torch.cuda.synchronize()
+        ref, _ = oracle.block_topk(sc, nb, k)
+        assert torch.equal(idx.cpu(), ref), (kind, nb, k)
