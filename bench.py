@@ -167,8 +167,8 @@ def cpu_baseline(w, layer, max_seqs):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=workloads.QWEN3_8B.name)
     ap.add_argument("--layers", type=int, default=0, help="layers rotated (0: auto)")
     ap.add_argument("--no-dense", action="store_true")

@@ -90,7 +90,9 @@ __global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a,
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int split = blockIdx.x, pair = blockIdx.y;
-    select_topk<KPT, kStepThreads>(scores + (size_t)pair * nb_cap, a.nb, a.k, sel, u.s);
+    select_clear(u.s);
+    __syncthreads();
+    select_topk<KPT, kStepThreads, false>(scores + (size_t)pair * nb_cap, a.nb, a.k, sel, u.s);
     __syncthreads();
     if (split == 0)
         for (int i = threadIdx.x; i < a.k; i += kStepThreads) idx_out[(size_t)pair * a.k + i] = sel[i];

@@ -12,21 +12,25 @@
 // Method: the pair's scores are held in registers (KPT per thread, block
 // j = e * NT + tid).  Each fp64 score maps to an unsigned 64-bit key with
 // the same order (flip all bits of negatives, set the sign bit of the
-// rest).  An MSD radix select finds the k-th largest key: the first pass
-// ranks keys by the distance of their sign+exponent field below the
-// largest one (so one pass fixes the exponent of the k-th key), the later
-// ones take the mantissa 8 bits at a time.  Each pass builds an LDS
+// rest).  An MSD radix select finds the k-th largest key.  Its top 12 bits
+// (sign and exponent) come from two count tables filled one atomic per key
+// before the select starts: by bits 63..56 (256 bins) and by bits 63..52
+// (4096 bins).  Every wave reads both tables itself (the 256 coarse bins,
+// then the 16 fine bins under the chosen coarse one), so fixing the
+// exponent costs no barrier; the fused decode step fills the tables while
+// it computes the scores, where the atomics hide under HBM latency.  The
+// mantissa follows 8 bits at a time (the last 4): each pass builds an LDS
 // histogram of the digit among the keys that still match the prefix (one
 // LDS atomic per candidate), then EVERY wave scans the 256 bins itself
 // (a DPP prefix sum, lane broadcasts by readlane), so a pass costs a single
-// barrier: three histogram buffers rotate, and the
-// buffer for pass p+1 is cleared during pass p (its last readers finished
-// before the barrier of pass p-1).  The select stops as soon as the bin
-// holding the k-th key holds exactly the keys still needed; if all 64 bits
-// are used up, the remaining equal keys are exact ties and the lowest
-// indices among them are kept.  The kept flags are compacted in block order
-// with ballot + mbcnt ranks and a scan of the per-wave counts that every
-// wave repeats (one barrier).
+// barrier: three histogram buffers rotate, and the buffer for pass p+1 is
+// cleared during pass p (its last readers finished before the barrier of
+// pass p-1).  The select stops as soon as the bin holding the k-th key
+// holds exactly the keys still needed; if all 64 bits are used up, the
+// remaining equal keys are exact ties and the lowest indices among them are
+// kept.  The kept flags are compacted in block order with ballot + mbcnt
+// ranks and a scan of the per-wave counts that every wave repeats (one
+// barrier).
 #pragma once
 
 #include "kin_internal.h"
@@ -35,16 +39,37 @@ namespace kin {
 
 template <int KPT, int NT>
 struct SelectLds {
-    uint32_t hist[3][256];
+    uint32_t coarse[256];   // keys per value of bits 63..56
+    uint32_t fine[4096];    // keys per value of bits 63..52 (sign, exponent)
+    uint32_t hist[3][256];  // mantissa passes
     uint32_t cnt[KPT * (NT / 64)];
     uint32_t cnt_tie[KPT * (NT / 64)];
-    uint32_t wave_top[NT / 64];  // per wave: largest sign+exponent field of its keys
 };
 
 __device__ __forceinline__ uint64_t order_key(double s) {
     if (s == 0.0) s = 0.0;  // -0.0 and +0.0 are one score
     const uint64_t u = (uint64_t)__double_as_longlong(s);
     return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// Zero the count tables and the first mantissa histogram; every thread of
+// the workgroup calls this, and a barrier must separate it from the first
+// select_count or select_topk.
+template <int KPT, int NT>
+__device__ __forceinline__ void select_clear(SelectLds<KPT, NT> &lds) {
+    for (int i = threadIdx.x; i < 4096; i += NT) lds.fine[i] = 0u;
+    for (int i = threadIdx.x; i < 256; i += NT) {
+        lds.coarse[i] = 0u;
+        lds.hist[0][i] = 0u;
+    }
+}
+
+// Count one score in the two exponent tables (each score exactly once).
+template <int KPT, int NT>
+__device__ __forceinline__ void select_count(SelectLds<KPT, NT> &lds, double s) {
+    const uint64_t key = order_key(s);
+    atomicAdd(&lds.coarse[key >> 56], 1u);
+    atomicAdd(&lds.fine[key >> 52], 1u);
 }
 
 __device__ __forceinline__ uint32_t rank_below(uint64_t mask) {
@@ -106,11 +131,42 @@ __device__ __forceinline__ void offsets_of(const uint32_t *cnt, int wave, int la
     }
 }
 
+// Every wave: the bin holding the krem-th largest key, given that lane l
+// holds the counts c[0..3] of bins base - 4l .. base - 4l - 3 (descending
+// digits).  Returns the digit, the keys in bins above it and in it.
+struct BinHit {
+    uint32_t digit, above, in_bin;
+};
+
+__device__ __forceinline__ BinHit find_bin(const uint32_t (&c)[4], uint32_t krem, uint32_t base,
+                                           int lane) {
+    const uint32_t sum = c[0] + c[1] + c[2] + c[3];
+    const uint32_t incl = wave_incl_scan(sum);
+    const uint32_t excl = incl - sum;
+    const uint64_t hit = __ballot(excl < krem && krem <= incl);
+    const int src = __builtin_ctzll(hit);
+    // bins are disjoint in the running sum: at most one r of the hit lane
+    // brackets krem (selects, no branches)
+    uint32_t run = excl, dsel = 0, above = 0, in_bin = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t next = run + c[r];
+        const bool here = run < krem && krem <= next;
+        dsel = here ? base - 4u * lane - r : dsel;
+        above = here ? run : above;
+        in_bin = here ? c[r] : in_bin;
+        run = next;
+    }
+    return BinHit{lane_value(dsel, src), lane_value(above, src), lane_value(in_bin, src)};
+}
+
 // Write out[0..k): the min(k, nb) selected block indices ascending, then -1.
 // sc: the pair's scores (nb entries; global memory or LDS).  Every thread of
-// the workgroup calls this; it ends without a barrier, so callers
-// synchronise before other waves read `out`.
-template <int KPT, int NT>
+// the workgroup calls this, after select_clear and a barrier; with COUNTED
+// the caller has also passed every score to select_count (and synchronised
+// since).  It ends without a barrier, so callers synchronise before other
+// waves read `out`.  Requires 1 <= k and nb <= KPT * NT.
+template <int KPT, int NT, bool COUNTED>
 __device__ void select_topk(const double *__restrict__ sc, int nb, int k, int32_t *out,
                             SelectLds<KPT, NT> &lds) {
     constexpr int NW = NT / 64;
@@ -124,103 +180,73 @@ __device__ void select_topk(const double *__restrict__ sc, int nb, int k, int32_
         return;
     }
 
+    // all loads first (slots past nb re-read entry nb - 1), then the keys;
+    // 0 is below every finite key
+    double v[KPT];
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) v[e] = sc[min(e * NT + tid, nb - 1)];
     uint64_t key[KPT];
-    uint32_t top = 0;  // largest sign+exponent field (key >> 52) of this lane
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
         const int j = e * NT + tid;
-        key[e] = j < nb ? order_key(sc[j]) : 0ull;  // 0 is below every finite key
-        top = max(top, (uint32_t)(key[e] >> 52));
+        key[e] = order_key(v[e]) & (0ull - (uint64_t)(j < nb));  // a mask, not a branch
+        if (!COUNTED && j < nb) {
+            atomicAdd(&lds.coarse[key[e] >> 56], 1u);
+            atomicAdd(&lds.fine[key[e] >> 52], 1u);
+        }
     }
-    top = wave_max(top);
-    if (lane == 0) lds.wave_top[wave] = top;
-    for (int i = tid; i < 256; i += NT) lds.hist[0][i] = 0u;
-    __syncthreads();
-    top = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) top = max(top, lds.wave_top[w]);
+    if (!COUNTED) __syncthreads();
 
-    // Pass 1 ranks keys by how far their sign+exponent field lies below the
-    // largest one (digit 255 - distance, clamped at 0): it fixes the
-    // exponent of the k-th key in one pass.  Later passes take the 52
-    // mantissa bits 8 at a time (the last one 4).  Should the k-th key fall
-    // into the clamped bin, the select restarts as a plain 8-bit MSD radix
-    // select over all 64 bits.
-    uint64_t prefix = 0, pmask = 0;
+    // sign and exponent: the coarse bin, then the fine bin under it
     uint32_t krem = (uint32_t)keff;
-    bool resolved = false;  // true: every key matching `prefix` is kept
-    bool plain = false;     // restarted as the plain select
+    uint64_t prefix, pmask = 0xFFFull << 52;
+    uint32_t in_bin;
+    {
+        uint32_t c[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) c[r] = lds.coarse[255 - 4 * lane - r];
+        const BinHit h1 = find_bin(c, krem, 255u, lane);
+        krem -= h1.above;
+        // lanes 0..3 hold the 16 fine bins of coarse bin h1.digit, descending
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            c[r] = lane < 4 ? lds.fine[16 * h1.digit + 15 - 4 * lane - r] : 0u;
+        const BinHit h2 = find_bin(c, krem, 16u * h1.digit + 15u, lane);
+        krem -= h2.above;
+        prefix = (uint64_t)h2.digit << 52;
+        in_bin = h2.in_bin;
+    }
+    bool resolved = in_bin == krem;  // true: every key matching `prefix` is kept
+
+    // mantissa: bits 51..44, 43..36, ..., 11..4, then 3..0
     int buf = 0;
-    int lo = 52, width = 12;  // bit range of the current digit: [lo, lo + width)
-    for (;;) {
+    int lo = 44, width = 8;  // bit range of the current digit: [lo, lo + width)
+    while (!resolved) {
         uint32_t *h = lds.hist[buf];
         const int nbuf = buf == 2 ? 0 : buf + 1;
-        const bool first_pass = !plain && lo == 52;
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
             const bool cand = (e * NT + tid < nb) && ((key[e] & pmask) == prefix);
-            uint32_t dig;
-            if (first_pass) {
-                const uint32_t dist = top - (uint32_t)(key[e] >> 52);
-                dig = dist >= 255u ? 0u : 255u - dist;
-            } else {
-                dig = (uint32_t)(key[e] >> lo) & ((1u << width) - 1u);
-            }
+            const uint32_t dig = (uint32_t)(key[e] >> lo) & ((1u << width) - 1u);
             if (cand) atomicAdd(&h[dig], 1u);
         }
         for (int i = tid; i < 256; i += NT) lds.hist[nbuf][i] = 0u;
         __syncthreads();
         // every wave: lane l holds bins 255-4l .. 252-4l (descending digits)
-        uint32_t c[4], sum = 0;
+        uint32_t c[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            c[r] = h[255 - 4 * lane - r];
-            sum += c[r];
-        }
-        const uint32_t incl = wave_incl_scan(sum);
-        const uint32_t excl = incl - sum;
-        const uint64_t hit = __ballot(excl < krem && krem <= incl);
-        const int src = __builtin_ctzll(hit);
-        uint32_t run = excl, dsel = 0, above = 0, in_bin = 0;
-        bool found = false;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            if (!found && run + c[r] >= krem) {
-                dsel = 255u - 4u * lane - r;
-                above = run;
-                in_bin = c[r];
-                found = true;
-            }
-            run += c[r];
-        }
-        dsel = lane_value(dsel, src);
-        above = lane_value(above, src);
-        in_bin = lane_value(in_bin, src);
+        for (int r = 0; r < 4; ++r) c[r] = h[255 - 4 * lane - r];
+        const BinHit hb = find_bin(c, krem, 255u, lane);
         buf = nbuf;
-        if (first_pass && dsel == 0u) {
-            // the k-th key is 255 or more exponent steps below the largest
-            plain = true;
-            lo = 56;
-            width = 8;
-            continue;
-        }
-        krem -= above;
-        if (first_pass) {
-            prefix = (uint64_t)(top - (255u - dsel)) << 52;
-            pmask = 0xFFFull << 52;
-        } else {
-            prefix |= (uint64_t)dsel << lo;
-            pmask |= (uint64_t)((1u << width) - 1u) << lo;
-        }
-        if (in_bin == krem) {
+        krem -= hb.above;
+        prefix |= (uint64_t)hb.digit << lo;
+        pmask |= (uint64_t)((1u << width) - 1u) << lo;
+        if (hb.in_bin == krem) {
             resolved = true;
             break;
         }
         if (lo == 0) break;  // all 64 bits used: the rest are exact ties
-        if (first_pass) {
-            lo = 44;
-            width = 8;
-        } else if (lo >= 8) {
+        if (lo >= 8) {
             lo -= 8;
         } else {
             width = lo;

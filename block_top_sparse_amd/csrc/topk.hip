@@ -12,7 +12,9 @@ __global__ __launch_bounds__(kTopkThreads) void k_block_topk(const double *__res
                                                              int nb_cap, int nb, int k) {
     __shared__ SelectLds<KPT, kTopkThreads> lds;
     const size_t pair = blockIdx.x;
-    select_topk<KPT, kTopkThreads>(scores + pair * (size_t)nb_cap, nb, k, idx + pair * (size_t)k,
+    select_clear(lds);
+    __syncthreads();
+    select_topk<KPT, kTopkThreads, false>(scores + pair * (size_t)nb_cap, nb, k, idx + pair * (size_t)k,
                                    lds);
 }
 
