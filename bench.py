@@ -76,13 +76,16 @@ def make_layers(w, n_layers, with_dense):
     return layers
 
 
-def sparse_step(w, inp, bufs, ev=None):
+def sparse_step(w, inp, bufs, ev=None, scores=False):
     """One decode step of one layer through kin_sparse_decode_step (one
-    kernel when there are enough pairs, else two), events around it."""
+    kernel when there are enough pairs, else two), events around it.  The
+    step returns idx and out; the fp64 scores are written out only with
+    scores=True (they are not part of the method's output)."""
     if ev is not None:
         ev[0].record()
-    kb.kin_sparse_decode_step(bufs.desc, inp["q"], inp["K"], inp["V"], bufs.S, bufs.scores,
-                              bufs.k, bufs.idx, bufs.out, bufs.ws)
+    kb.kin_sparse_decode_step(bufs.desc, inp["q"], inp["K"], inp["V"], bufs.S,
+                              bufs.scores if scores else None, bufs.k, bufs.idx, bufs.out,
+                              bufs.ws)
     if ev is not None:
         ev[1].record()
 
@@ -218,9 +221,15 @@ def main():
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": w.dtype, "data": "synthetic",
-           "config": dict(w.describe(), layers_rotated=n_layers),
+           "config": dict(w.describe(), layers_rotated=n_layers,
+                          step_outputs="out, idx, S row (fp64 scores not written)"),
            "step_bytes": step_bytes, "hbm_gbs": round(gbs, 1),
            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "roofline": roofline}
+
+    # the same step also writing the fp64 scores (an inspection output)
+    sms, _ = time_steps(lambda i, b, e: sparse_step(w, i, b, None, scores=True), layers,
+                        max(5, args.steps // 4), 5)
+    res["with_scores_ms_per_step"] = round(sms, 5)
 
     if not args.no_unfused:
         n = max(5, args.steps // 5)

@@ -103,13 +103,24 @@ static kin_status check_step(const kin_desc *desc, kin::Geo *g) {
     return KIN_OK;
 }
 
-static kin_status check_ws(const kin::AttnPlan &p, const void *ws, size_t ws_bytes) {
-    if (p.ws_bytes == 0) return KIN_OK;
-    if (!ws) return fail(KIN_ERR_NULL, "ws is NULL but %zu bytes are needed", p.ws_bytes);
+static kin_status check_ws_size(size_t need, const void *ws, size_t ws_bytes) {
+    if (need == 0) return KIN_OK;
+    if (!ws) return fail(KIN_ERR_NULL, "ws is NULL but %zu bytes are needed", need);
     if (!aligned16(ws)) return fail(KIN_ERR_ALIGN, "ws is not 16-byte aligned");
-    if (ws_bytes < p.ws_bytes)
-        return fail(KIN_ERR_WORKSPACE, "ws has %zu bytes, %zu needed", ws_bytes, p.ws_bytes);
+    if (ws_bytes < need)
+        return fail(KIN_ERR_WORKSPACE, "ws has %zu bytes, %zu needed", ws_bytes, need);
     return KIN_OK;
+}
+
+static kin_status check_ws(const kin::AttnPlan &p, const void *ws, size_t ws_bytes) {
+    return check_ws_size(p.ws_bytes, ws, ws_bytes);
+}
+
+// Workspace of the two-kernel decode step when the caller passes no scores
+// buffer: the attention plan's bytes, then the pair-major fp64 scores.
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+static size_t step_scores_bytes(const kin::Geo &g) {
+    return (size_t)g.pairs * (size_t)g.nb_cap * sizeof(double);
 }
 
 extern "C" {
@@ -239,7 +250,8 @@ kin_status kin_sparse_decode_step(const kin_desc *desc, const void *q, const voi
     KIN_REQUIRE_PTR(K);
     KIN_REQUIRE_PTR(V);
     KIN_REQUIRE_PTR(S);
-    KIN_REQUIRE_PTR(scores);
+    if (scores && !aligned16(scores))  // NULL: the scores are not returned
+        return fail(KIN_ERR_ALIGN, "scores is not 16-byte aligned");
     KIN_REQUIRE_PTR(idx);
     KIN_REQUIRE_PTR(out);
     if (k < 1) return fail(KIN_ERR_SHAPE, "k = %d: need k >= 1", k);
@@ -249,10 +261,16 @@ kin_status kin_sparse_decode_step(const kin_desc *desc, const void *q, const voi
         return launched(kin::launch_decode_step(g, q, K, V, S, scores, k, idx, out, s),
                         "kin_sparse_decode_step");
     const kin::AttnPlan p = kin::plan_step(g, k, cu);
-    st = check_ws(p, ws, ws_bytes);
+    // two kernels hand the scores over in memory: the caller's buffer, or
+    // the workspace after the attention's part
+    const size_t need = scores ? p.ws_bytes : align256(p.ws_bytes) + step_scores_bytes(g);
+    st = check_ws_size(need, ws, ws_bytes);
     if (st != KIN_OK) return st;
-    hipError_t e = kin::launch_update_and_score(g, q, K, S, scores, s);
-    if (e == hipSuccess) e = kin::launch_select_attend(g, p, q, K, V, scores, k, idx, out, ws, s);
+    double *sc = scores ? scores
+                        : reinterpret_cast<double *>(static_cast<char *>(ws) +
+                                                     align256(p.ws_bytes));
+    hipError_t e = kin::launch_update_and_score(g, q, K, S, sc, s);
+    if (e == hipSuccess) e = kin::launch_select_attend(g, p, q, K, V, sc, k, idx, out, ws, s);
     return launched(e, "kin_sparse_decode_step");
 }
 
@@ -265,7 +283,10 @@ size_t kin_sparse_ws_bytes(const kin_desc *desc, int32_t k) {
     }
     const int cu = num_cu();
     const size_t a = kin::plan_attention(g, k, false, cu).ws_bytes;
-    const size_t b = kin::plan_step(g, k, cu).ws_bytes;
+    // the step's two-kernel form, with room for the scores (scores == NULL)
+    const size_t b = kin::step_single_kernel(g, k, cu)
+                         ? 0
+                         : align256(kin::plan_step(g, k, cu).ws_bytes) + step_scores_bytes(g);
     return a > b ? a : b;
 }
 

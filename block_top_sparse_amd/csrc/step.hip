@@ -41,7 +41,7 @@ constexpr int kKPre = 16;  // newest-block K rows each wave stages (8 x 16 >= 12
 
 struct StepExtra {
     void *S;
-    double *scores;
+    double *scores;  // may be null: the scores are then not written out
     int32_t *idx;
     int nb_cap;
 };
@@ -83,7 +83,7 @@ __device__ __forceinline__ void score_batch(const double (&qs)[8], const u32x4 (
     if ((lane & 3) == 0 && j < nb - 1) {  // the newest block is scored apart
         if (x == 0.0) x = 0.0;  // one zero: -0.0 becomes +0.0
         sc_lds[j] = x;
-        sc_out[j] = x;
+        if (sc_out) sc_out[j] = x;  // scores are an optional output
         select_count(sl, x);
     }
 }
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step(AttnArgs a, StepEx
         const uint16_t *S = static_cast<const uint16_t *>(x.S);
         const uint16_t *qp = static_cast<const uint16_t *>(a.q) +
                              ((size_t)b * a.hkv * a.gqa + (size_t)g * a.gqa) * kHeadDim + 8 * sub;
-        double *sc_out = x.scores + row0;
+        double *sc_out = x.scores ? x.scores + row0 : nullptr;
         constexpr int kBatch = 16;  // blocks per wave per batch
         constexpr int kStride = NW * kBatch;  // the 8 waves read 128 consecutive rows
         const int jw = wave * kBatch;
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step(AttnArgs a, StepEx
             if (lane == 0) {
                 if (v == 0.0) v = 0.0;
                 u.sc[nb - 1] = v;
-                sc_out[nb - 1] = v;
+                if (sc_out) sc_out[nb - 1] = v;
                 select_count(sl, v);
             }
         }

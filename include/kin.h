@@ -159,7 +159,9 @@ KIN_API kin_status kin_decode_select_attend(const kin_desc *desc, const void *q,
  * the newest block ([ctx_len-1, ctx_len)), scores, top-k and sparse
  * attention, with the same results as those four calls in sequence.  S is
  * updated in place; scores and idx receive the step's intermediate
- * results.  With bf16 data and at least as many (sequence, KV head) pairs
+ * results.  scores may be NULL: the scores are then not written (the
+ * single-kernel form keeps them in LDS; the two-kernel form keeps them in
+ * ws, which must then hold kin_sparse_ws_bytes(desc, k) bytes).  With bf16 data and at least as many (sequence, KV head) pairs
  * as the device has compute units it is ONE kernel (a workgroup per pair
  * runs all four steps, the scores never leave LDS before the selection);
  * otherwise it is kin_decode_update_score then kin_decode_select_attend
@@ -172,7 +174,7 @@ KIN_API kin_status kin_sparse_decode_step(const kin_desc *desc, const void *q, c
 
 /* Workspace sizes in bytes (0 when none is needed); -1 cast to size_t on
  * a bad descriptor.  kin_sparse_ws_bytes covers both kin_sparse_decode_attn
- * and kin_sparse_decode_step.  Sizes depend on the current device's
+ * and kin_sparse_decode_step (also with scores == NULL).  Sizes depend on the current device's
  * compute-unit count: query them on the device the calls will run on. */
 KIN_API size_t kin_sparse_ws_bytes(const kin_desc *desc, int32_t k);
 KIN_API size_t kin_dense_ws_bytes(const kin_desc *desc);

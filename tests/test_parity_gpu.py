@@ -114,6 +114,38 @@ def test_single_kernel_step_against_oracle(case):
     assert torch.equal(sep.idx, bufs.idx)
     assert torch.equal(bits(sep.S[:, :, :w.nb]), bits(bufs.S[:, :, :w.nb]))
     assert torch.equal(sep.scores[:, :, :w.nb], bufs.scores[:, :, :w.nb])
+    # without a scores buffer: the same selection and output, scores untouched
+    quiet = run_gpu(w, inp, step=True, no_scores=True)
+    assert torch.equal(quiet.idx, bufs.idx)
+    assert torch.equal(bits(quiet.out), bits(bufs.out))
+    assert torch.equal(bits(quiet.S[:, :, :w.nb]), bits(bufs.S[:, :, :w.nb]))
+    assert torch.isnan(quiet.scores).all()
+    say(f"  ok {r}")
+
+
+NO_SCORES_TWO_KERNEL = [
+    # name, batch, hq, hkv, ctx, block, k, dtype, t_cap  (few pairs: two kernels)
+    ("nosc-g4-b16", 2, 8, 2, 3000, 16, 24, "bf16", 3072),
+    ("nosc-g5-b32-f32", 3, 10, 2, 999, 32, 7, "f32", 1024),
+    ("nosc-g8-b64-kpast", 1, 16, 2, 500, 64, 20, "bf16", 512),
+]
+
+
+@pytest.mark.parametrize("case", NO_SCORES_TWO_KERNEL, ids=[c[0] for c in NO_SCORES_TWO_KERNEL])
+def test_two_kernel_step_without_scores_buffer(case):
+    """scores == NULL in the two-kernel form: the scores live in the
+    workspace; idx and out equal those of the call with a scores buffer."""
+    name, b, hq, hkv, L, B, k, dt, cap = case
+    w = Workload(name, batch=b, hq=hq, hkv=hkv, ctx_len=L, block=B, topk=k, dtype=dt,
+                 seed=zlib.crc32(name.encode()) % 10000, t_cap=cap)
+    say(f"case {name}: {w.describe()}")
+    inp = gpu_inputs(w)
+    ref = run_gpu(w, inp, step=True)
+    quiet = run_gpu(w, inp, step=True, no_scores=True)
+    assert torch.equal(quiet.idx, ref.idx)
+    assert torch.equal(bits(quiet.out), bits(ref.out))
+    assert torch.isnan(quiet.scores).all()
+    r = check_sequences(w, inp, quiet, range(b), check_scores=False)
     say(f"  ok {r}")
 
 
@@ -184,11 +216,21 @@ def test_workspace_too_small_is_rejected():
     n = kb.kin_sparse_ws_bytes(bufs.desc, w.topk)
     if n == 0:
         pytest.skip("no workspace needed for this plan")
-    small = torch.empty(n - 16, dtype=torch.uint8, device="cuda")
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
     with pytest.raises(kb.KinError) as e:
         kb.kin_sparse_decode_attn(bufs.desc, inp["q"], inp["K"], inp["V"], bufs.idx, w.topk,
                                   bufs.out, small)
     assert e.value.status == -6
+    # the two-kernel step without a scores buffer keeps the scores in ws
+    with pytest.raises(kb.KinError) as e:
+        kb.kin_sparse_decode_step(bufs.desc, inp["q"], inp["K"], inp["V"], bufs.S, None,
+                                  w.topk, bufs.idx, bufs.out, small)
+    assert e.value.status == -6
+    kb.kin_block_summary_update(bufs.desc, inp["K"], bufs.S, 0, w.ctx_len)
+    kb.kin_sparse_decode_step(bufs.desc, inp["q"], inp["K"], inp["V"], bufs.S, None, w.topk,
+                              bufs.idx, bufs.out, bufs.ws)  # kin_sparse_ws_bytes is enough
+    torch.cuda.synchronize()
+    check_sequences(w, inp, bufs, [0, 1], check_scores=False)
 
 
 @pytest.mark.parametrize("w", [workloads.QWEN3_8B, workloads.QWEN3_14B, workloads.QWEN3_32B],
@@ -209,6 +251,9 @@ def test_full_size_workloads(w):
     assert torch.equal(step.idx, bufs.idx)
     assert torch.equal(step.scores[:, :, :w.nb], bufs.scores[:, :, :w.nb])
     check_sequences(w, inp, step, sample, check_out=True)
+    quiet = run_gpu(w, inp, step=True, no_scores=True)  # the benchmarked call
+    assert torch.equal(quiet.idx, bufs.idx)
+    assert torch.equal(bits(quiet.out), bits(step.out))
     if w.heavy_blocks:
         heavy = synth.heavy_block_ids(w, device="cuda")
         idx = bufs.idx.cpu()
