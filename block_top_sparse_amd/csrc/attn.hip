@@ -80,7 +80,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_f32(AttnArgs a) {
 template <int DT, int KPT>
 __global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a,
                                                                 const double *__restrict__ scores,
-                                                                int nb_cap, int32_t *idx_out) {
+                                                                int nb_cap, int32_t *idx_out,
+                                                                uint64_t *ctrl, uint32_t epoch) {
     constexpr int NW = kStepThreads / 64;
     __shared__ int32_t sel[kStepIdxCap];
     __shared__ union {
@@ -110,7 +111,18 @@ __global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a,
         attend_f32<false, NW>(a, sel, pair, c_beg, c_end, wave, NW, wave, fl, u.m);
     }
     __syncthreads();
-    merge_waves_and_store<DT, NW>(a, u.m, pair, split);
+    if (a.nsplit == 1) {
+        merge_waves_and_store<DT, NW>(a, u.m, pair, split);
+        return;
+    }
+    // this split's partial, then the pair's last split combines all of them
+    merge_waves_and_store<DT, NW, true>(a, u.m, pair, split);
+    stores_complete();
+    __shared__ uint32_t last;
+    __syncthreads();
+    if (threadIdx.x == 0) last = arrive_count(ctrl + pair, epoch) == (uint32_t)a.nsplit;
+    __syncthreads();
+    if (last) combine_pair<DT, kStepThreads>(a, pair);
 }
 
 // ---------------------------------------------------------------------------
@@ -153,6 +165,8 @@ static size_t ws_for(const Geo &g, int ns) {
     return ns == 1 ? 0 : (size_t)g.batch * g.hq * ns * (kHeadDim + 2) * sizeof(float);
 }
 
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
 AttnPlan plan_attention(const Geo &g, int k, bool dense, int num_cu) {
     AttnPlan p;
     const int keff = dense ? 0 : (k < g.nb ? k : g.nb);
@@ -188,7 +202,8 @@ AttnPlan plan_step(const Geo &g, int k, int num_cu) {
     if (ns < 1) ns = 1;
     p.nsplit = ns;
     p.fused = 1;
-    p.ws_bytes = ws_for(g, ns);
+    // split partials, then one arrival word per pair for the in-kernel combine
+    p.ws_bytes = ns == 1 ? 0 : align256(ws_for(g, ns)) + (size_t)g.pairs * sizeof(uint64_t);
     return p;
 }
 
@@ -226,20 +241,23 @@ hipError_t launch_attention(const Geo &g, const AttnPlan &p, const void *q, cons
 
 template <int DT>
 static void launch_sa(const Geo &g, const AttnArgs &a, dim3 grid, const double *scores,
-                      int32_t *idx, hipStream_t s) {
+                      int32_t *idx, uint64_t *ctrl, uint32_t epoch, hipStream_t s) {
+#define KIN_SA(KPT)                                                                            \
+    k_select_attend<DT, KPT><<<grid, kStepThreads, 0, s>>>(a, scores, g.nb_cap, idx, ctrl, epoch)
     switch (select_kpt(g.nb, kStepThreads)) {
-    case 1: k_select_attend<DT, 1><<<grid, kStepThreads, 0, s>>>(a, scores, g.nb_cap, idx); break;
-    case 2: k_select_attend<DT, 2><<<grid, kStepThreads, 0, s>>>(a, scores, g.nb_cap, idx); break;
-    case 4: k_select_attend<DT, 4><<<grid, kStepThreads, 0, s>>>(a, scores, g.nb_cap, idx); break;
-    case 8: k_select_attend<DT, 8><<<grid, kStepThreads, 0, s>>>(a, scores, g.nb_cap, idx); break;
-    case 16: k_select_attend<DT, 16><<<grid, kStepThreads, 0, s>>>(a, scores, g.nb_cap, idx); break;
-    default: k_select_attend<DT, 32><<<grid, kStepThreads, 0, s>>>(a, scores, g.nb_cap, idx); break;
+    case 1: KIN_SA(1); break;
+    case 2: KIN_SA(2); break;
+    case 4: KIN_SA(4); break;
+    case 8: KIN_SA(8); break;
+    case 16: KIN_SA(16); break;
+    default: KIN_SA(32); break;
     }
+#undef KIN_SA
 }
 
 hipError_t launch_select_attend(const Geo &g, const AttnPlan &p, const void *q, const void *K,
                                 const void *V, const double *scores, int k, int32_t *idx,
-                                void *out, void *ws, hipStream_t s) {
+                                void *out, void *ws, uint32_t epoch, hipStream_t s) {
     if (!p.fused) {
         hipError_t e = launch_block_topk(g, scores, k, idx, s);
         if (e != hipSuccess) return e;
@@ -247,14 +265,16 @@ hipError_t launch_select_attend(const Geo &g, const AttnPlan &p, const void *q, 
     }
     AttnArgs a;
     fill_args(a, g, p, q, K, V, nullptr, k, out, ws);
+    // one arrival word per pair after the split partials (combined in-kernel)
+    uint64_t *ctrl = p.nsplit > 1 ? reinterpret_cast<uint64_t *>(
+                                        static_cast<char *>(ws) + align256(ws_for(g, p.nsplit)))
+                                  : nullptr;
     dim3 grid(p.nsplit, g.pairs);
     if (g.dtype == KIN_BF16)
-        launch_sa<KIN_BF16>(g, a, grid, scores, idx, s);
+        launch_sa<KIN_BF16>(g, a, grid, scores, idx, ctrl, epoch, s);
     else
-        launch_sa<KIN_F32>(g, a, grid, scores, idx, s);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.nsplit == 1) return e;
-    return launch_combine(g, a, out, p.nsplit, s);
+        launch_sa<KIN_F32>(g, a, grid, scores, idx, ctrl, epoch, s);
+    return hipGetLastError();
 }
 
 }  // namespace kin

@@ -52,10 +52,48 @@ struct MergeLds {
     float l[NW][kMaxGqa];
 };
 
+// Data handed between workgroups of one running kernel is written and read
+// with agent-scope atomic accesses: the stores write through to the
+// device-coherent level and the loads bypass the non-coherent caches, so
+// the release / acquire of such a handoff reduce to the writer waiting for
+// its stores to complete (stores_complete) before it signals.  This avoids
+// the L2 writeback and invalidate of a full device-scope fence.
+template <class T>
+__device__ __forceinline__ void st_agent(T *p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T ld_agent(const T *p) {
+    return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Every memory access this wave issued has completed (the compiler fences
+// keep the accesses on their side of the wait).
+__device__ __forceinline__ void stores_complete() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Count this workgroup's arrival at *ctr in round `epoch` (ctr holds
+// epoch << 32 | count; a word left by another round counts as zero, so the
+// word needs no clearing between calls).  Returns the count including this
+// arrival.
+__device__ inline uint32_t arrive_count(uint64_t *ctr, uint32_t epoch) {
+    uint64_t old = ld_agent(ctr);
+    for (;;) {
+        const uint32_t c = (uint32_t)(old >> 32) == epoch ? (uint32_t)old + 1u : 1u;
+        const uint64_t next = ((uint64_t)epoch << 32) | c;
+        if (__hip_atomic_compare_exchange_weak(ctr, &old, next, __ATOMIC_RELAXED,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            return c;
+    }
+}
+
 // Merge the NW waves' (m, l, o) of one workgroup in wave order and write the
-// result (the output when nsplit == 1, else this split's partial).  Uses the
-// first 256 threads: 16 per head, 8 channels each.
-template <int DT, int NW>
+// result (the output when nsplit == 1, else this split's partial; AGENT:
+// the partial with agent-scope stores, for a combine in the same kernel).
+// Uses the first 256 threads: 16 per head, 8 channels each.
+template <int DT, int NW, bool AGENT = false>
 __device__ void merge_waves_and_store(const AttnArgs &a, const MergeLds<NW> &sm, int pair,
                                       int split) {
     const int tid = threadIdx.x;
@@ -98,12 +136,55 @@ __device__ void merge_waves_and_store(const AttnArgs &a, const MergeLds<NW> &sm,
         }
     } else {
         const size_t prow = row * a.nsplit + split;
-        f32x4 *p = reinterpret_cast<f32x4 *>(a.ws_o + prow * kHeadDim + c0);
-        p[0] = f32x4{o[0], o[1], o[2], o[3]};
-        p[1] = f32x4{o[4], o[5], o[6], o[7]};
-        if ((tid & 15) == 0) {
-            a.ws_ml[prow * 2 + 0] = M;
-            a.ws_ml[prow * 2 + 1] = L;
+        if (AGENT) {
+            float *p = a.ws_o + prow * kHeadDim + c0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st_agent(p + e, o[e]);
+            if ((tid & 15) == 0) {
+                st_agent(a.ws_ml + prow * 2 + 0, M);
+                st_agent(a.ws_ml + prow * 2 + 1, L);
+            }
+        } else {
+            f32x4 *p = reinterpret_cast<f32x4 *>(a.ws_o + prow * kHeadDim + c0);
+            p[0] = f32x4{o[0], o[1], o[2], o[3]};
+            p[1] = f32x4{o[4], o[5], o[6], o[7]};
+            if ((tid & 15) == 0) {
+                a.ws_ml[prow * 2 + 0] = M;
+                a.ws_ml[prow * 2 + 1] = L;
+            }
+        }
+    }
+}
+
+// LSE combine of the nsplit partials of one pair's query heads, read with
+// agent-scope loads (written by other workgroups of the same kernel):
+// M = max m_s, out = sum 2^(m_s - M) o_s / sum 2^(m_s - M) l_s, splits in
+// ascending order.  Every thread of an NT-thread workgroup calls this.
+template <int DT, int NT>
+__device__ void combine_pair(const AttnArgs &a, int pair) {
+    const int b = pair / a.hkv, g = pair % a.hkv;
+    const int hq = a.hkv * a.gqa;
+    for (int i = threadIdx.x; i < a.gqa * (kHeadDim / 2); i += NT) {
+        const int h = i / (kHeadDim / 2), c = 2 * (i % (kHeadDim / 2));
+        const size_t row = (size_t)b * hq + (size_t)g * a.gqa + h;
+        const float *ml = a.ws_ml + row * a.nsplit * 2;
+        float M = -INFINITY;
+        for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, ld_agent(ml + 2 * s));
+        float L = 0.f, o0 = 0.f, o1 = 0.f;
+        for (int s = 0; s < a.nsplit; ++s) {
+            const float w = (M == -INFINITY) ? 0.f : exp2f(ld_agent(ml + 2 * s) - M);
+            L += w * ld_agent(ml + 2 * s + 1);
+            const float *po = a.ws_o + (row * a.nsplit + s) * kHeadDim + c;
+            o0 += w * ld_agent(po);
+            o1 += w * ld_agent(po + 1);
+        }
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        if (DT == KIN_BF16) {
+            static_cast<uint32_t *>(a.out)[row * (kHeadDim / 2) + c / 2] =
+                f32_to_bf16_bits(o0 * inv) | (f32_to_bf16_bits(o1 * inv) << 16);
+        } else {
+            reinterpret_cast<float2 *>(a.out)[row * (kHeadDim / 2) + c / 2] =
+                make_float2(o0 * inv, o1 * inv);
         }
     }
 }

@@ -2,10 +2,12 @@
 // argument checks on the host, workspace sizing, launches on the caller's
 // stream.  Nothing here allocates device memory or synchronises.
 #include <stdarg.h>
+#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
 #include <atomic>
+#include <chrono>
 
 #include "kin_internal.h"
 
@@ -116,6 +118,17 @@ static kin_status check_ws(const kin::AttnPlan &p, const void *ws, size_t ws_byt
     return check_ws_size(p.ws_bytes, ws, ws_bytes);
 }
 
+// Round tag of one split select + attend launch: the arrival words in the
+// workspace count only when they carry the current call's tag, so the
+// workspace needs no clearing.  Starts at a per-process value so that a
+// workspace left by another process is unlikely to match.
+static uint32_t next_epoch() {
+    static std::atomic<uint32_t> epoch{
+        (uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() | 1u};
+    uint32_t e = epoch.fetch_add(2u);
+    return e ? e : epoch.fetch_add(2u);
+}
+
 // Workspace of the two-kernel decode step when the caller passes no scores
 // buffer: the attention plan's bytes, then the pair-major fp64 scores.
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -152,7 +165,7 @@ kin_status kin_block_score(const kin_desc *desc, const void *q, const void *S, d
     KIN_REQUIRE_PTR(scores);
     if (g.nb > kin::kMaxBlocks)
         return fail(KIN_ERR_UNSUPPORTED, "%d blocks: at most %d", g.nb, kin::kMaxBlocks);
-    return launched(kin::launch_block_score(g, q, S, scores, (hipStream_t)stream),
+    return launched(kin::launch_block_score(g, q, S, scores, num_cu(), (hipStream_t)stream),
                     "kin_block_score");
 }
 
@@ -213,7 +226,7 @@ kin_status kin_decode_update_score(const kin_desc *desc, const void *q, const vo
     KIN_REQUIRE_PTR(K);
     KIN_REQUIRE_PTR(S);
     KIN_REQUIRE_PTR(scores);
-    return launched(kin::launch_update_and_score(g, q, K, S, scores, (hipStream_t)stream),
+    return launched(kin::launch_update_and_score(g, q, K, S, scores, num_cu(), (hipStream_t)stream),
                     "kin_decode_update_score");
 }
 
@@ -234,7 +247,7 @@ kin_status kin_decode_select_attend(const kin_desc *desc, const void *q, const v
     st = check_ws(p, ws, ws_bytes);
     if (st != KIN_OK) return st;
     return launched(kin::launch_select_attend(g, p, q, K, V, scores, k, idx, out, ws,
-                                              (hipStream_t)stream),
+                                              next_epoch(), (hipStream_t)stream),
                     "kin_decode_select_attend");
 }
 
@@ -269,8 +282,9 @@ kin_status kin_sparse_decode_step(const kin_desc *desc, const void *q, const voi
     double *sc = scores ? scores
                         : reinterpret_cast<double *>(static_cast<char *>(ws) +
                                                      align256(p.ws_bytes));
-    hipError_t e = kin::launch_update_and_score(g, q, K, S, sc, s);
-    if (e == hipSuccess) e = kin::launch_select_attend(g, p, q, K, V, sc, k, idx, out, ws, s);
+    hipError_t e = kin::launch_update_and_score(g, q, K, S, sc, cu, s);
+    if (e == hipSuccess)
+        e = kin::launch_select_attend(g, p, q, K, V, sc, k, idx, out, ws, next_epoch(), s);
     return launched(e, "kin_sparse_decode_step");
 }
 

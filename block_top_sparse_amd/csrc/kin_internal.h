@@ -35,10 +35,10 @@ AttnPlan plan_attention(const Geo &g, int k, bool dense, int num_cu);
 hipError_t launch_block_summary(const Geo &g, const void *K, void *S, int j0, int j1,
                                 hipStream_t s);
 hipError_t launch_block_score(const Geo &g, const void *q, const void *S, double *scores,
-                              hipStream_t s);
+                              int num_cu, hipStream_t s);
 // decode step, first half: newest-block summary update + all block scores
 hipError_t launch_update_and_score(const Geo &g, const void *q, const void *K, void *S,
-                                   double *scores, hipStream_t s);
+                                   double *scores, int num_cu, hipStream_t s);
 hipError_t launch_block_topk(const Geo &g, const double *scores, int k, int32_t *idx,
                              hipStream_t s);
 hipError_t launch_attention(const Geo &g, const AttnPlan &p, const void *q, const void *K,
@@ -47,9 +47,10 @@ hipError_t launch_attention(const Geo &g, const AttnPlan &p, const void *q, cons
 // decode step, second half: top-k selection + sparse attention, fused per
 // pair when the plan allows it (plan_step); otherwise separate launches
 AttnPlan plan_step(const Geo &g, int k, int num_cu);
+// (epoch: the call's round tag for the in-kernel combine of split partials)
 hipError_t launch_select_attend(const Geo &g, const AttnPlan &p, const void *q, const void *K,
                                 const void *V, const double *scores, int k, int32_t *idx,
-                                void *out, void *ws, hipStream_t s);
+                                void *out, void *ws, uint32_t epoch, hipStream_t s);
 // the whole decode step in one kernel (one workgroup per pair); usable when
 // step_single_kernel() says so (bf16, enough pairs to cover the chip)
 bool step_single_kernel(const Geo &g, int k, int num_cu);

@@ -26,9 +26,63 @@
 // summary of the newest block (ctx_len - 1 lies in it), writes it to S and
 // scores it with the same per-lane math and the same butterfly; every other
 // workgroup scores its range of blocks and leaves the newest block alone.
-#include "score_impl.h"
+#include "attn_impl.h"
+#include "scoring.h"
 
 namespace kin {
+
+// bf16: score tiles.  One 512-thread workgroup scores tile_rows consecutive
+// blocks of one pair with the streaming loop of the decode step
+// (scoring.h: 16-block batches, the 8 waves on consecutive batches, a ring
+// of 4 batches in flight per wave); with UPDATE the tile holding the newest
+// block rebuilds that block's summary first.  About one tile per CU, so a
+// few pairs still spread over the whole chip.
+constexpr int kTileThreads = 512;
+
+template <bool UPDATE>
+__global__ __launch_bounds__(kTileThreads) void k_score_tiles(AttnArgs a, void *S,
+                                                             double *scores, int nb_cap,
+                                                             int tile_rows) {
+    constexpr int NW = kTileThreads / 64;
+    __shared__ NewestLds<NW> nl;
+    const int pair = blockIdx.y;
+    const int nb = a.nb;
+    const int j_beg = blockIdx.x * tile_rows;
+    const int j_end = min(nb, j_beg + tile_rows);
+    double *sp = scores + (size_t)pair * nb_cap;
+    auto emit = [&](int j, double v) { sp[j] = v; };
+    if (UPDATE && j_end == nb) {
+        if (threadIdx.x == 0) nl.ready = 0u;
+        __syncthreads();
+        score_blocks<NW, true>(a, S, nb_cap, pair, j_beg, nb, nl, emit);
+    } else {
+        score_blocks<NW, false>(a, S, nb_cap, pair, j_beg, j_end, nl, emit);
+    }
+}
+
+static hipError_t launch_tiles(const Geo &g, bool update, const void *q, const void *K, void *S,
+                               double *scores, int num_cu, hipStream_t s) {
+    AttnArgs a{};
+    a.q = q;
+    a.K = K;
+    a.hkv = g.hkv;
+    a.gqa = g.gqa;
+    a.t_cap = g.t_cap;
+    a.ctx_len = g.ctx_len;
+    a.block = g.block;
+    a.nb = g.nb;
+    constexpr int kRows = (kTileThreads / 64) * kScoreBatch;  // one round of the 8 waves
+    const int cu = num_cu > 0 ? num_cu : 256;
+    const int tiles = g.pairs >= cu ? 1 : (cu + g.pairs - 1) / g.pairs;
+    int rows = (g.nb + tiles - 1) / tiles;
+    rows = (rows + kRows - 1) / kRows * kRows;
+    const dim3 grid((g.nb + rows - 1) / rows, g.pairs);
+    if (update)
+        k_score_tiles<true><<<grid, kTileThreads, 0, s>>>(a, S, scores, g.nb_cap, rows);
+    else
+        k_score_tiles<false><<<grid, kTileThreads, 0, s>>>(a, S, scores, g.nb_cap, rows);
+    return hipGetLastError();
+}
 
 template <int DT, int TPW, bool UPDATE>
 __global__ __launch_bounds__(256) void k_block_score(const void *__restrict__ qv,
@@ -70,8 +124,12 @@ __global__ __launch_bounds__(256) void k_block_score(const void *__restrict__ qv
         return;
     }
 
+    // With UPDATE the newest row is rewritten by workgroup 0 during this
+    // launch, so no other workgroup loads it (a store to it while loads of
+    // the same lines are in flight can be lost): they cover rows < nb - 1.
+    const int n_rows = UPDATE ? nb - 1 : nb;
     const int wave_j0 = ((blockIdx.x - (UPDATE ? 1 : 0)) * 4 + wave) * kBlocksPerWave;
-    if (wave_j0 >= nb) return;
+    if (wave_j0 >= n_rows) return;
     double qs[8];
     group_query_sum<DT>(qv, b, g, hkv, gqa, sub, qs);
 
@@ -81,7 +139,7 @@ __global__ __launch_bounds__(256) void k_block_score(const void *__restrict__ qv
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int j = min(wave_j0 + 16 * t + 4 * u + grp, nb - 1);
+            const int j = min(wave_j0 + 16 * t + 4 * u + grp, n_rows - 1);
             load_row_slice<DT>(Sv, row0 + j, sub, wa[t][u], wb[t][u]);
         }
 #pragma unroll
@@ -92,8 +150,7 @@ __global__ __launch_bounds__(256) void k_block_score(const void *__restrict__ qv
         const double x = fold4(part, lane);
         const int u = ((lane & 8) ? 2 : 0) + ((lane & 4) ? 1 : 0);
         const int j = wave_j0 + 16 * t + 4 * u + grp;
-        if ((lane & 3) == 0 && j < nb && !(UPDATE && j == newest))
-            store_score(scores, row0 + j, x);
+        if ((lane & 3) == 0 && j < n_rows) store_score(scores, row0 + j, x);
     }
 }
 
@@ -119,15 +176,15 @@ static hipError_t launch_dt(const Geo &g, const void *q, const void *K, void *S,
 }
 
 hipError_t launch_block_score(const Geo &g, const void *q, const void *S, double *scores,
-                              hipStream_t s) {
+                              int num_cu, hipStream_t s) {
     void *Sm = const_cast<void *>(S);  // not written without UPDATE
-    return g.dtype == KIN_BF16 ? launch_dt<KIN_BF16, false>(g, q, nullptr, Sm, scores, s)
+    return g.dtype == KIN_BF16 ? launch_tiles(g, false, q, nullptr, Sm, scores, num_cu, s)
                                : launch_dt<KIN_F32, false>(g, q, nullptr, Sm, scores, s);
 }
 
 hipError_t launch_update_and_score(const Geo &g, const void *q, const void *K, void *S,
-                                   double *scores, hipStream_t s) {
-    return g.dtype == KIN_BF16 ? launch_dt<KIN_BF16, true>(g, q, K, S, scores, s)
+                                   double *scores, int num_cu, hipStream_t s) {
+    return g.dtype == KIN_BF16 ? launch_tiles(g, true, q, K, S, scores, num_cu, s)
                                : launch_dt<KIN_F32, true>(g, q, K, S, scores, s);
 }
 

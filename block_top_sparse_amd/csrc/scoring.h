@@ -1,0 +1,214 @@
+// scoring.h -- the scoring phase of a decode step, run by one workgroup of
+// NW waves over a range of a pair's blocks: the fp64 group scores of the
+// blocks (skill summary "Kinetics: Memory-Aware Test-Time Scaling",
+// Implementation: the mean-score-per-block of BlockTopKAttention, here
+// (sum of the group's queries) . (mean key of the block)), and, when the
+// range holds the newest block, that block's summary rebuilt from K first.
+//
+// Memory pattern: the summary rows stream in 16-block batches (16 lanes per
+// row, 4 rows per 1 KiB load); the NW waves of the workgroup read
+// consecutive batches, so one round covers 16 * NW consecutive rows, and
+// each wave keeps kRing batches in flight (a ring: a batch's slot is
+// refilled right after its math).  Every load is unconditional (rows past
+// the range re-read a row that is never written during the step, and are
+// never used), so the compiler's wait before each batch's math covers
+// exactly that batch's loads.
+//
+// Shared by the single-kernel decode step (step.hip) and the score tiles of
+// the scoring calls (score.hip).
+#pragma once
+
+#include "score_impl.h"
+
+namespace kin {
+
+constexpr int kQPre = 8;    // query rows of the group requested up front
+constexpr int kRing = 4;    // summary batches in flight per wave
+constexpr int kKPre = 16;   // newest-block K rows each wave stages
+constexpr int kScoreBatch = 16;  // blocks per wave per batch
+
+// LDS of the newest-block rebuild: the block's K rows (each wave stages
+// kKPre of them), the count of threads that have staged theirs, the new row.
+template <int NW>
+struct NewestLds {
+    static_assert(NW * kKPre >= 128, "the largest block must fit");
+    uint32_t k[NW * kKPre][kHeadDim / 2];
+    uint32_t row[kHeadDim / 2];
+    uint32_t ready;
+};
+
+// Load the 16-block batch starting at j0 of the rows at `rows`: 16 lanes
+// per row, 4 rows per load (one 1 KiB request), 4 loads.  Rows past j_max
+// re-read row j_max.
+__device__ __forceinline__ void load_batch(const uint16_t *rows, int j0, int j_max, int sub,
+                                           int grp, u32x4 (&w)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int j = min(j0 + 4 * u + grp, j_max);
+        w[u] = ld_nt16(rows + (size_t)j * kHeadDim + 8 * sub);
+    }
+}
+
+// qs[0..8) += the 8 channels of one bf16 query slice if `on`, else += 0.0
+// (exact: the sums start at +0.0, so they are never -0.0).  A select, not a
+// branch, so the slice's load is not moved next to its use.
+__device__ __forceinline__ void add_q_slice(double (&qs)[8], const u32x4 &w, bool on) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        qs[2 * e] += on ? (double)bf16_lo(w[e]) : 0.0;
+        qs[2 * e + 1] += on ? (double)bf16_hi(w[e]) : 0.0;
+    }
+}
+
+// Score one batch (blocks j0 .. j0+15) and hand every score of a block below
+// j_lim to emit(j, score) (one lane per block; -0.0 becomes +0.0).
+template <class Emit>
+__device__ __forceinline__ void score_batch(const double (&qs)[8], const u32x4 (&w)[4], int j0,
+                                            int j_lim, int lane, int grp, Emit &emit) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    double part[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) part[u] = slice_dot<KIN_BF16>(qs, w[u], zero);
+    double x = fold4(part, lane);
+    const int u = ((lane & 8) ? 2 : 0) + ((lane & 4) ? 1 : 0);
+    const int j = j0 + 4 * u + grp;
+    if ((lane & 3) == 0 && j < j_lim) {
+        if (x == 0.0) x = 0.0;  // one zero: -0.0 becomes +0.0
+        emit(j, x);
+    }
+}
+
+// Blocks [j_beg, j_end) of pair `pair` (bf16 cache).  NEWEST: the range ends
+// with the newest block nb - 1 (ctx_len - 1 lies in it): its summary is
+// rebuilt (fp64 sum in ascending token order, fp64 mean, fp32 then bf16
+// rounding), written to S and scored by wave 0 after its batches, with the
+// same math as every other block.  Requires, when NEWEST, nl.ready == 0 and
+// a barrier since.  Ends without a barrier.
+template <int NW, bool NEWEST, class Emit>
+__device__ void score_blocks(const AttnArgs &a, void *Sv, int nb_cap, int pair, int j_beg,
+                             int j_end, NewestLds<NW> &nl, Emit emit) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int sub = lane & 15, grp = lane >> 4;
+    const int b = pair / a.hkv, g = pair % a.hkv;
+    const int nb = a.nb;
+    const size_t row0 = (size_t)pair * nb_cap;
+    const uint16_t *S = static_cast<const uint16_t *>(Sv);
+    const uint16_t *qp = static_cast<const uint16_t *>(a.q) +
+                         ((size_t)b * a.hkv * a.gqa + (size_t)g * a.gqa) * kHeadDim + 8 * sub;
+    constexpr int kStride = NW * kScoreBatch;
+    const int j_lim = NEWEST ? nb - 1 : j_end;  // the newest block is scored apart
+    const int jw = j_beg + wave * kScoreBatch;
+    const int n = jw < j_lim ? (j_lim - jw + kStride - 1) / kStride : 0;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    // Rows loaded past the range (the ring's spare loads) re-read a row that
+    // nothing writes during the step: the last scored row, else the row
+    // before the range, else (a range holding only the newest block of a
+    // one-block context) row 0 of the pair's K.  Never the newest block's
+    // row: a store to it while loads of the same lines are in flight can be
+    // lost.
+    const int j_safe = j_lim > j_beg ? j_lim - 1 : j_beg - 1;
+    const uint16_t *rows = j_safe >= 0 ? S + row0 * kHeadDim
+                                       : static_cast<const uint16_t *>(a.K) +
+                                             (size_t)pair * a.t_cap * kHeadDim;
+    const int j_max = j_safe >= 0 ? j_safe : 0;
+
+    // Issue order: query rows, this wave's share of the newest block's K
+    // rows, batches 0 .. kRing - 1.
+    u32x4 qw[kQPre];
+#pragma unroll
+    for (int r = 0; r < kQPre; ++r)
+        qw[r] = *reinterpret_cast<const u32x4 *>(qp + min(r, a.gqa - 1) * kHeadDim);
+    const int jn = nb - 1;
+    const int tn = min(a.block, a.ctx_len - jn * a.block);
+    const int tw = wave * kKPre;
+    uint32_t kw[kKPre];
+    if (NEWEST) {
+        const uint32_t *kn = static_cast<const uint32_t *>(a.K) +
+                             ((size_t)pair * a.t_cap + (size_t)jn * a.block) * (kHeadDim / 2) +
+                             lane;
+#pragma unroll
+        for (int t = 0; t < kKPre; ++t) kw[t] = kn[(size_t)min(tw + t, tn - 1) * (kHeadDim / 2)];
+    }
+    u32x4 w[kRing][4];
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) {
+        load_batch(rows, jw + r * kStride, j_max, sub, grp, w[r]);
+        // keep slot order: the loop's waits assume slot 0 was issued first
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // group query sum, heads in ascending order (fp64)
+    double qs[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qs[e] = 0.0;
+#pragma unroll
+    for (int r = 0; r < kQPre; ++r) add_q_slice(qs, qw[r], r < a.gqa);
+    for (int r = kQPre; r < a.gqa; ++r)
+        add_q_slice(qs, *reinterpret_cast<const u32x4 *>(qp + r * kHeadDim), true);
+
+    if (NEWEST) {
+        // stage this wave's K rows (rows past the block are never read);
+        // every thread releases its own stores with its own increment
+#pragma unroll
+        for (int t = 0; t < kKPre; ++t) nl.k[tw + t][lane] = kw[t];
+        __hip_atomic_fetch_add(&nl.ready, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+
+    // batch i is scored from slot i % kRing, which then takes batch i + kRing;
+    // every round scores all kRing slots (a batch past the range emits
+    // nothing) and refills them unconditionally
+    for (int i0 = 0; i0 < n; i0 += kRing) {
+#pragma unroll
+        for (int r = 0; r < kRing; ++r) {
+            score_batch(qs, w[r], jw + (i0 + r) * kStride, j_lim, lane, grp, emit);
+            load_batch(rows, jw + (i0 + r + kRing) * kStride, j_max, sub, grp, w[r]);
+        }
+    }
+    // The last refills are used after the loop as well (an empty asm reads
+    // them), so the compiler cannot sink them below the loop test, where
+    // they would become conditional and every wait would turn strict.
+#pragma unroll
+    for (int r = 0; r < kRing; ++r)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            asm volatile("" ::"v"(w[r][v][0]), "v"(w[r][v][1]), "v"(w[r][v][2]), "v"(w[r][v][3]));
+
+    if (NEWEST && wave == 0) {
+        // wait for all NW * 64 threads' stores (every wave stages its rows
+        // before its first batch, so this wait is normally already over)
+        while (__hip_atomic_load(&nl.ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <
+               (uint32_t)(NW * 64))
+            __builtin_amdgcn_s_sleep(1);
+        double s0 = 0.0, s1 = 0.0;  // lane = channels 2 lane, 2 lane + 1
+#pragma unroll 16
+        for (int t = 0; t < tn; ++t) {
+            const uint32_t v = nl.k[t][lane];
+            s0 += (double)bf16_lo(v);
+            s1 += (double)bf16_hi(v);
+        }
+        const double cnt = (double)tn;
+        const float m0 = (float)(s0 / cnt), m1 = (float)(s1 / cnt);
+        const uint32_t v = f32_to_bf16_bits(m0) | (f32_to_bf16_bits(m1) << 16);
+        static_cast<uint32_t *>(Sv)[(row0 + jn) * (kHeadDim / 2) + lane] = v;
+        nl.row[lane] = v;
+
+        // the newest row in slot u = 0 of row group 0, zero rows elsewhere:
+        // the butterfly every block goes through
+        u32x4 r = zero;
+        if (grp == 0) {
+            const uint32_t *p = nl.row + 4 * sub;
+            r = u32x4{p[0], p[1], p[2], p[3]};
+        }
+        double part[4];
+        part[0] = slice_dot<KIN_BF16>(qs, r, zero);
+        part[1] = part[2] = part[3] = slice_dot<KIN_BF16>(qs, zero, zero);
+        double x = fold4(part, lane);
+        if (lane == 0) {
+            if (x == 0.0) x = 0.0;
+            emit(jn, x);
+        }
+    }
+}
+
+}  // namespace kin

@@ -13,12 +13,15 @@
 // j = e * NT + tid).  Each fp64 score maps to an unsigned 64-bit key with
 // the same order (flip all bits of negatives, set the sign bit of the
 // rest).  An MSD radix select finds the k-th largest key.  Its top 12 bits
-// (sign and exponent) come from two count tables filled one atomic per key
-// before the select starts: by bits 63..56 (256 bins) and by bits 63..52
-// (4096 bins).  Every wave reads both tables itself (the 256 coarse bins,
-// then the 16 fine bins under the chosen coarse one), so fixing the
-// exponent costs no barrier; the fused decode step fills the tables while
-// it computes the scores, where the atomics hide under HBM latency.  The
+// (sign and exponent) come either from two count tables filled one atomic
+// per key while the scores are computed (COUNTED: the fused decode step,
+// where the atomics hide under HBM latency; by bits 63..56, 256 bins, and
+// by bits 63..52, 4096 bins; every wave reads the 256 coarse bins, then the
+// 16 fine bins under the chosen coarse one, with no barrier), or, when the
+// scores arrive ready-made, from a search down from the largest bin: the
+// keys of the 8 bins below it are counted with ballots per round (a pair's
+// scores sit in a few neighbouring bins, and per-key LDS atomics on those
+// few words would queue), falling back to the tables after two rounds.  The
 // mantissa follows 8 bits at a time (the last 4): each pass builds an LDS
 // histogram of the digit among the keys that still match the prefix (one
 // LDS atomic per candidate), then EVERY wave scans the 256 bins itself
@@ -44,6 +47,9 @@ struct SelectLds {
     uint32_t hist[3][256];  // mantissa passes
     uint32_t cnt[KPT * (NT / 64)];
     uint32_t cnt_tie[KPT * (NT / 64)];
+    uint32_t wtop[NT / 64];             // per wave: largest sign/exponent bin
+    uint32_t wcnt[2][8 * (NT / 64)];    // per round, bin and wave: keys counted
+    static_assert(NT / 64 <= 8, "the bin counts of all waves fit one wave");
 };
 
 __device__ __forceinline__ uint64_t order_key(double s) {
@@ -131,6 +137,25 @@ __device__ __forceinline__ void offsets_of(const uint32_t *cnt, int wave, int la
     }
 }
 
+// table[bin] += 1 for every lane with `on`, one atomic per distinct bin of
+// the wave instead of one per lane: the scores of a pair fall into a few
+// sign/exponent bins, so per-lane atomics would queue on the same words.
+// The first two distinct bins are added by their lowest lane with a
+// population count; lanes with other bins add 1 each.
+__device__ __forceinline__ void count_wave_aggregated(uint32_t *table, uint32_t bin, bool on) {
+#pragma unroll
+    for (int round = 0; round < 2; ++round) {
+        const uint64_t act = __ballot(on);
+        if (act == 0) return;
+        const int src = __builtin_ctzll(act);
+        const uint32_t lead = lane_value(bin, src);
+        const uint64_t same = __ballot(on && bin == lead);
+        if ((int)(threadIdx.x & 63) == src) atomicAdd(&table[lead], (uint32_t)__popcll(same));
+        on = on && bin != lead;
+    }
+    if (on) atomicAdd(&table[bin], 1u);
+}
+
 // Every wave: the bin holding the krem-th largest key, given that lane l
 // holds the counts c[0..3] of bins base - 4l .. base - 4l - 3 (descending
 // digits).  Returns the digit, the keys in bins above it and in it.
@@ -190,18 +215,89 @@ __device__ void select_topk(const double *__restrict__ sc, int nb, int k, int32_
     for (int e = 0; e < KPT; ++e) {
         const int j = e * NT + tid;
         key[e] = order_key(v[e]) & (0ull - (uint64_t)(j < nb));  // a mask, not a branch
-        if (!COUNTED && j < nb) {
-            atomicAdd(&lds.coarse[key[e] >> 56], 1u);
-            atomicAdd(&lds.fine[key[e] >> 52], 1u);
-        }
     }
-    if (!COUNTED) __syncthreads();
 
-    // sign and exponent: the coarse bin, then the fine bin under it
+    // sign and exponent of the k-th key
     uint32_t krem = (uint32_t)keff;
-    uint64_t prefix, pmask = 0xFFFull << 52;
-    uint32_t in_bin;
-    {
+    uint64_t prefix = 0, pmask = 0xFFFull << 52;
+    uint32_t in_bin = 0;
+    bool have = COUNTED;  // COUNTED: read off the count tables below
+    if (!COUNTED) {
+        // Without count tables: the largest sign/exponent bin of the pair,
+        // then the keys in the 8 bins below it counted with ballots (no
+        // atomics; a pair's scores sit in a few neighbouring bins, so the
+        // k-th key is almost always there), one barrier per round of 8.
+        uint32_t top = 0;
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) top = max(top, (uint32_t)(key[e] >> 52));  // invalid: 0
+        top = wave_max(top);
+        if (lane == 0) lds.wtop[wave] = top;
+        __syncthreads();
+        top = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) top = max(top, lds.wtop[w]);
+        bool found = false;
+#pragma unroll
+        for (int round = 0; round < 2; ++round) {
+            if (found) break;
+            const uint32_t base = 8u * round;
+            // this lane's keys per bin q, two 16-bit counters per word
+            // (a wave holds at most 64 * 32 keys, so the sums fit)
+            uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                const bool valid = e * NT + tid < nb;
+                const uint32_t d = top - (uint32_t)(key[e] >> 52) - base;
+                const uint32_t inc = (valid && d < 8u) ? 1u << (16 * (d & 1u)) : 0u;
+#pragma unroll
+                for (int h = 0; h < 4; ++h) c[h] += (d >> 1) == (uint32_t)h ? inc : 0u;
+            }
+#pragma unroll
+            for (int h = 0; h < 4; ++h) c[h] = wave_incl_scan(c[h]);  // lane 63: the wave's
+            if (lane == 63) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    lds.wcnt[round][q * NW + wave] = (c[q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
+            }
+            __syncthreads();
+            // lane q * NW + w reads one count; bin q's total is the scan's
+            // step over lanes q * NW .. q * NW + NW - 1
+            const uint32_t mine = lane < 8 * NW ? lds.wcnt[round][lane] : 0u;
+            const uint32_t incl = wave_incl_scan(mine);
+            uint32_t run = 0;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const uint32_t total = lane_value(incl, q * NW + NW - 1) - run;
+                if (!found && run + total >= krem) {
+                    found = true;
+                    prefix = (uint64_t)(top - base - q) << 52;
+                    krem -= run;
+                    in_bin = total;
+                }
+                run += total;
+            }
+            if (!found) krem -= run;
+        }
+        if (!found) {
+            // far below the top (e.g. across zero): the count tables after all
+            krem = (uint32_t)keff;
+#pragma unroll
+            for (int e = 0; e < KPT; ++e)
+                count_wave_aggregated(lds.fine, (uint32_t)(key[e] >> 52), e * NT + tid < nb);
+            __syncthreads();
+            for (int i = tid; i < 256; i += NT) {  // coarse = fine summed over 16 bins
+                const uint32_t *f = lds.fine + 16 * i;
+                uint32_t c = 0;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) c += f[r];
+                lds.coarse[i] = c;
+            }
+            __syncthreads();
+        }
+        have = !found;
+    }
+    if (have) {
+        // from the count tables: the coarse bin, then the fine bin under it
         uint32_t c[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) c[r] = lds.coarse[255 - 4 * lane - r];

@@ -123,6 +123,80 @@ def test_single_kernel_step_against_oracle(case):
     say(f"  ok {r}")
 
 
+FEW_PAIRS = [
+    # name, batch, hq, hkv, ctx, block, k, dtype, t_cap  (bf16, fewer pairs than CUs: the
+    # two-kernel step)
+    ("few-g4-b16-ragged", 3, 16, 4, 5000, 16, 40, "bf16", 5120),
+    ("few-g8-b64-k1", 2, 64, 8, 3000, 64, 1, "bf16", 3072),         # one split
+    ("few-g5-b32-kpast", 4, 20, 4, 700, 32, 40, "bf16", 704),       # k > nb
+    ("few-g1-b16-nb8192", 1, 2, 2, 131072, 16, 512, "bf16", 131072),
+    ("few-g16-b128", 2, 64, 4, 20000, 128, 10, "bf16", 20096),
+]
+
+
+@pytest.mark.parametrize("case", FEW_PAIRS, ids=[c[0] for c in FEW_PAIRS])
+def test_few_pair_step_against_oracle(case):
+    """kin_sparse_decode_step with few pairs (split attention): the selection
+    must equal the four-call path's, the output the oracle's, and repeated
+    calls on the same workspace must agree bitwise, with or without a scores
+    buffer."""
+    name, b, hq, hkv, L, B, k, dt, cap = case
+    w = Workload(name, batch=b, hq=hq, hkv=hkv, ctx_len=L, block=B, topk=k, dtype=dt,
+                 seed=zlib.crc32(name.encode()) % 10000, t_cap=cap)
+    say(f"case {name}: {w.describe()}")
+    inp = gpu_inputs(w)
+    ref = run_gpu(w, inp)  # four calls
+    step = run_gpu(w, inp, step=True)
+    assert torch.equal(step.idx, ref.idx)
+    assert torch.equal(step.scores[:, :, :w.nb], ref.scores[:, :, :w.nb])
+    r = check_sequences(w, inp, step, range(b))
+    out1 = step.out.clone()
+    again = run_gpu(w, inp, step=True, bufs=step)
+    assert torch.equal(bits(again.out), bits(out1))
+    quiet = run_gpu(w, inp, step=True, no_scores=True)
+    assert torch.equal(quiet.idx, ref.idx)
+    assert torch.equal(bits(quiet.out), bits(out1))
+    say(f"  ok {r}")
+
+
+NEWEST_ROW = [
+    # name, batch, hq, hkv, ctx, block, k, dtype, t_cap
+    ("newest-single-nb1", 16, 256, 16, 100, 128, 2, "bf16", 128),   # one kernel, one block
+    ("newest-single-nb2", 32, 64, 8, 150, 128, 1, "bf16", 256),     # one kernel, two blocks
+    ("newest-few-nb1", 2, 16, 4, 90, 128, 3, "bf16", 128),          # two kernels
+    ("newest-few-nb3", 2, 16, 4, 40, 16, 1, "bf16", 48),
+    ("newest-two-kernel-f32", 2, 8, 2, 70, 64, 1, "f32", 128),      # update + score kernel
+]
+
+
+@pytest.mark.parametrize("case", NEWEST_ROW, ids=[c[0] for c in NEWEST_ROW])
+def test_newest_row_independent_of_old_contents(case):
+    """The step rewrites the newest block's summary row while it scores the
+    other rows; the row must come out as the oracle's whatever S held before
+    (no load of that row may be in flight while it is stored)."""
+    name, b, hq, hkv, L, B, k, dt, cap = case
+    w = Workload(name, batch=b, hq=hq, hkv=hkv, ctx_len=L, block=B, topk=k, dtype=dt,
+                 seed=zlib.crc32(name.encode()) % 10000, t_cap=cap)
+    say(f"case {name}: {w.describe()}")
+    inp = gpu_inputs(w)
+    S_or, _ = oracle.block_summary(inp["K"].cpu(), w.block, w.ctx_len)
+    want = bits(S_or[:, :, :w.nb])
+    for fill in (0.0, 1.0, -3.0, float("nan")):
+        for scores in (True, False):
+            bufs = LayerBuffers(w)
+            newest0 = (w.nb - 1) * w.block
+            if newest0 > 0:
+                kb.kin_block_summary_update(bufs.desc, inp["K"], bufs.S, 0, newest0)
+            bufs.S[:, :, w.nb - 1:].fill_(fill)
+            kb.kin_sparse_decode_step(bufs.desc, inp["q"], inp["K"], inp["V"], bufs.S,
+                                      bufs.scores if scores else None, bufs.k, bufs.idx,
+                                      bufs.out, bufs.ws)
+            torch.cuda.synchronize()
+            got = bits(bufs.S[:, :, :w.nb].cpu())
+            assert torch.equal(got, want), f"fill {fill}, scores {scores}"
+    say("  ok")
+
+
 NO_SCORES_TWO_KERNEL = [
     # name, batch, hq, hkv, ctx, block, k, dtype, t_cap  (few pairs: two kernels)
     ("nosc-g4-b16", 2, 8, 2, 3000, 16, 24, "bf16", 3072),
