@@ -37,6 +37,20 @@ class kin_desc(ctypes.Structure):
         return "kin_desc(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
 
 
+class kin_pages(ctypes.Structure):
+    """Variable lengths / paged caches: device pointers (ctx_lens [batch],
+    page_table [batch][max_pages], int32, or None) and the page geometry."""
+    _fields_ = [("ctx_lens", ctypes.c_void_p), ("page_table", ctypes.c_void_p),
+                ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32)]
+
+
+def make_pages(ctx_lens=None, page_table=None, page_size=0, max_pages=0, num_pages=0):
+    """A kin_pages from torch int32 device tensors (or None)."""
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    return kin_pages(ptr(ctx_lens), ptr(page_table), page_size, max_pages, num_pages)
+
+
 def make_desc(batch, hkv, gqa, t_cap, ctx_len, block, dtype, head_dim=128) -> kin_desc:
     dt = _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     return kin_desc(batch, hkv, gqa, head_dim, t_cap, ctx_len, block, dt)
@@ -53,6 +67,7 @@ def lib():
                               "(or python block_top_sparse_amd/build.py) first")
         L = ctypes.CDLL(LIB_PATH)
         D, P, I, Z = ctypes.POINTER(kin_desc), ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        G = ctypes.POINTER(kin_pages)
         sig = {
             "kin_block_summary_update": (I, [D, P, P, I, I, P]),
             "kin_block_score": (I, [D, P, P, P, P]),
@@ -67,6 +82,8 @@ def lib():
             "kin_status_str": (ctypes.c_char_p, [I]),
             "kin_last_error": (ctypes.c_char_p, []),
             "kin_version": (I, []),
+            "kin_paged_summary_update": (I, [D, G, P, P, I, I, P]),
+            "kin_paged_decode_step": (I, [D, G, P, P, P, P, P, I, P, P, P, Z, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -80,7 +97,7 @@ def exported_names():
             "kin_sparse_decode_attn", "kin_dense_decode_attn", "kin_sparse_decode_step",
             "kin_decode_update_score", "kin_decode_select_attend",
             "kin_sparse_ws_bytes", "kin_dense_ws_bytes", "kin_status_str", "kin_last_error",
-            "kin_version"]
+            "kin_version", "kin_paged_summary_update", "kin_paged_decode_step"]
 
 
 def _p(t):
@@ -135,6 +152,17 @@ def kin_sparse_decode_step(desc, q, K, V, S, scores, k, idx, out, ws=None, strea
     _check(lib().kin_sparse_decode_step(ctypes.byref(desc), _p(q), _p(K), _p(V), _p(S),
                                         _p(scores), k, _p(idx), _p(out), _p(ws), _nbytes(ws),
                                         _s(stream)))
+
+
+def kin_paged_summary_update(desc, pages, K, S, t_begin, t_end, stream=None):
+    _check(lib().kin_paged_summary_update(ctypes.byref(desc), ctypes.byref(pages), _p(K), _p(S),
+                                          t_begin, t_end, _s(stream)))
+
+
+def kin_paged_decode_step(desc, pages, q, K, V, S, scores, k, idx, out, ws=None, stream=None):
+    _check(lib().kin_paged_decode_step(ctypes.byref(desc), ctypes.byref(pages), _p(q), _p(K),
+                                       _p(V), _p(S), _p(scores), k, _p(idx), _p(out), _p(ws),
+                                       _nbytes(ws), _s(stream)))
 
 
 def kin_decode_update_score(desc, q, K, S, scores, stream=None):

@@ -49,8 +49,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(AttnArgs a) {
     const int cps = (a.n_chunks + a.nsplit - 1) / a.nsplit;
     const int c_beg = split * cps;
     const int c_end = min(a.n_chunks, c_beg + cps);
-    const int32_t *sel = DENSE ? nullptr : a.idx + (size_t)pair * a.k;
-    attend_bf16<DENSE, 4>(a, sel, pair, c_beg, c_end, wave, 4, wave, sm);
+    if (DENSE)
+        attend_bf16<DenseRuns, 4>(a, dense_runs(a, pair), pair, c_beg, c_end, wave, 4, wave, sm);
+    else
+        attend_bf16<ListRuns, 4>(a, list_runs(a, pair, a.idx + (size_t)pair * a.k), pair, c_beg,
+                                 c_end, wave, 4, wave, sm);
     __syncthreads();
     merge_waves_and_store<KIN_BF16, 4>(a, sm, pair, split);
 }
@@ -77,8 +80,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_f32(AttnArgs a) {
 // (pair, split); every split of a pair repeats the same selection)
 // ---------------------------------------------------------------------------
 
-template <int DT, int KPT>
-__global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a,
+template <int DT, int KPT, bool PAGED>
+__global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a0,
                                                                 const double *__restrict__ scores,
                                                                 int nb_cap, int32_t *idx_out,
                                                                 uint64_t *ctrl, uint32_t epoch) {
@@ -91,6 +94,7 @@ __global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a,
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int split = blockIdx.x, pair = blockIdx.y;
+    const AttnArgs a = for_pair(a0, pair);  // this sequence's own length
     select_clear(u.s);
     __syncthreads();
     select_topk<KPT, kStepThreads, false>(scores + (size_t)pair * nb_cap, a.nb, a.k, sel, u.s);
@@ -102,8 +106,20 @@ __global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a,
     const int cps = (a.n_chunks + a.nsplit - 1) / a.nsplit;
     const int c_beg = split * cps;
     const int c_end = min(a.n_chunks, c_beg + cps);
-    if constexpr (DT == KIN_BF16) {
-        attend_bf16<false, NW>(a, sel, pair, c_beg, c_end, wave, NW, wave, u.m);
+    if constexpr (DT == KIN_BF16 && PAGED) {
+        // first row of every kept block (a block lies inside one page)
+        __shared__ int64_t selrow[kStepIdxCap];
+        for (int i = threadIdx.x; i < a.k; i += kStepThreads) {
+            const int id = sel[i];
+            selrow[i] = id >= 0 && id < a.nb ? token_row(a, pair, id * a.block) : -1;
+        }
+        __syncthreads();
+        const PagedRuns runs{sel, selrow, token_row(a, pair, 0), a.k, a.nb, a.block,
+                             a.block_shift};
+        attend_bf16<PagedRuns, NW>(a, runs, pair, c_beg, c_end, wave, NW, wave, u.m);
+    } else if constexpr (DT == KIN_BF16) {
+        attend_bf16<ListRuns, NW>(a, list_runs(a, pair, sel), pair, c_beg, c_end, wave, NW, wave,
+                                  u.m);
     } else {
         __shared__ F32Lds<NW> fl;
         load_q_f32<NW>(a, pair, fl);
@@ -243,7 +259,10 @@ template <int DT>
 static void launch_sa(const Geo &g, const AttnArgs &a, dim3 grid, const double *scores,
                       int32_t *idx, uint64_t *ctrl, uint32_t epoch, hipStream_t s) {
 #define KIN_SA(KPT)                                                                            \
-    k_select_attend<DT, KPT><<<grid, kStepThreads, 0, s>>>(a, scores, g.nb_cap, idx, ctrl, epoch)
+    (g.pages ? k_select_attend<DT, KPT, true><<<grid, kStepThreads, 0, s>>>(a, scores, g.nb_cap, \
+                                                                            idx, ctrl, epoch)    \
+             : k_select_attend<DT, KPT, false><<<grid, kStepThreads, 0, s>>>(a, scores, g.nb_cap, \
+                                                                             idx, ctrl, epoch))
     switch (select_kpt(g.nb, kStepThreads)) {
     case 1: KIN_SA(1); break;
     case 2: KIN_SA(2); break;

@@ -15,7 +15,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kAttnThreads = 256;  // standalone attention: 4 waves
 constexpr int kStepThreads = 512;  // fused select + attention: 8 waves
-constexpr int kStepIdxCap = 2048;  // kept blocks the fused kernel holds in LDS
 
 struct AttnArgs {
     const void *q, *K, *V;
@@ -25,23 +24,88 @@ struct AttnArgs {
     float *ws_ml;  // [batch][hq][nsplit][2]   (running max in log2 units, sum)
     int hkv, gqa, t_cap, ctx_len, block, block_shift, nb, k, nsplit, n_chunks;
     float scale_log2;  // log2(e) / sqrt(head_dim)
+    // variable lengths and paged caches (both null: every sequence holds
+    // ctx_len tokens in a contiguous [pair][t_cap] cache)
+    const int32_t *ctx_lens;  // [batch] tokens per sequence (clamped to [1, ctx_len])
+    const int32_t *pages;     // [batch][max_pages] page of the pool per page_size tokens
+    int page_shift, max_pages, num_pages;
 };
 
-// Resolve list position p0 .. p0+15 (16 consecutive positions inside one
-// block) to the first token of that run; valid = false if the slot is
-// empty or past the list.  `sel` may point to global memory or LDS.
-template <bool DENSE>
-__device__ __forceinline__ int run_base(const AttnArgs &a, const int32_t *sel, int p0,
-                                        bool &valid) {
-    if (DENSE) {
-        valid = p0 < a.ctx_len;
-        return p0;
+// This pair's arguments: its own context length, block count and chunk
+// count when the sequences differ in length.
+__device__ __forceinline__ AttnArgs for_pair(const AttnArgs &a, int pair) {
+    AttnArgs p = a;
+    if (a.ctx_lens) {
+        const int L = min(max(a.ctx_lens[pair / a.hkv], 1), a.ctx_len);
+        p.ctx_len = L;
+        p.nb = (L + a.block - 1) >> a.block_shift;
+        p.n_chunks = (min(a.k, p.nb) * a.block + kChunkBf16 - 1) / kChunkBf16;
     }
-    const int slot = p0 >> a.block_shift;
-    const int id = slot < a.k ? sel[slot] : -1;
-    valid = id >= 0 && id < a.nb;
-    return id * a.block + (p0 & (a.block - 1));
+    return p;
 }
+
+// Row (in head_dim-element rows from the cache base) of token t of `pair`:
+// [pair][t_cap] contiguous, or [page][hkv][page_size] through the page table
+// (an entry outside the pool is clamped into it).
+__device__ __forceinline__ int64_t token_row(const AttnArgs &a, int pair, int t) {
+    if (!a.pages) return (int64_t)pair * a.t_cap + t;
+    const int b = pair / a.hkv, g = pair % a.hkv;
+    int page = a.pages[(size_t)b * a.max_pages + (t >> a.page_shift)];
+    page = min(max(page, 0), a.num_pages - 1);
+    return (((int64_t)page * a.hkv + g) << a.page_shift) + (t & ((1 << a.page_shift) - 1));
+}
+
+// Where the tokens of list positions p0 .. p0+15 (16 consecutive positions
+// inside one block) live: run(p0, valid, t0) gives the K/V row (in
+// head_dim-element rows from the cache base) of position p0's token and that
+// token's index t0 in its sequence; the run's other tokens follow in the
+// next rows.  valid = false if the slot is empty or past the list.  `safe`
+// is a row that may always be read (for lanes whose token does not count).
+
+// all tokens [0, ctx_len) of one pair, contiguous cache [pair][t_cap]
+struct DenseRuns {
+    int64_t row0;  // the pair's first row
+    int ctx_len;
+    __device__ int64_t run(int p0, bool &valid, int &t0) const {
+        valid = p0 < ctx_len;
+        t0 = p0;
+        return row0 + p0;
+    }
+    __device__ int64_t safe() const { return row0; }
+};
+
+// the kept blocks `sel` (global memory or LDS) of one pair, contiguous cache
+struct ListRuns {
+    int64_t row0;
+    const int32_t *sel;
+    int k, nb, block, block_shift;
+    __device__ int64_t run(int p0, bool &valid, int &t0) const {
+        const int slot = p0 >> block_shift;
+        const int id = slot < k ? sel[slot] : -1;
+        valid = id >= 0 && id < nb;
+        t0 = id * block + (p0 & (block - 1));
+        return row0 + t0;
+    }
+    __device__ int64_t safe() const { return row0; }
+};
+
+// the kept blocks of one pair in a paged cache: selrow[slot] is the row of
+// block sel[slot]'s first token (a block lies inside one page), or -1
+struct PagedRuns {
+    const int32_t *sel;
+    const int64_t *selrow;
+    int64_t safe_row;
+    int k, nb, block, block_shift;
+    __device__ int64_t run(int p0, bool &valid, int &t0) const {
+        const int slot = p0 >> block_shift;
+        const int id = slot < k ? sel[slot] : -1;
+        valid = id >= 0 && id < nb;
+        const int off = p0 & (block - 1);
+        t0 = id * block + off;
+        return valid ? selrow[slot] + off : safe_row;
+    }
+    __device__ int64_t safe() const { return safe_row; }
+};
 
 // LDS the waves of one workgroup merge through: per wave, per head, the
 // running max, running sum and unnormalised output.
@@ -214,26 +278,26 @@ struct WaveState {
     float l_run;  // this lane's share of the running sum of head j
 };
 
-template <bool DENSE>
-__device__ __forceinline__ void load_chunk(const AttnArgs &a, const int32_t *sel,
-                                           const uint16_t *Kp, const uint16_t *Vp, int c, int j,
-                                           int g4, ChunkRegs &cr) {
+template <class Runs>
+__device__ __forceinline__ void load_chunk(const AttnArgs &a, const Runs &runs, const uint16_t *K,
+                                           const uint16_t *V, int c, int j, int g4,
+                                           ChunkRegs &cr) {
     cr.ok = 0;
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
         bool valid;
-        const int base = run_base<DENSE>(a, sel, c * kChunkBf16 + 16 * tau, valid);
-        const int tk = base + j;
-        const int rowk = (valid && tk < a.ctx_len) ? tk : 0;
+        int t0;
+        const int64_t row0 = runs.run(c * kChunkBf16 + 16 * tau, valid, t0);
+        const int64_t rowk = (valid && t0 + j < a.ctx_len) ? row0 + j : runs.safe();
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-            cr.k[tau][kk] = ld_nt16(Kp + (size_t)rowk * kHeadDim + 32 * kk + 8 * g4);
+            cr.k[tau][kk] = ld_nt16(K + rowk * kHeadDim + 32 * kk + 8 * g4);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int tv = base + 4 * g4 + r;
-            const bool ok = valid && tv < a.ctx_len;
+            const int dv = 4 * g4 + r;
+            const bool ok = valid && t0 + dv < a.ctx_len;
             cr.ok |= (ok ? 1u : 0u) << (4 * tau + r);
-            cr.v[4 * tau + r] = ld_nt16(Vp + (size_t)(ok ? tv : 0) * kHeadDim + 8 * j);
+            cr.v[4 * tau + r] = ld_nt16(V + (ok ? row0 + dv : runs.safe()) * kHeadDim + 8 * j);
         }
     }
 }
@@ -291,15 +355,16 @@ __device__ __forceinline__ void compute_chunk(const ChunkRegs &cr, const bf16x8 
 
 // One wave's share of a pair's chunks [c_beg, c_end), every `step`-th chunk
 // starting at c_beg + first, then its (m, l, o) into merge slot `slot`.
-template <bool DENSE, int NW>
-__device__ void attend_bf16(const AttnArgs &a, const int32_t *sel, int pair, int c_beg,
+// `runs` maps list positions to cache rows (DenseRuns, ListRuns, PagedRuns).
+template <class Runs, int NW>
+__device__ void attend_bf16(const AttnArgs &a, const Runs &runs, int pair, int c_beg,
                             int c_end, int first, int step, int slot, MergeLds<NW> &sm) {
     const int lane = threadIdx.x & 63;
     const int j = lane & 15, g4 = lane >> 4;
     const int b = pair / a.hkv, gk = pair % a.hkv;
     const int hq = a.hkv * a.gqa;
-    const uint16_t *Kp = static_cast<const uint16_t *>(a.K) + (size_t)pair * a.t_cap * kHeadDim;
-    const uint16_t *Vp = static_cast<const uint16_t *>(a.V) + (size_t)pair * a.t_cap * kHeadDim;
+    const uint16_t *Kp = static_cast<const uint16_t *>(a.K);
+    const uint16_t *Vp = static_cast<const uint16_t *>(a.V);
 
     // B operand of S^T = K . Q^T: head j, channels 32*kk + 8*g4 .. +8
     bf16x8 qb[4];
@@ -327,16 +392,16 @@ __device__ void attend_bf16(const AttnArgs &a, const int32_t *sel, int pair, int
     const int n = c0 < c_end ? (c_end - c0 + step - 1) / step : 0;
     ChunkRegs ra, rb;
     if (n > 0) {
-        load_chunk<DENSE>(a, sel, Kp, Vp, c0, j, g4, ra);
+        load_chunk(a, runs, Kp, Vp, c0, j, g4, ra);
         int i = 0;
         for (; i + 2 < n; i += 2) {
-            load_chunk<DENSE>(a, sel, Kp, Vp, c0 + (i + 1) * step, j, g4, rb);
+            load_chunk(a, runs, Kp, Vp, c0 + (i + 1) * step, j, g4, rb);
             compute_chunk(ra, qb, a.scale_log2, g4, st);
-            load_chunk<DENSE>(a, sel, Kp, Vp, c0 + (i + 2) * step, j, g4, ra);
+            load_chunk(a, runs, Kp, Vp, c0 + (i + 2) * step, j, g4, ra);
             compute_chunk(rb, qb, a.scale_log2, g4, st);
         }
         if (n - i == 2) {
-            load_chunk<DENSE>(a, sel, Kp, Vp, c0 + (i + 1) * step, j, g4, rb);
+            load_chunk(a, runs, Kp, Vp, c0 + (i + 1) * step, j, g4, rb);
             compute_chunk(ra, qb, a.scale_log2, g4, st);
             compute_chunk(rb, qb, a.scale_log2, g4, st);
         } else {
@@ -354,6 +419,13 @@ __device__ void attend_bf16(const AttnArgs &a, const int32_t *sel, int pair, int
     for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int n = 0; n < 8; ++n) sm.o[slot][4 * g4 + r][8 * j + n] = st.o[n][r];
+}
+
+__device__ __forceinline__ DenseRuns dense_runs(const AttnArgs &a, int pair) {
+    return DenseRuns{(int64_t)pair * a.t_cap, a.ctx_len};
+}
+__device__ __forceinline__ ListRuns list_runs(const AttnArgs &a, int pair, const int32_t *sel) {
+    return ListRuns{(int64_t)pair * a.t_cap, sel, a.k, a.nb, a.block, a.block_shift};
 }
 
 // ---------------------------------------------------------------------------
@@ -507,6 +579,11 @@ inline void fill_args(AttnArgs &a, const Geo &g, const AttnPlan &p, const void *
     a.nsplit = p.nsplit;
     a.n_chunks = p.n_chunks;
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kHeadDim));
+    a.ctx_lens = g.ctx_lens;
+    a.pages = g.pages;
+    a.page_shift = g.page_shift;
+    a.max_pages = g.max_pages;
+    a.num_pages = g.num_pages;
 }
 
 }  // namespace kin

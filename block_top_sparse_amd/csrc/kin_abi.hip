@@ -251,14 +251,11 @@ kin_status kin_decode_select_attend(const kin_desc *desc, const void *q, const v
                     "kin_decode_select_attend");
 }
 
-kin_status kin_sparse_decode_step(const kin_desc *desc, const void *q, const void *K,
-                                  const void *V, void *S, double *scores, int32_t k,
-                                  int32_t *idx, void *out, void *ws, size_t ws_bytes,
-                                  kin_stream stream) {
-    // check everything before enqueueing anything
-    kin::Geo g;
-    kin_status st = check_step(desc, &g);
-    if (st != KIN_OK) return st;
+// The decode step for a checked geometry (contiguous or paged).
+static kin_status decode_step(const kin::Geo &g, const void *q, const void *K, const void *V,
+                              void *S, double *scores, int32_t k, int32_t *idx, void *out,
+                              void *ws, size_t ws_bytes, kin_stream stream) {
+    kin_status st;
     KIN_REQUIRE_PTR(q);
     KIN_REQUIRE_PTR(K);
     KIN_REQUIRE_PTR(V);
@@ -286,6 +283,78 @@ kin_status kin_sparse_decode_step(const kin_desc *desc, const void *q, const voi
     if (e == hipSuccess)
         e = kin::launch_select_attend(g, p, q, K, V, sc, k, idx, out, ws, next_epoch(), s);
     return launched(e, "kin_sparse_decode_step");
+}
+
+kin_status kin_sparse_decode_step(const kin_desc *desc, const void *q, const void *K,
+                                  const void *V, void *S, double *scores, int32_t k,
+                                  int32_t *idx, void *out, void *ws, size_t ws_bytes,
+                                  kin_stream stream) {
+    // check everything before enqueueing anything
+    kin::Geo g;
+    kin_status st = check_step(desc, &g);
+    if (st != KIN_OK) return st;
+    return decode_step(g, q, K, V, S, scores, k, idx, out, ws, ws_bytes, stream);
+}
+
+// Variable lengths and paged caches: the descriptor plus the kin_pages
+// fields, checked; the kernels read ctx_lens and the page table on the
+// device.
+static kin_status check_pages(const kin_desc *desc, const kin_pages *pg, kin::Geo *g) {
+    kin_status st = check_step(desc, g);
+    if (st != KIN_OK) return st;
+    if (!pg) return fail(KIN_ERR_NULL, "pages is NULL");
+    if (g->dtype != KIN_BF16)
+        return fail(KIN_ERR_UNSUPPORTED, "variable lengths and paged caches: bf16 only");
+    if (pg->ctx_lens && ((uintptr_t)pg->ctx_lens & 3u))
+        return fail(KIN_ERR_ALIGN, "ctx_lens is not 4-byte aligned");
+    if (pg->page_table) {
+        if ((uintptr_t)pg->page_table & 3u)
+            return fail(KIN_ERR_ALIGN, "page_table is not 4-byte aligned");
+        const int P = pg->page_size;
+        if (P < 16 || (P & (P - 1)) || P < g->block || P % g->block)
+            return fail(KIN_ERR_SHAPE,
+                        "page_size = %d: need a power of two >= 16, a multiple of block %d", P,
+                        g->block);
+        if (pg->max_pages < 1 || pg->num_pages < 1)
+            return fail(KIN_ERR_SHAPE, "max_pages = %d, num_pages = %d: need >= 1",
+                        pg->max_pages, pg->num_pages);
+        if ((long long)pg->max_pages * P != g->t_cap)
+            return fail(KIN_ERR_SHAPE, "t_cap = %d: need max_pages * page_size = %lld", g->t_cap,
+                        (long long)pg->max_pages * P);
+        g->pages = pg->page_table;
+        g->page_shift = __builtin_ctz((unsigned)P);
+        g->max_pages = pg->max_pages;
+        g->num_pages = pg->num_pages;
+    }
+    g->ctx_lens = pg->ctx_lens;
+    return KIN_OK;
+}
+
+kin_status kin_paged_summary_update(const kin_desc *desc, const kin_pages *pages, const void *K,
+                                    void *S, int32_t t_begin, int32_t t_end, kin_stream stream) {
+    kin::Geo g;
+    kin_status st = check_pages(desc, pages, &g);
+    if (st != KIN_OK) return st;
+    KIN_REQUIRE_PTR(K);
+    KIN_REQUIRE_PTR(S);
+    if (t_begin < 0 || t_end < t_begin || t_end > g.t_cap)
+        return fail(KIN_ERR_SHAPE, "need 0 <= t_begin (%d) <= t_end (%d) <= t_cap (%d)", t_begin,
+                    t_end, g.t_cap);
+    return launched(kin::launch_block_summary_paged(g, K, S, t_begin, t_end, (hipStream_t)stream),
+                    "kin_paged_summary_update");
+}
+
+kin_status kin_paged_decode_step(const kin_desc *desc, const kin_pages *pages, const void *q,
+                                 const void *K, const void *V, void *S, double *scores,
+                                 int32_t k, int32_t *idx, void *out, void *ws, size_t ws_bytes,
+                                 kin_stream stream) {
+    kin::Geo g;
+    kin_status st = check_pages(desc, pages, &g);
+    if (st != KIN_OK) return st;
+    if (k > kin::kStepIdxCap)
+        return fail(KIN_ERR_UNSUPPORTED, "k = %d: paged steps keep at most %d blocks", k,
+                    kin::kStepIdxCap);
+    return decode_step(g, q, K, V, S, scores, k, idx, out, ws, ws_bytes, stream);
 }
 
 size_t kin_sparse_ws_bytes(const kin_desc *desc, int32_t k) {

@@ -14,11 +14,17 @@ constexpr int kMaxGqa = 16;    // query heads of one group fit one 16-row MFMA t
 constexpr int kMaxBlocks = 16384;
 constexpr int kChunkBf16 = 32;  // tokens per wave iteration, bf16 attention
 constexpr int kChunkF32 = 64;   // tokens per wave iteration, fp32 attention
+constexpr int kStepIdxCap = 2048;  // kept blocks the select+attend kernels hold in LDS
 
 // Geometry shared by the launchers (all derived from a validated desc).
 struct Geo {
     int batch, hkv, gqa, hq, t_cap, ctx_len, block, dtype;
     int nb, nb_cap, pairs;
+    // variable lengths / paged caches (null: every sequence holds ctx_len
+    // tokens in a contiguous cache); ctx_len and nb are then upper bounds
+    const int32_t *ctx_lens = nullptr;
+    const int32_t *pages = nullptr;
+    int page_shift = 0, max_pages = 0, num_pages = 0;
 };
 
 // Split-KV plan of one attention call.
@@ -34,6 +40,10 @@ AttnPlan plan_attention(const Geo &g, int k, bool dense, int num_cu);
 
 hipError_t launch_block_summary(const Geo &g, const void *K, void *S, int j0, int j1,
                                 hipStream_t s);
+// the same for variable lengths / paged caches (bf16): blocks of [t_begin,
+// t_end) inside each sequence
+hipError_t launch_block_summary_paged(const Geo &g, const void *K, void *S, int t_begin,
+                                      int t_end, hipStream_t s);
 hipError_t launch_block_score(const Geo &g, const void *q, const void *S, double *scores,
                               int num_cu, hipStream_t s);
 // decode step, first half: newest-block summary update + all block scores

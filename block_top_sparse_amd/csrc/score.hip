@@ -40,14 +40,16 @@ namespace kin {
 constexpr int kTileThreads = 512;
 
 template <bool UPDATE>
-__global__ __launch_bounds__(kTileThreads) void k_score_tiles(AttnArgs a, void *S,
+__global__ __launch_bounds__(kTileThreads) void k_score_tiles(AttnArgs a0, void *S,
                                                              double *scores, int nb_cap,
                                                              int tile_rows) {
     constexpr int NW = kTileThreads / 64;
     __shared__ NewestLds<NW> nl;
     const int pair = blockIdx.y;
+    const AttnArgs a = for_pair(a0, pair);  // this sequence's own length
     const int nb = a.nb;
     const int j_beg = blockIdx.x * tile_rows;
+    if (j_beg >= nb) return;  // a shorter sequence: nothing left for this tile
     const int j_end = min(nb, j_beg + tile_rows);
     double *sp = scores + (size_t)pair * nb_cap;
     auto emit = [&](int j, double v) { sp[j] = v; };
@@ -70,7 +72,14 @@ static hipError_t launch_tiles(const Geo &g, bool update, const void *q, const v
     a.t_cap = g.t_cap;
     a.ctx_len = g.ctx_len;
     a.block = g.block;
+    a.block_shift = __builtin_ctz((unsigned)g.block);
     a.nb = g.nb;
+    a.k = 1;  // unused here (for_pair's chunk count)
+    a.ctx_lens = g.ctx_lens;
+    a.pages = g.pages;
+    a.page_shift = g.page_shift;
+    a.max_pages = g.max_pages;
+    a.num_pages = g.num_pages;
     constexpr int kRows = (kTileThreads / 64) * kScoreBatch;  // one round of the 8 waves
     const int cu = num_cu > 0 ? num_cu : 256;
     const int tiles = g.pairs >= cu ? 1 : (cu + g.pairs - 1) / g.pairs;

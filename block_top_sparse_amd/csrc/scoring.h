@@ -18,6 +18,7 @@
 // the scoring calls (score.hip).
 #pragma once
 
+#include "attn_impl.h"
 #include "score_impl.h"
 
 namespace kin {
@@ -78,7 +79,8 @@ __device__ __forceinline__ void score_batch(const double (&qs)[8], const u32x4 (
     }
 }
 
-// Blocks [j_beg, j_end) of pair `pair` (bf16 cache).  NEWEST: the range ends
+// Blocks [j_beg, j_end) of pair `pair` (bf16 cache; `a` already holds the
+// pair's own length, for_pair).  NEWEST: the range ends
 // with the newest block nb - 1 (ctx_len - 1 lies in it): its summary is
 // rebuilt (fp64 sum in ascending token order, fp64 mean, fp32 then bf16
 // rounding), written to S and scored by wave 0 after its batches, with the
@@ -110,7 +112,7 @@ __device__ void score_blocks(const AttnArgs &a, void *Sv, int nb_cap, int pair, 
     const int j_safe = j_lim > j_beg ? j_lim - 1 : j_beg - 1;
     const uint16_t *rows = j_safe >= 0 ? S + row0 * kHeadDim
                                        : static_cast<const uint16_t *>(a.K) +
-                                             (size_t)pair * a.t_cap * kHeadDim;
+                                             token_row(a, pair, 0) * kHeadDim;
     const int j_max = j_safe >= 0 ? j_safe : 0;
 
     // Issue order: query rows, this wave's share of the newest block's K
@@ -124,9 +126,9 @@ __device__ void score_blocks(const AttnArgs &a, void *Sv, int nb_cap, int pair, 
     const int tw = wave * kKPre;
     uint32_t kw[kKPre];
     if (NEWEST) {
+        // the block lies inside one page: its rows are consecutive
         const uint32_t *kn = static_cast<const uint32_t *>(a.K) +
-                             ((size_t)pair * a.t_cap + (size_t)jn * a.block) * (kHeadDim / 2) +
-                             lane;
+                             token_row(a, pair, jn * a.block) * (kHeadDim / 2) + lane;
 #pragma unroll
         for (int t = 0; t < kKPre; ++t) kw[t] = kn[(size_t)min(tw + t, tn - 1) * (kHeadDim / 2)];
     }

@@ -43,11 +43,18 @@ struct StepExtra {
     int nb_cap;
 };
 
-template <int KPT>
-__global__ __launch_bounds__(kStepThreads) void k_decode_step(AttnArgs a, StepExtra x) {
+// PAGED: K/V through the page table (the kept blocks' first rows are looked
+// up once, after the selection); the sequences may differ in length either
+// way (for_pair).
+template <int KPT, bool PAGED>
+__global__ __launch_bounds__(kStepThreads) void k_decode_step(AttnArgs a0, StepExtra x) {
     constexpr int NW = kStepThreads / 64;
     __shared__ int32_t sel[kStepIdxCap];
-    __shared__ SelectLds<KPT, kStepThreads> sl;
+    __shared__ union {
+        SelectLds<KPT, kStepThreads> sl;
+        int64_t selrow[kStepIdxCap];  // PAGED, after the selection
+    } su;
+    SelectLds<KPT, kStepThreads> &sl = su.sl;
     __shared__ union {
         double sc[kStepMaxBlocks];
         MergeLds<NW> m;
@@ -56,6 +63,7 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step(AttnArgs a, StepEx
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int pair = blockIdx.x;
+    const AttnArgs a = for_pair(a0, pair);
     const size_t row0 = (size_t)pair * x.nb_cap;
     const int nb = a.nb;
 
@@ -80,7 +88,21 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step(AttnArgs a, StepEx
     for (int i = tid; i < a.k; i += kStepThreads) x.idx[(size_t)pair * a.k + i] = sel[i];
 
     // 4. attention over the kept blocks, then the merge of the 8 waves
-    attend_bf16<false, NW>(a, sel, pair, 0, a.n_chunks, wave, NW, wave, u.m);
+    if constexpr (PAGED) {
+        // first row of every kept block (a block lies inside one page); the
+        // select's LDS is dead now
+        for (int i = tid; i < a.k; i += kStepThreads) {
+            const int id = sel[i];
+            su.selrow[i] = id >= 0 && id < nb ? token_row(a, pair, id * a.block) : -1;
+        }
+        __syncthreads();
+        const PagedRuns runs{sel, su.selrow, token_row(a, pair, 0), a.k, nb, a.block,
+                             a.block_shift};
+        attend_bf16<PagedRuns, NW>(a, runs, pair, 0, a.n_chunks, wave, NW, wave, u.m);
+    } else {
+        attend_bf16<ListRuns, NW>(a, list_runs(a, pair, sel), pair, 0, a.n_chunks, wave, NW,
+                                  wave, u.m);
+    }
     __syncthreads();
     merge_waves_and_store<KIN_BF16, NW>(a, u.m, pair, 0);
 }
@@ -103,13 +125,17 @@ hipError_t launch_decode_step(const Geo &g, const void *q, const void *K, const 
     fill_args(a, g, p, q, K, V, nullptr, k, out, nullptr);
     StepExtra x{S, scores, idx, g.nb_cap};
     dim3 grid(g.pairs);
+#define KIN_STEP(KPT)                                                                          \
+    (g.pages ? k_decode_step<KPT, true><<<grid, kStepThreads, 0, s>>>(a, x)                      \
+             : k_decode_step<KPT, false><<<grid, kStepThreads, 0, s>>>(a, x))
     switch (select_kpt(g.nb, kStepThreads)) {
-    case 1: k_decode_step<1><<<grid, kStepThreads, 0, s>>>(a, x); break;
-    case 2: k_decode_step<2><<<grid, kStepThreads, 0, s>>>(a, x); break;
-    case 4: k_decode_step<4><<<grid, kStepThreads, 0, s>>>(a, x); break;
-    case 8: k_decode_step<8><<<grid, kStepThreads, 0, s>>>(a, x); break;
-    default: k_decode_step<16><<<grid, kStepThreads, 0, s>>>(a, x); break;
+    case 1: KIN_STEP(1); break;
+    case 2: KIN_STEP(2); break;
+    case 4: KIN_STEP(4); break;
+    case 8: KIN_STEP(8); break;
+    default: KIN_STEP(16); break;
     }
+#undef KIN_STEP
     return hipGetLastError();
 }
 

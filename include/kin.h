@@ -172,6 +172,52 @@ KIN_API kin_status kin_sparse_decode_step(const kin_desc *desc, const void *q, c
                                   int32_t *idx, void *out, void *ws, size_t ws_bytes,
                                   kin_stream stream);
 
+/* ---- Variable lengths and paged caches ---------------------------------
+ * The serving layout of the latency runs on the rebuttal page "Kinetics:
+ * Rethinking Test-Time Scaling Law" (W2 & Q2: Real-world latency
+ * benchmarks: sequences of about 32K tokens that differ by a few thousand,
+ * a paged KV cache): every sequence has its own length and K/V live in
+ * fixed-size pages of a shared pool.  bf16 only.
+ *
+ * kin_pages (all device pointers; the struct itself is host memory):
+ *   ctx_lens    [batch] int32 tokens of each sequence, or NULL: every
+ *               sequence holds desc->ctx_len tokens.  desc->ctx_len is then
+ *               an upper bound; entries are clamped to [1, desc->ctx_len].
+ *   page_table  [batch][max_pages] int32: page p of sequence b holds its
+ *               tokens [p * page_size, (p + 1) * page_size); or NULL: K and
+ *               V are the contiguous [batch][hkv][t_cap][head_dim] caches.
+ *               Entries outside [0, num_pages) are clamped into the pool.
+ *   page_size   tokens per page: a power of two, >= 16, a multiple of block
+ *               (so a KV block never straddles two pages).
+ *   max_pages   columns of page_table; desc->t_cap = max_pages * page_size.
+ *   num_pages   pages in the pools.
+ * Paged K and V pools: [num_pages][hkv][page_size][head_dim].  The summaries
+ * S stay contiguous, [batch][hkv][nb_cap][head_dim], nb_cap from t_cap.
+ *
+ * kin_paged_summary_update: as kin_block_summary_update, over the blocks of
+ * [t_begin, t_end) inside each sequence's own length.
+ * kin_paged_decode_step: as kin_sparse_decode_step, each sequence with its
+ * own length (its newest block is the one holding its last token); k <=
+ * 2048; workspace kin_sparse_ws_bytes(desc, k).  scores entries past a
+ * sequence's own block count are unspecified.  Errors: as the contiguous
+ * calls, plus KIN_ERR_UNSUPPORTED for fp32 or k > 2048 and KIN_ERR_SHAPE for
+ * a page geometry that breaks the rules above. */
+typedef struct kin_pages {
+    const int32_t *ctx_lens;
+    const int32_t *page_table;
+    int32_t page_size;
+    int32_t max_pages;
+    int32_t num_pages;
+} kin_pages;
+
+KIN_API kin_status kin_paged_summary_update(const kin_desc *desc, const kin_pages *pages,
+                                            const void *K, void *S, int32_t t_begin,
+                                            int32_t t_end, kin_stream stream);
+KIN_API kin_status kin_paged_decode_step(const kin_desc *desc, const kin_pages *pages,
+                                         const void *q, const void *K, const void *V, void *S,
+                                         double *scores, int32_t k, int32_t *idx, void *out,
+                                         void *ws, size_t ws_bytes, kin_stream stream);
+
 /* Workspace sizes in bytes (0 when none is needed); -1 cast to size_t on
  * a bad descriptor.  kin_sparse_ws_bytes covers both kin_sparse_decode_attn
  * and kin_sparse_decode_step (also with scores == NULL).  Sizes depend on the current device's

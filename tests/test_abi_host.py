@@ -29,7 +29,7 @@ def header_entry_points():
 
 def test_every_declared_entry_point_is_exported():
     declared = header_entry_points()
-    assert len(declared) == 13, declared
+    assert len(declared) == 15, declared
     lib = ctypes.CDLL(kb.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
@@ -96,6 +96,29 @@ def test_bad_ranges_and_k_are_rejected():
                 FAKE, FAKE, None, 0, None) == -2
     big = _desc(t_cap=16 * 20000, ctx_len=16 * 20000)
     assert _raw("kin_block_topk", ctypes.byref(big), FAKE, 4, FAKE, None) == -5
+
+
+def test_paged_calls_validate_on_the_host():
+    """kin_pages rules (include/kin.h): bf16 only, page_size a power of two
+    >= 16 and a multiple of block, t_cap = max_pages * page_size, k <= 2048."""
+    bf = _desc(dtype=1)  # t_cap 256, block 16
+    ok = kb.kin_pages(None, FAKE, 64, 4, 8)
+    step = lambda d, p, k=4: _raw("kin_paged_decode_step", ctypes.byref(d), p, FAKE, FAKE,  # noqa
+                                  FAKE, FAKE, FAKE, k, FAKE, FAKE, None, 0, None)
+    assert step(bf, None) == -1
+    assert step(_desc(dtype=0), ctypes.byref(ok)) == -5          # fp32
+    for bad in (kb.kin_pages(None, FAKE, 48, 4, 8),              # not a power of two
+                kb.kin_pages(None, FAKE, 8, 32, 8),              # below 16
+                kb.kin_pages(None, FAKE, 64, 3, 8),              # t_cap != 3 * 64
+                kb.kin_pages(None, FAKE, 64, 4, 0)):             # empty pool
+        assert step(bf, ctypes.byref(bad)) == -2, bad
+    big_block = _desc(dtype=1, block=128)
+    assert step(big_block, ctypes.byref(kb.kin_pages(None, FAKE, 64, 4, 8))) == -2  # 64 % 128
+    assert step(bf, ctypes.byref(kb.kin_pages(MISALIGNED + 2, None, 0, 0, 0))) == -4
+    assert step(bf, ctypes.byref(ok), k=4096) == -5
+    assert step(bf, ctypes.byref(ok), k=0) == -2
+    assert _raw("kin_paged_summary_update", ctypes.byref(bf), ctypes.byref(ok), FAKE, FAKE, 0,
+                300, None) == -2
 
 
 def test_workspace_query_rejects_bad_descriptor():
