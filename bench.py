@@ -141,6 +141,46 @@ def time_steps(fn, layers, steps, warmup, n_events=0):
     return total_ms / steps, stage_ms
 
 
+def layers_for(w, requested=0):
+    """Layers rotated: enough that one round of steps moves >= 1 GiB (so the
+    Infinity Cache holds no previous step's bytes), within 150 GiB of HBM."""
+    n = requested or max(2, min(8, math.ceil(2**30 / w.bytes_sparse_step())))
+    cap = max(1, int(150 * 2**30 // (w.cache_bytes() + w.summary_bytes())))
+    return min(n, cap)
+
+
+def single_kernel(w, num_cu):
+    return w.dtype == "bf16" and w.pairs >= num_cu and w.nb <= 8192 and w.topk <= 2048
+
+
+def run_sweep(args):
+    """The budget/length grid: per point, kin_sparse_decode_step timed back to
+    back over rotated layers, as for the headline workload."""
+    pts = workloads.sweep()
+    if args.sweep == "big":
+        pts = [w for w in pts if w.bytes_sparse_step() >= 256 * 2**20]
+    if args.sweep_batch:
+        pts = [w for w in pts if w.batch == args.sweep_batch]
+    num_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    for w in pts:
+        n_layers = layers_for(w, args.layers)
+        layers = make_layers(w, n_layers, with_dense=False)
+        est_us = w.bytes_sparse_step() / 5e12 * 1e6
+        steps = max(10, min(args.steps, int(2e5 / est_us)))
+        ms, _ = time_steps(lambda i, b, e: sparse_step(w, i, b, None), layers, steps,
+                           max(3, steps // 5))
+        gbs = w.bytes_sparse_step() / (ms * 1e-3) / 1e9
+        print(json.dumps({"workload": w.name, "batch": w.batch, "ctx_len": w.ctx_len,
+                          "block": w.block, "topk_blocks": w.topk, "pairs": w.pairs,
+                          "step_bytes": w.bytes_sparse_step(), "steps": steps,
+                          "layers_rotated": n_layers, "ms_per_step": round(ms, 5),
+                          "queries_per_s": round(w.batch / (ms * 1e-3), 1),
+                          "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                          "kernels": "one" if single_kernel(w, num_cu) else "two"}), flush=True)
+        del layers
+        torch.cuda.empty_cache()
+
+
 def cpu_baseline(w, layer, max_seqs):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     newest-block summary update + scores + selection + attention for the
@@ -180,6 +220,10 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--cpu-seqs", type=int, default=32)
+    ap.add_argument("--sweep", choices=["big", "all"], default=None,
+                    help="time the budget/length grid instead (big: the points of at least "
+                         "256 MiB per step), one JSON line per point")
+    ap.add_argument("--sweep-batch", type=int, default=0, help="only grid points of this batch")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -188,11 +232,12 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    w = workloads.by_name(args.workload)
     torch.cuda.set_device(0)
-    n_layers = args.layers or max(2, min(8, math.ceil(2**30 / w.bytes_sparse_step())))
-    cap_layers = max(1, int(150 * 2**30 // (w.cache_bytes() + w.summary_bytes())))
-    n_layers = min(n_layers, cap_layers)
+    if args.sweep:
+        run_sweep(args)
+        return
+    w = workloads.by_name(args.workload)
+    n_layers = layers_for(w, args.layers)
     log(f"workload {w.name}: {n_layers} layers rotated, step bytes "
         f"{w.bytes_sparse_step() / 2**20:.1f} MiB")
     layers = make_layers(w, n_layers, with_dense=not args.no_dense)
@@ -208,7 +253,7 @@ def main():
     step_bytes = w.bytes_sparse_step()
     gbs = step_bytes / (ms * 1e-3) / 1e9
     num_cu = torch.cuda.get_device_properties(0).multi_processor_count
-    single = w.dtype == "bf16" and w.pairs >= num_cu and w.nb <= 8192 and w.topk <= 2048
+    single = single_kernel(w, num_cu)
     kern = "k_decode_step" if single else "k_block_score + k_select_attend (two launches)"
     kbytes, kus = step_bytes, ms * 1000
     achieved = kbytes / (kus * 1e-6) / 1e9
