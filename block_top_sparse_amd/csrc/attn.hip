@@ -136,7 +136,9 @@ __global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a0,
     stores_complete();
     __shared__ uint32_t last;
     __syncthreads();
-    if (threadIdx.x == 0) last = arrive_count(ctrl + pair, epoch) == (uint32_t)a.nsplit;
+    if (threadIdx.x == 0)
+        last = (epoch ? arrive_count(ctrl + pair, epoch) : arrive_add(ctrl + pair)) ==
+               (uint32_t)a.nsplit;
     __syncthreads();
     if (last) combine_pair<DT, kStepThreads>(a, pair);
 }
@@ -274,6 +276,12 @@ static void launch_sa(const Geo &g, const AttnArgs &a, dim3 grid, const double *
 #undef KIN_SA
 }
 
+// one arrival word per pair after the split partials (combined in-kernel)
+uint64_t *step_ctrl(const Geo &g, const AttnPlan &p, void *ws) {
+    if (!p.fused || p.nsplit <= 1) return nullptr;
+    return reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + align256(ws_for(g, p.nsplit)));
+}
+
 hipError_t launch_select_attend(const Geo &g, const AttnPlan &p, const void *q, const void *K,
                                 const void *V, const double *scores, int k, int32_t *idx,
                                 void *out, void *ws, uint32_t epoch, hipStream_t s) {
@@ -284,10 +292,7 @@ hipError_t launch_select_attend(const Geo &g, const AttnPlan &p, const void *q, 
     }
     AttnArgs a;
     fill_args(a, g, p, q, K, V, nullptr, k, out, ws);
-    // one arrival word per pair after the split partials (combined in-kernel)
-    uint64_t *ctrl = p.nsplit > 1 ? reinterpret_cast<uint64_t *>(
-                                        static_cast<char *>(ws) + align256(ws_for(g, p.nsplit)))
-                                  : nullptr;
+    uint64_t *ctrl = step_ctrl(g, p, ws);
     dim3 grid(p.nsplit, g.pairs);
     if (g.dtype == KIN_BF16)
         launch_sa<KIN_BF16>(g, a, grid, scores, idx, ctrl, epoch, s);

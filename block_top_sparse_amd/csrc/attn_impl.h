@@ -153,6 +153,13 @@ __device__ inline uint32_t arrive_count(uint64_t *ctr, uint32_t epoch) {
     }
 }
 
+// Count an arrival at *ctr, a word that an earlier kernel on the stream set
+// to zero: one atomic round trip.
+__device__ inline uint32_t arrive_add(uint64_t *ctr) {
+    return (uint32_t)__hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) + 1u;
+}
+
 // Merge the NW waves' (m, l, o) of one workgroup in wave order and write the
 // result (the output when nsplit == 1, else this split's partial; AGENT:
 // the partial with agent-scope stores, for a combine in the same kernel).
@@ -221,26 +228,49 @@ __device__ void merge_waves_and_store(const AttnArgs &a, const MergeLds<NW> &sm,
 }
 
 // LSE combine of the nsplit partials of one pair's query heads, read with
-// agent-scope loads (written by other workgroups of the same kernel):
-// M = max m_s, out = sum 2^(m_s - M) o_s / sum 2^(m_s - M) l_s, splits in
+// agent-scope loads (written by other workgroups of the same kernel), 8
+// splits per group with all of a group's loads issued together (one round
+// trip per group): per group M' = max(M, m_s), the running sums rescaled by
+// 2^(M - M'), then out = sum 2^(m_s - M) o_s / sum 2^(m_s - M) l_s, splits in
 // ascending order.  Every thread of an NT-thread workgroup calls this.
 template <int DT, int NT>
 __device__ void combine_pair(const AttnArgs &a, int pair) {
+    constexpr int kGroup = 8;
     const int b = pair / a.hkv, g = pair % a.hkv;
     const int hq = a.hkv * a.gqa;
     for (int i = threadIdx.x; i < a.gqa * (kHeadDim / 2); i += NT) {
         const int h = i / (kHeadDim / 2), c = 2 * (i % (kHeadDim / 2));
         const size_t row = (size_t)b * hq + (size_t)g * a.gqa + h;
         const float *ml = a.ws_ml + row * a.nsplit * 2;
-        float M = -INFINITY;
-        for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, ld_agent(ml + 2 * s));
-        float L = 0.f, o0 = 0.f, o1 = 0.f;
-        for (int s = 0; s < a.nsplit; ++s) {
-            const float w = (M == -INFINITY) ? 0.f : exp2f(ld_agent(ml + 2 * s) - M);
-            L += w * ld_agent(ml + 2 * s + 1);
-            const float *po = a.ws_o + (row * a.nsplit + s) * kHeadDim + c;
-            o0 += w * ld_agent(po);
-            o1 += w * ld_agent(po + 1);
+        float M = -INFINITY, L = 0.f, o0 = 0.f, o1 = 0.f;
+        for (int s0 = 0; s0 < a.nsplit; s0 += kGroup) {
+            float m[kGroup], l[kGroup], x0[kGroup], x1[kGroup];
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u) {
+                const int s = min(s0 + u, a.nsplit - 1);  // repeats past the end are not used
+                const float *po = a.ws_o + (row * a.nsplit + s) * kHeadDim + c;
+                m[u] = ld_agent(ml + 2 * s);
+                l[u] = ld_agent(ml + 2 * s + 1);
+                x0[u] = ld_agent(po);
+                x1[u] = ld_agent(po + 1);
+            }
+            float Mg = M;
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u)
+                if (s0 + u < a.nsplit) Mg = fmaxf(Mg, m[u]);
+            const float r = (M == -INFINITY) ? 0.f : exp2f(M - Mg);
+            L *= r;
+            o0 *= r;
+            o1 *= r;
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u) {
+                if (s0 + u >= a.nsplit) continue;
+                const float w = (Mg == -INFINITY) ? 0.f : exp2f(m[u] - Mg);
+                L += w * l[u];
+                o0 += w * x0[u];
+                o1 += w * x1[u];
+            }
+            M = Mg;
         }
         const float inv = L > 0.f ? 1.f / L : 0.f;
         if (DT == KIN_BF16) {

@@ -279,9 +279,12 @@ static kin_status decode_step(const kin::Geo &g, const void *q, const void *K, c
     double *sc = scores ? scores
                         : reinterpret_cast<double *>(static_cast<char *>(ws) +
                                                      align256(p.ws_bytes));
-    hipError_t e = kin::launch_update_and_score(g, q, K, S, sc, cu, s);
-    if (e == hipSuccess)
-        e = kin::launch_select_attend(g, p, q, K, V, sc, k, idx, out, ws, next_epoch(), s);
+    // every block kept and no scores wanted: the first kernel only rebuilds
+    // the newest summary row; it also clears the second kernel's arrival words
+    const bool newest_only = !scores && k >= g.nb && g.dtype == KIN_BF16;
+    hipError_t e = kin::launch_update_and_score(g, q, K, S, sc, cu, s, newest_only,
+                                                kin::step_ctrl(g, p, ws));
+    if (e == hipSuccess) e = kin::launch_select_attend(g, p, q, K, V, sc, k, idx, out, ws, 0u, s);
     return launched(e, "kin_sparse_decode_step");
 }
 

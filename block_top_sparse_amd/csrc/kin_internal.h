@@ -47,8 +47,11 @@ hipError_t launch_block_summary_paged(const Geo &g, const void *K, void *S, int 
 hipError_t launch_block_score(const Geo &g, const void *q, const void *S, double *scores,
                               int num_cu, hipStream_t s);
 // decode step, first half: newest-block summary update + all block scores
+// (bf16: newest_only skips the scores, for a step that keeps every block;
+// ctrl_zero: arrival words, one per pair, to clear for the second half)
 hipError_t launch_update_and_score(const Geo &g, const void *q, const void *K, void *S,
-                                   double *scores, int num_cu, hipStream_t s);
+                                   double *scores, int num_cu, hipStream_t s,
+                                   bool newest_only = false, uint64_t *ctrl_zero = nullptr);
 hipError_t launch_block_topk(const Geo &g, const double *scores, int k, int32_t *idx,
                              hipStream_t s);
 hipError_t launch_attention(const Geo &g, const AttnPlan &p, const void *q, const void *K,
@@ -57,13 +60,16 @@ hipError_t launch_attention(const Geo &g, const AttnPlan &p, const void *q, cons
 // decode step, second half: top-k selection + sparse attention, fused per
 // pair when the plan allows it (plan_step); otherwise separate launches
 AttnPlan plan_step(const Geo &g, int k, int num_cu);
-// (epoch: the call's round tag for the in-kernel combine of split partials)
+// (epoch: the call's round tag for the in-kernel combine of split partials;
+// 0: the arrival words at step_ctrl() were cleared by an earlier kernel)
 hipError_t launch_select_attend(const Geo &g, const AttnPlan &p, const void *q, const void *K,
                                 const void *V, const double *scores, int k, int32_t *idx,
                                 void *out, void *ws, uint32_t epoch, hipStream_t s);
 // the whole decode step in one kernel (one workgroup per pair); usable when
 // step_single_kernel() says so (bf16, enough pairs to cover the chip)
 bool step_single_kernel(const Geo &g, int k, int num_cu);
+// the arrival words of a plan's in-kernel combine inside ws (nullptr: none)
+uint64_t *step_ctrl(const Geo &g, const AttnPlan &p, void *ws);
 hipError_t launch_decode_step(const Geo &g, const void *q, const void *K, const void *V, void *S,
                               double *scores, int k, int32_t *idx, void *out, hipStream_t s);
 

@@ -42,13 +42,19 @@ constexpr int kTileThreads = 512;
 template <bool UPDATE>
 __global__ __launch_bounds__(kTileThreads) void k_score_tiles(AttnArgs a0, void *S,
                                                              double *scores, int nb_cap,
-                                                             int tile_rows) {
+                                                             int tile_rows, uint64_t *ctrl_zero,
+                                                             int newest_only) {
     constexpr int NW = kTileThreads / 64;
     __shared__ NewestLds<NW> nl;
     const int pair = blockIdx.y;
+    // the pair's arrival word for the next kernel's in-kernel combine starts
+    // at zero (kernels on one stream run in order)
+    if (ctrl_zero && blockIdx.x == 0 && threadIdx.x == 0) ctrl_zero[pair] = 0ull;
     const AttnArgs a = for_pair(a0, pair);  // this sequence's own length
     const int nb = a.nb;
-    const int j_beg = blockIdx.x * tile_rows;
+    // newest_only: every block is kept and no scores are wanted, so only the
+    // newest block's summary is rebuilt (by tile 0)
+    const int j_beg = newest_only ? (blockIdx.x == 0 ? nb - 1 : nb) : blockIdx.x * tile_rows;
     if (j_beg >= nb) return;  // a shorter sequence: nothing left for this tile
     const int j_end = min(nb, j_beg + tile_rows);
     double *sp = scores + (size_t)pair * nb_cap;
@@ -63,7 +69,8 @@ __global__ __launch_bounds__(kTileThreads) void k_score_tiles(AttnArgs a0, void 
 }
 
 static hipError_t launch_tiles(const Geo &g, bool update, const void *q, const void *K, void *S,
-                               double *scores, int num_cu, hipStream_t s) {
+                               double *scores, int num_cu, hipStream_t s, bool newest_only,
+                               uint64_t *ctrl_zero) {
     AttnArgs a{};
     a.q = q;
     a.K = K;
@@ -85,11 +92,12 @@ static hipError_t launch_tiles(const Geo &g, bool update, const void *q, const v
     const int tiles = g.pairs >= cu ? 1 : (cu + g.pairs - 1) / g.pairs;
     int rows = (g.nb + tiles - 1) / tiles;
     rows = (rows + kRows - 1) / kRows * kRows;
-    const dim3 grid((g.nb + rows - 1) / rows, g.pairs);
+    const dim3 grid(newest_only ? 1 : (g.nb + rows - 1) / rows, g.pairs);
     if (update)
-        k_score_tiles<true><<<grid, kTileThreads, 0, s>>>(a, S, scores, g.nb_cap, rows);
+        k_score_tiles<true><<<grid, kTileThreads, 0, s>>>(a, S, scores, g.nb_cap, rows, ctrl_zero,
+                                                          newest_only ? 1 : 0);
     else
-        k_score_tiles<false><<<grid, kTileThreads, 0, s>>>(a, S, scores, g.nb_cap, rows);
+        k_score_tiles<false><<<grid, kTileThreads, 0, s>>>(a, S, scores, g.nb_cap, rows, nullptr, 0);
     return hipGetLastError();
 }
 
@@ -187,13 +195,16 @@ static hipError_t launch_dt(const Geo &g, const void *q, const void *K, void *S,
 hipError_t launch_block_score(const Geo &g, const void *q, const void *S, double *scores,
                               int num_cu, hipStream_t s) {
     void *Sm = const_cast<void *>(S);  // not written without UPDATE
-    return g.dtype == KIN_BF16 ? launch_tiles(g, false, q, nullptr, Sm, scores, num_cu, s)
+    return g.dtype == KIN_BF16
+               ? launch_tiles(g, false, q, nullptr, Sm, scores, num_cu, s, false, nullptr)
                                : launch_dt<KIN_F32, false>(g, q, nullptr, Sm, scores, s);
 }
 
 hipError_t launch_update_and_score(const Geo &g, const void *q, const void *K, void *S,
-                                   double *scores, int num_cu, hipStream_t s) {
-    return g.dtype == KIN_BF16 ? launch_tiles(g, true, q, K, S, scores, num_cu, s)
+                                   double *scores, int num_cu, hipStream_t s, bool newest_only,
+                                   uint64_t *ctrl_zero) {
+    return g.dtype == KIN_BF16 ? launch_tiles(g, true, q, K, S, scores, num_cu, s, newest_only,
+                                              ctrl_zero)
                                : launch_dt<KIN_F32, true>(g, q, K, S, scores, s);
 }
 

@@ -74,7 +74,10 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step(AttnArgs a0, StepE
     if (tid == 0) nl.ready = 0u;
     __syncthreads();
     double *sc_out = x.scores ? x.scores + row0 : nullptr;
-    score_blocks<NW, true>(a, x.S, x.nb_cap, pair, 0, nb, nl, [&](int j, double v) {
+    // every block kept and no scores wanted: only the newest block's summary
+    // is rebuilt (the range then holds just that block)
+    const int j_beg = (a.k >= nb && !sc_out) ? nb - 1 : 0;
+    score_blocks<NW, true>(a, x.S, x.nb_cap, pair, j_beg, nb, nl, [&](int j, double v) {
         u.sc[j] = v;
         if (sc_out) sc_out[j] = v;  // scores are an optional output
         select_count(sl, v);
