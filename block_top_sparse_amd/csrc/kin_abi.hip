@@ -268,7 +268,7 @@ static kin_status decode_step(const kin::Geo &g, const void *q, const void *K, c
     hipStream_t s = (hipStream_t)stream;
     const int cu = num_cu();
     if (kin::step_single_kernel(g, k, cu))
-        return launched(kin::launch_decode_step(g, q, K, V, S, scores, k, idx, out, s),
+        return launched(kin::launch_decode_step(g, q, K, V, S, scores, k, idx, out, cu, s),
                         "kin_sparse_decode_step");
     const kin::AttnPlan p = kin::plan_step(g, k, cu);
     // two kernels hand the scores over in memory: the caller's buffer, or

@@ -71,7 +71,8 @@ bool step_single_kernel(const Geo &g, int k, int num_cu);
 // the arrival words of a plan's in-kernel combine inside ws (nullptr: none)
 uint64_t *step_ctrl(const Geo &g, const AttnPlan &p, void *ws);
 hipError_t launch_decode_step(const Geo &g, const void *q, const void *K, const void *V, void *S,
-                              double *scores, int k, int32_t *idx, void *out, hipStream_t s);
+                              double *scores, int k, int32_t *idx, void *out, int num_cu,
+                              hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // device helpers (bf16 is carried as its raw 16 bits)

@@ -45,6 +45,7 @@ __global__ __launch_bounds__(kTileThreads) void k_score_tiles(AttnArgs a0, void 
                                                              int tile_rows, uint64_t *ctrl_zero,
                                                              int newest_only) {
     constexpr int NW = kTileThreads / 64;
+    static_assert(NewestLds<NW>::kMaxBlock >= 128, "every block size");
     __shared__ NewestLds<NW> nl;
     const int pair = blockIdx.y;
     // the pair's arrival word for the next kernel's in-kernel combine starts

@@ -30,9 +30,11 @@ constexpr int kScoreBatch = 16;  // blocks per wave per batch
 
 // LDS of the newest-block rebuild: the block's K rows (each wave stages
 // kKPre of them), the count of threads that have staged theirs, the new row.
+// Holds blocks of up to kMaxBlock tokens (8 waves: every block size; the
+// launchers choose fewer waves only for blocks that fit).
 template <int NW>
 struct NewestLds {
-    static_assert(NW * kKPre >= 128, "the largest block must fit");
+    static constexpr int kMaxBlock = NW * kKPre;
     uint32_t k[NW * kKPre][kHeadDim / 2];
     uint32_t row[kHeadDim / 2];
     uint32_t ready;

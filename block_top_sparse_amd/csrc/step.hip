@@ -1,15 +1,16 @@
 // step.hip -- a whole block top-k sparse decode step in ONE kernel, one
-// 512-thread workgroup per (sequence, KV head) pair:
+// workgroup per (sequence, KV head) pair (8 waves, or 4 when two pairs share
+// a CU):
 //
 //   1. wave 0 rebuilds the summary of the newest block (fp64 mean in token
 //      order, rounded to bf16) and writes it to S, while
-//   2. all 8 waves score every other block of the pair against the group's
+//   2. all waves score every other block of the pair against the group's
 //      query sum (fp64, the same per-lane math and butterfly as the
 //      standalone scoring kernel); wave 0 then scores the newest block from
 //      its new row; the scores stay in LDS (and are written out);
 //   3. the workgroup selects the top k blocks from LDS (select.h; the
 //      exponent count tables are filled while the scores are made);
-//   4. the 8 waves attend over the kept blocks' K/V (MFMA, online softmax)
+//   4. the waves attend over the kept blocks' K/V (MFMA, online softmax)
 //      and merge into the output.
 //
 // The steps follow the method of BlockTopKAttention (skill summary
@@ -27,14 +28,23 @@
 // more on this chip than a kernel boundary; so a pair stays in one
 // workgroup.)  With fewer pairs than CUs the two-kernel split path is used.
 //
-// The scoring phase double-buffers its row loads: each wave keeps one
-// 64-block batch (16 KiB) in flight while it folds the previous one.
+// The scoring phase keeps a ring of four 16-row batches (4 KiB each) in
+// flight per wave while it folds the oldest one.
 #include "attn_impl.h"
 #include "scoring.h"
 
 namespace kin {
 
 constexpr int kStepMaxBlocks = 8192;  // fp64 scores of one pair in LDS
+
+// Two shapes of the step workgroup: 8 waves with room for 8192 scores (one
+// workgroup per CU), or 4 waves with room for 2048 scores and at most 256
+// registers per lane, so that two workgroups share a CU and one's
+// selection and merge overlap the other's streaming (batches with at least
+// two pairs per CU).
+constexpr int kStepSmallWaves = 4;
+constexpr int kStepSmallBlocks = 2048;
+constexpr int kStepSmallMaxBlock = NewestLds<kStepSmallWaves>::kMaxBlock;
 
 struct StepExtra {
     void *S;
@@ -45,18 +55,20 @@ struct StepExtra {
 
 // PAGED: K/V through the page table (the kept blocks' first rows are looked
 // up once, after the selection); the sequences may differ in length either
-// way (for_pair).
-template <int KPT, bool PAGED>
-__global__ __launch_bounds__(kStepThreads) void k_decode_step(AttnArgs a0, StepExtra x) {
-    constexpr int NW = kStepThreads / 64;
+// way (for_pair).  NW waves; MAXNB: scores held in LDS.
+template <int KPT, bool PAGED, int NW, int MAXNB>
+__global__ __launch_bounds__(NW * 64, NW == kStepSmallWaves ? 2 : 1) void k_decode_step(
+    AttnArgs a0, StepExtra x) {
+    constexpr int NT = NW * 64;
+    static_assert(NW == kStepSmallWaves || NewestLds<NW>::kMaxBlock >= 128, "every block size");
     __shared__ int32_t sel[kStepIdxCap];
     __shared__ union {
-        SelectLds<KPT, kStepThreads> sl;
+        SelectLds<KPT, NT> sl;
         int64_t selrow[kStepIdxCap];  // PAGED, after the selection
     } su;
-    SelectLds<KPT, kStepThreads> &sl = su.sl;
+    SelectLds<KPT, NT> &sl = su.sl;
     __shared__ union {
-        double sc[kStepMaxBlocks];
+        double sc[MAXNB];
         MergeLds<NW> m;
     } u;
 
@@ -86,15 +98,15 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step(AttnArgs a0, StepE
 
     // 3. selection (reads the scores from LDS; they are dead afterwards, so
     //    the merge area may reuse them)
-    select_topk<KPT, kStepThreads, true>(u.sc, nb, a.k, sel, sl);
+    select_topk<KPT, NT, true>(u.sc, nb, a.k, sel, sl);
     __syncthreads();
-    for (int i = tid; i < a.k; i += kStepThreads) x.idx[(size_t)pair * a.k + i] = sel[i];
+    for (int i = tid; i < a.k; i += NT) x.idx[(size_t)pair * a.k + i] = sel[i];
 
     // 4. attention over the kept blocks, then the merge of the 8 waves
     if constexpr (PAGED) {
         // first row of every kept block (a block lies inside one page); the
         // select's LDS is dead now
-        for (int i = tid; i < a.k; i += kStepThreads) {
+        for (int i = tid; i < a.k; i += NT) {
             const int id = sel[i];
             su.selrow[i] = id >= 0 && id < nb ? token_row(a, pair, id * a.block) : -1;
         }
@@ -110,13 +122,38 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step(AttnArgs a0, StepE
     merge_waves_and_store<KIN_BF16, NW>(a, u.m, pair, 0);
 }
 
+// the 4-wave shape: at least two pairs per CU, and the pair fits its LDS
+static bool step_small(const Geo &g, int cu) {
+    return g.pairs >= 2 * cu && g.nb <= kStepSmallBlocks && g.block <= kStepSmallMaxBlock;
+}
+
 bool step_single_kernel(const Geo &g, int k, int num_cu) {
     const int cu = num_cu > 0 ? num_cu : 256;
     return g.dtype == KIN_BF16 && g.nb <= kStepMaxBlocks && k <= kStepIdxCap && g.pairs >= cu;
 }
 
+template <int NW, int MAXNB>
+static void launch_shape(const Geo &g, const AttnArgs &a, const StepExtra &x, hipStream_t s) {
+    constexpr int NT = NW * 64;
+    const dim3 grid(g.pairs);
+#define KIN_STEP(KPT)                                                                          \
+    (g.pages ? k_decode_step<KPT, true, NW, MAXNB><<<grid, NT, 0, s>>>(a, x)                    \
+             : k_decode_step<KPT, false, NW, MAXNB><<<grid, NT, 0, s>>>(a, x))
+    switch (select_kpt(g.nb, NT)) {
+    case 1: KIN_STEP(1); break;
+    case 2: KIN_STEP(2); break;
+    case 4: KIN_STEP(4); break;
+    case 8: KIN_STEP(8); break;
+    default:
+        if constexpr (MAXNB / NT >= 16) KIN_STEP(16);
+        break;
+    }
+#undef KIN_STEP
+}
+
 hipError_t launch_decode_step(const Geo &g, const void *q, const void *K, const void *V, void *S,
-                              double *scores, int k, int32_t *idx, void *out, hipStream_t s) {
+                              double *scores, int k, int32_t *idx, void *out, int num_cu,
+                              hipStream_t s) {
     AttnPlan p;
     const int keff = k < g.nb ? k : g.nb;
     p.n_tokens = keff * g.block;
@@ -126,19 +163,11 @@ hipError_t launch_decode_step(const Geo &g, const void *q, const void *K, const 
     p.ws_bytes = 0;
     AttnArgs a;
     fill_args(a, g, p, q, K, V, nullptr, k, out, nullptr);
-    StepExtra x{S, scores, idx, g.nb_cap};
-    dim3 grid(g.pairs);
-#define KIN_STEP(KPT)                                                                          \
-    (g.pages ? k_decode_step<KPT, true><<<grid, kStepThreads, 0, s>>>(a, x)                      \
-             : k_decode_step<KPT, false><<<grid, kStepThreads, 0, s>>>(a, x))
-    switch (select_kpt(g.nb, kStepThreads)) {
-    case 1: KIN_STEP(1); break;
-    case 2: KIN_STEP(2); break;
-    case 4: KIN_STEP(4); break;
-    case 8: KIN_STEP(8); break;
-    default: KIN_STEP(16); break;
-    }
-#undef KIN_STEP
+    const StepExtra x{S, scores, idx, g.nb_cap};
+    if (step_small(g, num_cu > 0 ? num_cu : 256))
+        launch_shape<kStepSmallWaves, kStepSmallBlocks>(g, a, x, s);
+    else
+        launch_shape<kStepThreads / 64, kStepMaxBlocks>(g, a, x, s);
     return hipGetLastError();
 }
 

@@ -180,6 +180,7 @@ PAGED = [
     ("few-g16-b128-p128", 2, 2, 16, 128, 128, 3000, 5, "edge"),
     ("many-g4-b16-p256", 40, 8, 4, 16, 256, 4096, 64, "rand"),    # 320 pairs: one kernel
     ("many-g8-b32-p64", 36, 8, 8, 32, 64, 3000, 16, "edge"),       # 288 pairs: one kernel
+    ("many4w-g2-b32-p64", 64, 8, 2, 32, 64, 1500, 16, "edge"),     # 512 pairs: 4-wave step
 ]
 
 

@@ -97,6 +97,11 @@ SINGLE = [
     ("step-g8-b64-kpast", 32, 64, 8, 700, 64, 15, "bf16", 704),      # k > nb
     ("step-g1-b16-manyblk", 256, 1, 1, 60000, 16, 100, "bf16", 60000),  # nb 3750
     ("step-g16-b128-short", 16, 256, 16, 100, 128, 2, "bf16", 128),  # a single partial block
+    # >= 2 pairs per CU, nb <= 2048, block <= 64: the 4-wave step, two per CU
+    ("step4w-g4-b16-ragged", 128, 16, 4, 2000, 16, 20, "bf16", 2048),
+    ("step4w-g8-b64-kpast", 64, 64, 8, 700, 64, 15, "bf16", 704),    # k > nb
+    ("step4w-g5-b32-k1", 130, 20, 4, 1111, 32, 1, "bf16", 1152),
+    ("step4w-g2-b16-nb2048", 512, 2, 1, 32768, 16, 64, "bf16", 32768),
 ]
 
 
