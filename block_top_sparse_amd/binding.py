@@ -84,6 +84,8 @@ def lib():
             "kin_version": (I, []),
             "kin_paged_summary_update": (I, [D, G, P, P, I, I, P]),
             "kin_paged_decode_step": (I, [D, G, P, P, P, P, P, I, P, P, P, Z, P]),
+            "kin_token_decode_step": (I, [D, P, P, P, P, I, P, P, P, Z, P]),
+            "kin_token_ws_bytes": (Z, [D, I]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -97,7 +99,8 @@ def exported_names():
             "kin_sparse_decode_attn", "kin_dense_decode_attn", "kin_sparse_decode_step",
             "kin_decode_update_score", "kin_decode_select_attend",
             "kin_sparse_ws_bytes", "kin_dense_ws_bytes", "kin_status_str", "kin_last_error",
-            "kin_version", "kin_paged_summary_update", "kin_paged_decode_step"]
+            "kin_version", "kin_paged_summary_update", "kin_paged_decode_step",
+            "kin_token_decode_step", "kin_token_ws_bytes"]
 
 
 def _p(t):
@@ -163,6 +166,18 @@ def kin_paged_decode_step(desc, pages, q, K, V, S, scores, k, idx, out, ws=None,
     _check(lib().kin_paged_decode_step(ctypes.byref(desc), ctypes.byref(pages), _p(q), _p(K),
                                        _p(V), _p(S), _p(scores), k, _p(idx), _p(out), _p(ws),
                                        _nbytes(ws), _s(stream)))
+
+
+def kin_token_decode_step(desc, q, K, V, scores, k, idx, out, ws=None, stream=None):
+    _check(lib().kin_token_decode_step(ctypes.byref(desc), _p(q), _p(K), _p(V), _p(scores), k,
+                                       _p(idx), _p(out), _p(ws), _nbytes(ws), _s(stream)))
+
+
+def kin_token_ws_bytes(desc, k) -> int:
+    n = lib().kin_token_ws_bytes(ctypes.byref(desc), k)
+    if n == ctypes.c_size_t(-1).value:
+        raise KinError(-2, lib().kin_last_error().decode())
+    return n
 
 
 def kin_decode_update_score(desc, q, K, S, scores, stream=None):

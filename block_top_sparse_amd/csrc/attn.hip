@@ -179,11 +179,6 @@ __global__ __launch_bounds__(64) void k_combine(const float *__restrict__ ws_o,
 
 static int chunk_tokens(const Geo &g) { return g.dtype == KIN_BF16 ? kChunkBf16 : kChunkF32; }
 
-static size_t ws_for(const Geo &g, int ns) {
-    return ns == 1 ? 0 : (size_t)g.batch * g.hq * ns * (kHeadDim + 2) * sizeof(float);
-}
-
-static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 AttnPlan plan_attention(const Geo &g, int k, bool dense, int num_cu) {
     AttnPlan p;

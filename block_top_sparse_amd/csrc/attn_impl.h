@@ -64,6 +64,7 @@ __device__ __forceinline__ int64_t token_row(const AttnArgs &a, int pair, int t)
 
 // all tokens [0, ctx_len) of one pair, contiguous cache [pair][t_cap]
 struct DenseRuns {
+    static constexpr bool kPerToken = false;
     int64_t row0;  // the pair's first row
     int ctx_len;
     __device__ int64_t run(int p0, bool &valid, int &t0) const {
@@ -76,6 +77,7 @@ struct DenseRuns {
 
 // the kept blocks `sel` (global memory or LDS) of one pair, contiguous cache
 struct ListRuns {
+    static constexpr bool kPerToken = false;
     int64_t row0;
     const int32_t *sel;
     int k, nb, block, block_shift;
@@ -92,6 +94,7 @@ struct ListRuns {
 // the kept blocks of one pair in a paged cache: selrow[slot] is the row of
 // block sel[slot]'s first token (a block lies inside one page), or -1
 struct PagedRuns {
+    static constexpr bool kPerToken = false;
     const int32_t *sel;
     const int64_t *selrow;
     int64_t safe_row;
@@ -105,6 +108,21 @@ struct PagedRuns {
         return valid ? selrow[slot] + off : safe_row;
     }
     __device__ int64_t safe() const { return safe_row; }
+};
+
+// the kept tokens `sel` (one token per list position, token-level
+// selection) of one pair, contiguous cache: every position has its own row
+struct TokenRuns {
+    static constexpr bool kPerToken = true;
+    int64_t row0;
+    const int32_t *sel;
+    int k, ctx_len;
+    __device__ int64_t row_of(int p, bool &valid) const {
+        const int id = p < k ? sel[p] : -1;
+        valid = id >= 0 && id < ctx_len;
+        return valid ? row0 + id : row0;
+    }
+    __device__ int64_t safe() const { return row0; }
 };
 
 // LDS the waves of one workgroup merge through: per wave, per head, the
@@ -313,21 +331,40 @@ __device__ __forceinline__ void load_chunk(const AttnArgs &a, const Runs &runs, 
                                            const uint16_t *V, int c, int j, int g4,
                                            ChunkRegs &cr) {
     cr.ok = 0;
+    if constexpr (Runs::kPerToken) {
+        // K: row j of each 16-token tile; V: rows 4*g4 .. 4*g4+3
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-        bool valid;
-        int t0;
-        const int64_t row0 = runs.run(c * kChunkBf16 + 16 * tau, valid, t0);
-        const int64_t rowk = (valid && t0 + j < a.ctx_len) ? row0 + j : runs.safe();
+        for (int tau = 0; tau < 2; ++tau) {
+            bool valid;
+            const int64_t rowk = runs.row_of(c * kChunkBf16 + 16 * tau + j, valid);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            cr.k[tau][kk] = ld_nt16(K + rowk * kHeadDim + 32 * kk + 8 * g4);
+            for (int kk = 0; kk < 4; ++kk)
+                cr.k[tau][kk] = ld_nt16(K + rowk * kHeadDim + 32 * kk + 8 * g4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int dv = 4 * g4 + r;
-            const bool ok = valid && t0 + dv < a.ctx_len;
-            cr.ok |= (ok ? 1u : 0u) << (4 * tau + r);
-            cr.v[4 * tau + r] = ld_nt16(V + (ok ? row0 + dv : runs.safe()) * kHeadDim + 8 * j);
+            for (int r = 0; r < 4; ++r) {
+                bool ok;
+                const int64_t rowv = runs.row_of(c * kChunkBf16 + 16 * tau + 4 * g4 + r, ok);
+                cr.ok |= (ok ? 1u : 0u) << (4 * tau + r);
+                cr.v[4 * tau + r] = ld_nt16(V + rowv * kHeadDim + 8 * j);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+            bool valid;
+            int t0;
+            const int64_t row0 = runs.run(c * kChunkBf16 + 16 * tau, valid, t0);
+            const int64_t rowk = (valid && t0 + j < a.ctx_len) ? row0 + j : runs.safe();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                cr.k[tau][kk] = ld_nt16(K + rowk * kHeadDim + 32 * kk + 8 * g4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int dv = 4 * g4 + r;
+                const bool ok = valid && t0 + dv < a.ctx_len;
+                cr.ok |= (ok ? 1u : 0u) << (4 * tau + r);
+                cr.v[4 * tau + r] = ld_nt16(V + (ok ? row0 + dv : runs.safe()) * kHeadDim + 8 * j);
+            }
         }
     }
 }
@@ -589,6 +626,13 @@ __device__ void load_q_f32(const AttnArgs &a, int pair, F32Lds<NW> &fl) {
 }
 
 // Kernel arguments from a validated geometry and plan (host side).
+// Bytes of the split partials (o, then m and l) of one attention call.
+inline size_t ws_for(const Geo &g, int ns) {
+    return ns == 1 ? 0 : (size_t)g.batch * g.hq * ns * (kHeadDim + 2) * sizeof(float);
+}
+
+inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
 inline void fill_args(AttnArgs &a, const Geo &g, const AttnPlan &p, const void *q, const void *K,
                       const void *V, const int32_t *idx, int k, void *out, void *ws) {
     a.q = q;

@@ -360,6 +360,54 @@ kin_status kin_paged_decode_step(const kin_desc *desc, const kin_pages *pages, c
     return decode_step(g, q, K, V, S, scores, k, idx, out, ws, ws_bytes, stream);
 }
 
+// Token-level step: the descriptor with block 1 (every token its own block).
+static kin_status check_tok(const kin_desc *desc, int32_t k, kin::Geo *g) {
+    if (!desc) return fail(KIN_ERR_NULL, "desc is NULL");
+    if (desc->block != 1)
+        return fail(KIN_ERR_SHAPE, "block %d: the token-level step takes block = 1", desc->block);
+    kin_desc d = *desc;
+    d.block = 16;  // the other fields are checked as for the block calls
+    kin_status st = check_desc(&d, g);
+    if (st != KIN_OK) return st;
+    if (g->dtype != KIN_BF16) return fail(KIN_ERR_UNSUPPORTED, "token-level step: bf16 only");
+    if (g->ctx_len > kin::kTokMaxLen)
+        return fail(KIN_ERR_UNSUPPORTED, "ctx_len %d: the token-level step takes at most %d",
+                    g->ctx_len, kin::kTokMaxLen);
+    if (k < 1 || k > kin::kTokIdxCap)
+        return fail(k < 1 ? KIN_ERR_SHAPE : KIN_ERR_UNSUPPORTED,
+                    "k = %d: the token-level step keeps 1 .. %d tokens", k, kin::kTokIdxCap);
+    g->block = 1;
+    g->nb = g->ctx_len;
+    g->nb_cap = g->t_cap;
+    return KIN_OK;
+}
+
+kin_status kin_token_decode_step(const kin_desc *desc, const void *q, const void *K,
+                                 const void *V, double *scores, int32_t k, int32_t *idx,
+                                 void *out, void *ws, size_t ws_bytes, kin_stream stream) {
+    kin::Geo g;
+    kin_status st = check_tok(desc, k, &g);
+    if (st != KIN_OK) return st;
+    KIN_REQUIRE_PTR(q);
+    KIN_REQUIRE_PTR(K);
+    KIN_REQUIRE_PTR(V);
+    if (scores && !aligned16(scores)) return fail(KIN_ERR_ALIGN, "scores is not 16-byte aligned");
+    KIN_REQUIRE_PTR(idx);
+    KIN_REQUIRE_PTR(out);
+    const int cu = num_cu();
+    st = check_ws_size(kin::plan_tok(g, k, cu).ws_bytes, ws, ws_bytes);
+    if (st != KIN_OK) return st;
+    return launched(kin::launch_tok_step(g, q, K, V, scores, k, idx, out, ws, cu,
+                                         (hipStream_t)stream),
+                    "kin_token_decode_step");
+}
+
+size_t kin_token_ws_bytes(const kin_desc *desc, int32_t k) {
+    kin::Geo g;
+    if (check_tok(desc, k, &g) != KIN_OK) return (size_t)-1;
+    return kin::plan_tok(g, k, num_cu()).ws_bytes;
+}
+
 size_t kin_sparse_ws_bytes(const kin_desc *desc, int32_t k) {
     kin::Geo g;
     if (check_desc(desc, &g) != KIN_OK) return (size_t)-1;

@@ -15,6 +15,8 @@ constexpr int kMaxBlocks = 16384;
 constexpr int kChunkBf16 = 32;  // tokens per wave iteration, bf16 attention
 constexpr int kChunkF32 = 64;   // tokens per wave iteration, fp32 attention
 constexpr int kStepIdxCap = 2048;  // kept blocks the select+attend kernels hold in LDS
+constexpr int kTokIdxCap = 8192;   // kept tokens of the token-level step (LDS)
+constexpr int kTokMaxLen = 262144;  // tokens of one pair the streaming select takes
 
 // Geometry shared by the launchers (all derived from a validated desc).
 struct Geo {
@@ -70,6 +72,16 @@ hipError_t launch_select_attend(const Geo &g, const AttnPlan &p, const void *q, 
 bool step_single_kernel(const Geo &g, int k, int num_cu);
 // the arrival words of a plan's in-kernel combine inside ws (nullptr: none)
 uint64_t *step_ctrl(const Geo &g, const AttnPlan &p, void *ws);
+// group scores of rows[pair][nb_cap][head_dim] (bf16) for rows j < nb, in
+// tiles over the chip; ctrl_zero: arrival words to clear for a next kernel
+hipError_t launch_score_rows(const Geo &g, const void *q, const void *rows, double *scores,
+                             int num_cu, uint64_t *ctrl_zero, hipStream_t s);
+// token-level decode step (every token its own block; bf16): scores from K,
+// then select + attend; workspace plan_tok(...).ws_bytes
+AttnPlan plan_tok(const Geo &g, int k, int num_cu);
+hipError_t launch_tok_step(const Geo &g, const void *q, const void *K, const void *V,
+                           double *scores, int k, int32_t *idx, void *out, void *ws, int num_cu,
+                           hipStream_t s);
 hipError_t launch_decode_step(const Geo &g, const void *q, const void *K, const void *V, void *S,
                               double *scores, int k, int32_t *idx, void *out, int num_cu,
                               hipStream_t s);

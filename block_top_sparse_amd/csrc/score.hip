@@ -98,7 +98,8 @@ static hipError_t launch_tiles(const Geo &g, bool update, const void *q, const v
         k_score_tiles<true><<<grid, kTileThreads, 0, s>>>(a, S, scores, g.nb_cap, rows, ctrl_zero,
                                                           newest_only ? 1 : 0);
     else
-        k_score_tiles<false><<<grid, kTileThreads, 0, s>>>(a, S, scores, g.nb_cap, rows, nullptr, 0);
+        k_score_tiles<false><<<grid, kTileThreads, 0, s>>>(a, S, scores, g.nb_cap, rows,
+                                                           ctrl_zero, 0);
     return hipGetLastError();
 }
 
@@ -199,6 +200,12 @@ hipError_t launch_block_score(const Geo &g, const void *q, const void *S, double
     return g.dtype == KIN_BF16
                ? launch_tiles(g, false, q, nullptr, Sm, scores, num_cu, s, false, nullptr)
                                : launch_dt<KIN_F32, false>(g, q, nullptr, Sm, scores, s);
+}
+
+hipError_t launch_score_rows(const Geo &g, const void *q, const void *rows, double *scores,
+                             int num_cu, uint64_t *ctrl_zero, hipStream_t s) {
+    return launch_tiles(g, false, q, nullptr, const_cast<void *>(rows), scores, num_cu, s, false,
+                        ctrl_zero);
 }
 
 hipError_t launch_update_and_score(const Geo &g, const void *q, const void *K, void *S,

@@ -218,6 +218,28 @@ KIN_API kin_status kin_paged_decode_step(const kin_desc *desc, const kin_pages *
                                          double *scores, int32_t k, int32_t *idx, void *out,
                                          void *ws, size_t ws_bytes, kin_stream stream);
 
+/* Token-level top-k decode step: every token is its own block (desc->block
+ * must be 1), so the keys are their own representatives and there is no
+ * summary array.  TopK attention over single tokens is the variant the
+ * rebuttal page "Kinetics: Rethinking Test-Time Scaling Law" (Q2) sets
+ * beside Block-TopK; here it is the block method with blocks of one token.
+ * Per (sequence, KV head): score_t = sum over the group's query heads of
+ * q_h . K[t] in fp64 for t < ctx_len; the k tokens with the largest scores
+ * (ties to the lower index) are written to idx[b][hkv][k] ascending, -1 past
+ * min(k, ctx_len); out = softmax(q . k / sqrt(d)) . v over the kept tokens.
+ *   K, V      [batch][hkv][t_cap][head_dim], bf16 (read only).
+ *   scores    NULL, or [batch][hkv][t_cap] fp64: entries t < ctx_len get the
+ *             scores (the others are left alone).
+ *   ws        kin_token_ws_bytes(desc, k) bytes of device scratch (the scores
+ *             live there when scores is NULL).
+ * bf16 only; 1 <= k <= 8192; ctx_len <= 262144.  Errors: KIN_ERR_SHAPE for
+ * block != 1 or k < 1, KIN_ERR_UNSUPPORTED for fp32, k > 8192 or longer
+ * contexts, plus the checks of the other calls.  Two kernels on `stream`. */
+KIN_API kin_status kin_token_decode_step(const kin_desc *desc, const void *q, const void *K,
+                                         const void *V, double *scores, int32_t k, int32_t *idx,
+                                         void *out, void *ws, size_t ws_bytes, kin_stream stream);
+KIN_API size_t kin_token_ws_bytes(const kin_desc *desc, int32_t k);
+
 /* Workspace sizes in bytes (0 when none is needed); -1 cast to size_t on
  * a bad descriptor.  kin_sparse_ws_bytes covers both kin_sparse_decode_attn
  * and kin_sparse_decode_step (also with scores == NULL).  Sizes depend on the current device's

@@ -29,7 +29,7 @@ def header_entry_points():
 
 def test_every_declared_entry_point_is_exported():
     declared = header_entry_points()
-    assert len(declared) == 15, declared
+    assert len(declared) == 17, declared
     lib = ctypes.CDLL(kb.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
@@ -119,6 +119,26 @@ def test_paged_calls_validate_on_the_host():
     assert step(bf, ctypes.byref(ok), k=0) == -2
     assert _raw("kin_paged_summary_update", ctypes.byref(bf), ctypes.byref(ok), FAKE, FAKE, 0,
                 300, None) == -2
+
+
+def test_token_calls_validate_on_the_host():
+    """Token-level step (include/kin.h): block must be 1, bf16 only,
+    1 <= k <= 8192, ctx_len <= 262144."""
+    tok = _desc(block=1)
+    step = lambda d, k=4, q=FAKE: _raw("kin_token_decode_step", ctypes.byref(d), q, FAKE,  # noqa
+                                       FAKE, None, k, FAKE, FAKE, None, 0, None)
+    assert step(_desc(block=16)) == -2
+    assert step(_desc(block=1, dtype=0)) == -5
+    assert step(tok, k=0) == -2
+    assert step(tok, k=8193) == -5
+    assert step(_desc(block=1, t_cap=300000, ctx_len=262145)) == -5
+    assert step(tok, q=None) == -1
+    assert step(tok, q=MISALIGNED) == -4
+    assert step(tok) == -1  # no workspace
+    n = kb.kin_token_ws_bytes(tok, 64)
+    assert n >= 2 * 2 * 256 * 8  # the scores at least
+    with pytest.raises(kb.KinError):
+        kb.kin_token_ws_bytes(_desc(block=2), 64)
 
 
 def test_workspace_query_rejects_bad_descriptor():

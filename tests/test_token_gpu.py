@@ -1,0 +1,110 @@
+"""GPU parity of the token-level step (block = 1) against the oracle.
+
+The oracle runs the same method with blocks of one token: its summaries are
+then the keys themselves, its scores, top-k and attention are the ones the
+block tests use.  Cases cover several rounds of the streaming selection,
+split attention (few pairs) and one workgroup per pair, k = 1, k past the
+context, the largest k, and exact ties (all keys equal: the lowest indices
+are kept).
+"""
+import zlib
+
+import pytest
+import torch
+
+import oracle
+from block_top_sparse_amd import binding as kb
+from block_top_sparse_amd import synth
+from block_top_sparse_amd.workloads import Workload
+
+from parity_util import GAP_MIN, TOL, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kb.lib()
+
+
+def run_token(w, inp, k, scores=True):
+    desc = kb.make_desc(w.batch, w.hkv, w.gqa, w.cap, w.ctx_len, 1, torch.bfloat16)
+    idx = torch.full((w.batch, w.hkv, k), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((w.batch, w.hq, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    sc = torch.full((w.batch, w.hkv, w.cap), float("nan"), dtype=torch.float64,
+                    device="cuda") if scores else None
+    ws = torch.empty(kb.kin_token_ws_bytes(desc, k), dtype=torch.uint8, device="cuda")
+    kb.kin_token_decode_step(desc, inp["q"], inp["K"], inp["V"], sc, k, idx, out, ws)
+    torch.cuda.synchronize()
+    return idx, out, sc
+
+
+def check(w, inp, k, idx, out, sc, seqs, certify=True):
+    L = w.ctx_len
+    worst = 0.0
+    for b in seqs:
+        qb, Kb, Vb = inp["q"][b:b + 1].cpu(), inp["K"][b:b + 1].cpu(), inp["V"][b:b + 1].cpu()
+        S_or, _ = oracle.block_summary(Kb, 1, L)  # block 1: the keys themselves
+        assert torch.equal(S_or[:, :, :L].view(torch.int16), Kb[:, :, :L].view(torch.int16))
+        sc_or = oracle.block_score(qb, S_or, w.gqa, L)
+        if sc is not None:
+            got = sc[b:b + 1, :, :L].cpu()
+            scale = sc_or[:, :, :L].abs().amax(dim=2, keepdim=True).clamp_min(1e-300)
+            assert ((got - sc_or[:, :, :L]).abs() / scale).max() < 1e-13, f"scores, seq {b}"
+        idx_or, gap = oracle.block_topk(sc_or.contiguous(), L, k)
+        if certify:
+            assert (gap > GAP_MIN).all(), f"margin certificate fails at seq {b}"
+        assert torch.equal(idx[b:b + 1].cpu(), idx_or), f"selection differs, seq {b}"
+        o = oracle.decode_attention(qb, Kb, Vb, w.gqa, L, 1, idx=idx_or)
+        og = out[b:b + 1].cpu().double()
+        assert torch.isfinite(og).all(), f"unwritten output, seq {b}"
+        err = (og - o).abs().max().item()
+        assert err <= TOL["bf16"], f"output error {err}, seq {b}"
+        worst = max(worst, err)
+    return worst
+
+
+TOKEN = [
+    # name, batch, hq, hkv, ctx, k, t_cap
+    ("tok-few-g4-ragged", 3, 16, 4, 5000, 100, 5120),      # 12 pairs: split attention
+    ("tok-few-g8-k1", 2, 16, 2, 3000, 1, 3072),
+    ("tok-few-g2-kpast", 2, 8, 4, 300, 400, 320),          # k > ctx: all kept, -1 after
+    ("tok-many-g4-k1024", 64, 16, 4, 20000, 1024, 20480),  # 256 pairs: one workgroup each
+    ("tok-long-g2-k2048", 1, 4, 2, 131072, 2048, 131072),  # 256 rounds of the select
+    ("tok-kmax-g4", 2, 4, 1, 40000, 8192, 40000),          # the largest k
+    ("tok-g16-short", 2, 32, 2, 33, 32, 48),               # one round, ragged
+]
+
+
+@pytest.mark.parametrize("case", TOKEN, ids=[c[0] for c in TOKEN])
+def test_token_step_against_oracle(case):
+    name, b, hq, hkv, L, k, cap = case
+    w = Workload(name, batch=b, hq=hq, hkv=hkv, ctx_len=L, block=1, topk=k, dtype="bf16",
+                 seed=zlib.crc32(name.encode()) % 10000, t_cap=cap)
+    say(f"case {name}: pairs {w.pairs}, ctx {L}, k {k}")
+    inp = synth.make_inputs(w, device="cuda", tail_fill=float("nan"))
+    idx, out, sc = run_token(w, inp, k)
+    seqs = sorted({0, b // 2, b - 1})
+    err = check(w, inp, k, idx, out, sc, seqs)
+    if k > L:
+        assert (idx[:, :, L:] == -1).all()
+    # no scores buffer: the same selection and bits
+    idx2, out2, _ = run_token(w, inp, k, scores=False)
+    assert torch.equal(idx2, idx)
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
+    say(f"  ok, max err {err:.3e}")
+
+
+def test_token_step_exact_ties_keep_lowest_indices():
+    """Every key equal: all scores tie, the k lowest token indices are kept
+    and the output is the mean of their values."""
+    w = Workload("tok-ties", batch=2, hq=8, hkv=2, ctx_len=3000, block=1, topk=300,
+                 dtype="bf16", seed=4242, t_cap=3072)
+    inp = synth.make_inputs(w, device="cuda", tail_fill=float("nan"))
+    inp["K"][:, :, :3000] = inp["K"][:, :, :1].clone()
+    idx, out, sc = run_token(w, inp, 300)
+    want = torch.arange(300, dtype=torch.int32, device="cuda").expand(2, 2, 300)
+    assert torch.equal(idx, want)
+    check(w, inp, 300, idx, out, sc, [0, 1], certify=False)
