@@ -181,6 +181,46 @@ def run_sweep(args):
         torch.cuda.empty_cache()
 
 
+def run_token(args, w):
+    """Token-level top-k (block 1): kin_token_decode_step timed like the
+    block step, over rotated layers; one JSON line."""
+    n_layers = layers_for(w, args.layers)
+    desc = kb.make_desc(w.batch, w.hkv, w.gqa, w.cap, w.ctx_len, 1, torch.bfloat16)
+    nws = kb.kin_token_ws_bytes(desc, w.topk)
+    layers = []
+    for l in range(n_layers):
+        inp = synth.make_inputs(w, device="cuda", seed=w.seed + 7919 * l)
+        bufs = {"idx": torch.empty((w.batch, w.hkv, w.topk), dtype=torch.int32, device="cuda"),
+                "out": torch.empty((w.batch, w.hq, 128), dtype=torch.bfloat16, device="cuda"),
+                "ws": torch.empty(nws, dtype=torch.uint8, device="cuda")}
+        layers.append((inp, bufs))
+        torch.cuda.synchronize()
+        log(f"layer {l}: cache {w.cache_bytes() / 2**30:.2f} GiB ready")
+
+    def step(inp, b, ev):
+        kb.kin_token_decode_step(desc, inp["q"], inp["K"], inp["V"], None, w.topk, b["idx"],
+                                 b["out"], b["ws"])
+
+    ms, _ = time_steps(step, layers, args.steps, args.warmup)
+    step_bytes = w.bytes_sparse_step()
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    res = {"metric": METRIC, "value": round(w.batch / (ms * 1e-3), 1), "unit": "queries/s/layer",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": w.dtype, "data": "synthetic",
+           "config": dict(w.describe(), layers_rotated=n_layers,
+                          step_outputs="out, idx (fp64 scores not written)"),
+           "step_bytes": step_bytes, "hbm_gbs": round(gbs, 1),
+           "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+           "roofline": {"bound": "hbm", "kernel": "k_score_tiles + k_tok_select_attend (two "
+                        "launches)", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                        "bytes_per_launch": step_bytes, "avg_us": round(ms * 1000, 2)}}
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, layers[0], args.cpu_seqs)
+    print(json.dumps(res), flush=True)
+
+
 def cpu_baseline(w, layer, max_seqs):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     newest-block summary update + scores + selection + attention for the
@@ -237,6 +277,9 @@ def main():
         run_sweep(args)
         return
     w = workloads.by_name(args.workload)
+    if w.block == 1:
+        run_token(args, w)
+        return
     n_layers = layers_for(w, args.layers)
     log(f"workload {w.name}: {n_layers} layers rotated, step bytes "
         f"{w.bytes_sparse_step() / 2**20:.1f} MiB")

@@ -72,10 +72,6 @@ hipError_t launch_select_attend(const Geo &g, const AttnPlan &p, const void *q, 
 bool step_single_kernel(const Geo &g, int k, int num_cu);
 // the arrival words of a plan's in-kernel combine inside ws (nullptr: none)
 uint64_t *step_ctrl(const Geo &g, const AttnPlan &p, void *ws);
-// group scores of rows[pair][nb_cap][head_dim] (bf16) for rows j < nb, in
-// tiles over the chip; ctrl_zero: arrival words to clear for a next kernel
-hipError_t launch_score_rows(const Geo &g, const void *q, const void *rows, double *scores,
-                             int num_cu, uint64_t *ctrl_zero, hipStream_t s);
 // token-level decode step (every token its own block; bf16): scores from K,
 // then select + attend; workspace plan_tok(...).ws_bytes
 AttnPlan plan_tok(const Geo &g, int k, int num_cu);

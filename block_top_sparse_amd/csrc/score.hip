@@ -202,12 +202,6 @@ hipError_t launch_block_score(const Geo &g, const void *q, const void *S, double
                                : launch_dt<KIN_F32, false>(g, q, nullptr, Sm, scores, s);
 }
 
-hipError_t launch_score_rows(const Geo &g, const void *q, const void *rows, double *scores,
-                             int num_cu, uint64_t *ctrl_zero, hipStream_t s) {
-    return launch_tiles(g, false, q, nullptr, const_cast<void *>(rows), scores, num_cu, s, false,
-                        ctrl_zero);
-}
-
 hipError_t launch_update_and_score(const Geo &g, const void *q, const void *K, void *S,
                                    double *scores, int num_cu, hipStream_t s, bool newest_only,
                                    uint64_t *ctrl_zero) {

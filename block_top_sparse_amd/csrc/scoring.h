@@ -63,22 +63,40 @@ __device__ __forceinline__ void add_q_slice(double (&qs)[8], const u32x4 &w, boo
     }
 }
 
-// Score one batch (blocks j0 .. j0+15) and hand every score of a block below
-// j_lim to emit(j, score) (one lane per block; -0.0 becomes +0.0).
-template <class Emit>
-__device__ __forceinline__ void score_batch(const double (&qs)[8], const u32x4 (&w)[4], int j0,
-                                            int j_lim, int lane, int grp, Emit &emit) {
+// Scores of one batch (blocks j0 .. j0+15): lane 4m holds the score of
+// block j0 + batch_offset(4m) (the other lanes hold partial sums).
+__device__ __forceinline__ double score_batch(const double (&qs)[8], const u32x4 (&w)[4],
+                                              int lane) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
     double part[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) part[u] = slice_dot<KIN_BF16>(qs, w[u], zero);
-    double x = fold4(part, lane);
-    const int u = ((lane & 8) ? 2 : 0) + ((lane & 4) ? 1 : 0);
-    const int j = j0 + 4 * u + grp;
-    if ((lane & 3) == 0 && j < j_lim) {
-        if (x == 0.0) x = 0.0;  // one zero: -0.0 becomes +0.0
-        emit(j, x);
+    return fold4(part, lane);
+}
+
+// Offset inside its batch of the block whose score lane 4m holds.
+__device__ __forceinline__ int batch_offset(int lead) {
+    const int u = ((lead & 8) ? 2 : 0) + ((lead & 4) ? 1 : 0);
+    return 4 * u + (lead >> 4);
+}
+
+// Lane 4m + r takes the value lane 4m holds in x[r] (a DPP broadcast inside
+// each quad per slot, then a select): kRing batch scores spread over all 64
+// lanes, so one round of the ring is handed out with one emit per lane.
+static_assert(kRing == 4, "one ring round: one slot per lane of a quad");
+__device__ __forceinline__ double quad_gather(const double (&x)[kRing], int r) {
+    double out = 0.0;
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) {
+        const uint64_t b = (uint64_t)__double_as_longlong(x[s]);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, 0x00, 0xF,
+                                                                  0xF, false);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), 0x00,
+                                                                  0xF, 0xF, false);
+        const double v = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+        out = r == s ? v : out;
     }
+    return out;
 }
 
 // Blocks [j_beg, j_end) of pair `pair` (bf16 cache; `a` already holds the
@@ -163,10 +181,22 @@ __device__ void score_blocks(const AttnArgs &a, void *Sv, int nb_cap, int pair, 
     // every round scores all kRing slots (a batch past the range emits
     // nothing) and refills them unconditionally
     for (int i0 = 0; i0 < n; i0 += kRing) {
+        double x[kRing];
 #pragma unroll
         for (int r = 0; r < kRing; ++r) {
-            score_batch(qs, w[r], jw + (i0 + r) * kStride, j_lim, lane, grp, emit);
+            x[r] = score_batch(qs, w[r], lane);
             load_batch(rows, jw + (i0 + r + kRing) * kStride, j_max, sub, grp, w[r]);
+        }
+        // lane 4m + r: the score of block batch_offset(4m) of slot r's batch
+        // (one emit per lane and round; -0.0 becomes +0.0)
+        {
+            const int r = lane & 3;
+            double v = quad_gather(x, r);
+            const int j = jw + (i0 + r) * kStride + batch_offset(lane & ~3);
+            if (j < j_lim) {
+                if (v == 0.0) v = 0.0;
+                emit(j, v);
+            }
         }
     }
     // The last refills are used after the loop as well (an empty asm reads

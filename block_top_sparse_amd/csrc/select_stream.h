@@ -24,6 +24,23 @@
 namespace kin {
 
 constexpr int kStreamMaxRounds = 512;
+constexpr int kStreamBatch = 16;  // rounds whose loads are issued together
+
+// The keys of rounds r0 .. r0 + kStreamBatch - 1 of this thread (slots past
+// n re-read key 0; callers ignore them): one batch of independent loads, so
+// a pass waits for memory once per batch, not once per round.
+template <int NT>
+__device__ __forceinline__ void load_keys(const double *__restrict__ sc, int n, int r0,
+                                          uint64_t (&key)[kStreamBatch]) {
+    double v[kStreamBatch];
+#pragma unroll
+    for (int u = 0; u < kStreamBatch; ++u) {
+        const int j = (r0 + u) * NT + (int)threadIdx.x;
+        v[u] = sc[j < n ? j : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < kStreamBatch; ++u) key[u] = order_key(v[u]);
+}
 
 template <int NT>
 struct StreamSelectLds {
@@ -69,13 +86,20 @@ __device__ void block_exclusive_scan2(uint32_t *a, uint32_t *b, int n, uint32_t 
     __syncthreads();
 }
 
+// Sign/exponent counts of a run of keys: 256 bins by bits 63..56, then 4096
+// by bits 63..52 (kTableWords words per run).
+constexpr int kTableWords = 256 + 4096;
+
 // Write out[0..k): the min(k, n) largest of sc[0..n) (global memory), their
 // indices ascending, then -1.  Every thread of the NT-thread workgroup calls
 // this; it ends with a barrier after the last write of `out` (LDS or
-// global).  Requires 1 <= k and n <= kStreamMaxRounds * NT.
+// global).  tables: NULL, or ntables count tables (kTableWords each, written
+// by an earlier kernel) that together count every key once; pass 0 is then
+// skipped.  Requires 1 <= k and n <= kStreamMaxRounds * NT.
 template <int NT>
 __device__ void select_stream(const double *__restrict__ sc, int n, int k, int32_t *out,
-                              StreamSelectLds<NT> &lds) {
+                              StreamSelectLds<NT> &lds, const uint32_t *__restrict__ tables,
+                              int ntables) {
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -89,26 +113,40 @@ __device__ void select_stream(const double *__restrict__ sc, int n, int k, int32
         return;
     }
 
-    for (int i = tid; i < 4096; i += NT) lds.fine[i] = 0u;
     for (int i = tid; i < 256; i += NT) lds.hist[0][i] = 0u;
-    __syncthreads();
+    if (tables) {
+        // pass 0 from the count tables: the coarse sums now, the 16 fine
+        // bins under the chosen coarse bin below
+        for (int i = tid; i < 256; i += NT) {
+            uint32_t c = 0;
+            for (int t = 0; t < ntables; ++t) c += tables[(size_t)t * kTableWords + i];
+            lds.coarse[i] = c;
+        }
+        __syncthreads();
+    } else {
+        for (int i = tid; i < 4096; i += NT) lds.fine[i] = 0u;
+        __syncthreads();
 
-    // pass 0: keys per sign/exponent bin
-    for (int r = 0; r < R; ++r) {
-        const int j = r * NT + tid;
-        const bool on = j < n;
-        const uint64_t key = order_key(sc[on ? j : 0]);
-        count_wave_aggregated(lds.fine, (uint32_t)(key >> 52), on);
-    }
-    __syncthreads();
-    for (int i = tid; i < 256; i += NT) {
-        const uint32_t *f = lds.fine + 16 * i;
-        uint32_t c = 0;
+        // pass 0: keys per sign/exponent bin
+        for (int r0 = 0; r0 < R; r0 += kStreamBatch) {
+            uint64_t key[kStreamBatch];
+            load_keys<NT>(sc, n, r0, key);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) c += f[r];
-        lds.coarse[i] = c;
+            for (int u = 0; u < kStreamBatch; ++u)
+                if (r0 + u < R)  // uniform over the workgroup
+                    count_wave_aggregated(lds.fine, (uint32_t)(key[u] >> 52),
+                                          (r0 + u) * NT + tid < n);
+        }
+        __syncthreads();
+        for (int i = tid; i < 256; i += NT) {
+            const uint32_t *f = lds.fine + 16 * i;
+            uint32_t c = 0;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) c += f[r];
+            lds.coarse[i] = c;
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
     uint32_t krem = (uint32_t)keff;
     uint64_t prefix, pmask = 0xFFFull << 52;
@@ -120,8 +158,19 @@ __device__ void select_stream(const double *__restrict__ sc, int n, int k, int32
         const BinHit h1 = find_bin(c, krem, 255u, lane);
         krem -= h1.above;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            c[r] = lane < 4 ? lds.fine[16 * h1.digit + 15 - 4 * lane - r] : 0u;
+        for (int r = 0; r < 4; ++r) {
+            const int f = 16 * h1.digit + 15 - 4 * lane - r;
+            uint32_t v = 0;
+            if (lane < 4) {
+                if (tables) {
+                    for (int t = 0; t < ntables; ++t)
+                        v += tables[(size_t)t * kTableWords + 256 + f];
+                } else {
+                    v = lds.fine[f];
+                }
+            }
+            c[r] = v;
+        }
         const BinHit h2 = find_bin(c, krem, 16u * h1.digit + 15u, lane);
         krem -= h2.above;
         prefix = (uint64_t)h2.digit << 52;
@@ -135,11 +184,13 @@ __device__ void select_stream(const double *__restrict__ sc, int n, int k, int32
         uint32_t *h = lds.hist[buf];
         const int nbuf = buf == 2 ? 0 : buf + 1;
         const uint32_t dmask = (1u << width) - 1u;
-#pragma unroll 4
-        for (int r = 0; r < R; ++r) {
-            const int j = r * NT + tid;
-            const uint64_t key = order_key(sc[j < n ? j : 0]);
-            if (j < n && (key & pmask) == prefix) atomicAdd(&h[(uint32_t)(key >> lo) & dmask], 1u);
+        for (int r0 = 0; r0 < R; r0 += kStreamBatch) {
+            uint64_t key[kStreamBatch];
+            load_keys<NT>(sc, n, r0, key);
+#pragma unroll
+            for (int u = 0; u < kStreamBatch; ++u)
+                if ((r0 + u) * NT + tid < n && (key[u] & pmask) == prefix)
+                    atomicAdd(&h[(uint32_t)(key[u] >> lo) & dmask], 1u);
         }
         for (int i = tid; i < 256; i += NT) lds.hist[nbuf][i] = 0u;
         __syncthreads();
@@ -166,28 +217,40 @@ __device__ void select_stream(const double *__restrict__ sc, int n, int k, int32
 
     // compaction: above = kept for sure; tie = equal to the exact k-th key
     // (only when not resolved), the first krem of them in index order kept
-    for (int r = 0; r < R; ++r) {
-        const int j = r * NT + tid;
-        const uint64_t key = order_key(sc[j < n ? j : 0]);
-        const bool above = j < n && (resolved ? key >= prefix : key > prefix);
-        const bool tie = j < n && !resolved && key == prefix;
-        const uint64_t ma = __ballot(above), mt = __ballot(tie);
-        if (lane == 0) {
-            lds.cnt[r * NW + wave] = (uint32_t)__popcll(ma);
-            lds.cnt_tie[r * NW + wave] = (uint32_t)__popcll(mt);
+    for (int r0 = 0; r0 < R; r0 += kStreamBatch) {
+        uint64_t key[kStreamBatch];
+        load_keys<NT>(sc, n, r0, key);
+#pragma unroll
+        for (int u = 0; u < kStreamBatch; ++u) {
+            const int r = r0 + u;
+            if (r >= R) break;  // uniform
+            const bool on = r * NT + tid < n;
+            const bool above = on && (resolved ? key[u] >= prefix : key[u] > prefix);
+            const bool tie = on && !resolved && key[u] == prefix;
+            const uint64_t ma = __ballot(above), mt = __ballot(tie);
+            if (lane == 0) {
+                lds.cnt[r * NW + wave] = (uint32_t)__popcll(ma);
+                lds.cnt_tie[r * NW + wave] = (uint32_t)__popcll(mt);
+            }
         }
     }
     __syncthreads();
     block_exclusive_scan2<NT>(lds.cnt, lds.cnt_tie, R * NW, lds.wsum);
-    for (int r = 0; r < R; ++r) {
-        const int j = r * NT + tid;
-        const uint64_t key = order_key(sc[j < n ? j : 0]);
-        const bool above = j < n && (resolved ? key >= prefix : key > prefix);
-        const bool tie = j < n && !resolved && key == prefix;
-        const uint64_t ma = __ballot(above), mt = __ballot(tie);
-        const uint32_t gt_before = lds.cnt[r * NW + wave] + rank_below(ma);
-        const uint32_t tie_before = lds.cnt_tie[r * NW + wave] + rank_below(mt);
-        if (above || (tie && tie_before < krem)) out[gt_before + min(tie_before, krem)] = j;
+    for (int r0 = 0; r0 < R; r0 += kStreamBatch) {
+        uint64_t key[kStreamBatch];
+        load_keys<NT>(sc, n, r0, key);
+#pragma unroll
+        for (int u = 0; u < kStreamBatch; ++u) {
+            const int r = r0 + u;
+            if (r >= R) break;  // uniform
+            const int j = r * NT + tid;
+            const bool above = j < n && (resolved ? key[u] >= prefix : key[u] > prefix);
+            const bool tie = j < n && !resolved && key[u] == prefix;
+            const uint64_t ma = __ballot(above), mt = __ballot(tie);
+            const uint32_t gt_before = lds.cnt[r * NW + wave] + rank_below(ma);
+            const uint32_t tie_before = lds.cnt_tie[r * NW + wave] + rank_below(mt);
+            if (above || (tie && tie_before < krem)) out[gt_before + min(tie_before, krem)] = j;
+        }
     }
     __syncthreads();
 }

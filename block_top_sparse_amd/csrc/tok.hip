@@ -2,10 +2,12 @@
 // (block size 1), so the keys are their own representatives and no summary
 // array exists.  Per (sequence, KV head) pair:
 //
-//   kernel 1 (score.hip, k_score_tiles): the group score of every key,
-//            fp64, streamed straight from K in tiles spread over the chip;
-//   kernel 2 (here): the k best tokens (select_stream.h, the scores read
-//            from memory), then attention over those tokens' K/V (MFMA,
+//   kernel 1 (k_tok_score): the group score of every key, fp64, streamed
+//            straight from K in tiles spread over the chip (the scoring loop
+//            of scoring.h), and each tile's sign/exponent counts;
+//   kernel 2 (k_tok_select_attend): the k best tokens (select_stream.h, the
+//            scores read from memory, its first pass taken from the counts),
+//            then attention over those tokens' K/V (MFMA,
 //            online softmax), split over several workgroups when there are
 //            fewer pairs than CUs, the splits combined in-kernel.
 //
@@ -15,9 +17,45 @@
 // = sum over the group's query heads of q_h . k_t, top k tokens with ties
 // to the lower index, softmax(q . k / sqrt(d)) over the kept tokens.
 #include "attn_impl.h"
+#include "scoring.h"
 #include "select_stream.h"
 
 namespace kin {
+
+constexpr int kTokScoreThreads = 512;
+
+// Kernel 1: the group score of every key of one tile of a pair's tokens,
+// written out, and the tile's sign/exponent counts (the selection's first
+// pass) written to `tables` ([pair][tile][kTableWords]).  Also clears the
+// pair's arrival word for kernel 2's combine.
+__global__ __launch_bounds__(kTokScoreThreads) void k_tok_score(AttnArgs a, double *scores,
+                                                               int tile_rows, uint32_t *tables,
+                                                               uint64_t *ctrl_zero) {
+    constexpr int NW = kTokScoreThreads / 64;
+    __shared__ NewestLds<NW> nl;  // not used: no summary to rebuild
+    __shared__ uint32_t coarse[256];
+    __shared__ uint32_t fine[4096];
+    const int pair = blockIdx.y, tile = blockIdx.x;
+    if (ctrl_zero && tile == 0 && threadIdx.x == 0) ctrl_zero[pair] = 0ull;
+    for (int i = threadIdx.x; i < 4096; i += kTokScoreThreads) fine[i] = 0u;
+    for (int i = threadIdx.x; i < 256; i += kTokScoreThreads) coarse[i] = 0u;
+    __syncthreads();
+    const int j_beg = tile * tile_rows;
+    const int j_end = min(a.ctx_len, j_beg + tile_rows);
+    double *sp = scores + (size_t)pair * a.t_cap;
+    if (j_beg < j_end)
+        score_blocks<NW, false>(a, const_cast<void *>(a.K), a.t_cap, pair, j_beg, j_end, nl,
+                                [&](int j, double v) {
+            sp[j] = v;
+            const uint64_t key = order_key(v);
+            atomicAdd(&coarse[key >> 56], 1u);
+            atomicAdd(&fine[key >> 52], 1u);
+        });
+    __syncthreads();
+    uint32_t *t = tables + ((size_t)pair * gridDim.x + tile) * kTableWords;
+    for (int i = threadIdx.x; i < 256; i += kTokScoreThreads) t[i] = coarse[i];
+    for (int i = threadIdx.x; i < 4096; i += kTokScoreThreads) t[256 + i] = fine[i];
+}
 
 template <int NT>
 struct TokLds {
@@ -31,14 +69,17 @@ struct TokLds {
 __global__ __launch_bounds__(kStepThreads) void k_tok_select_attend(AttnArgs a,
                                                                    const double *__restrict__ scores,
                                                                    int n_cap, int32_t *idx_out,
-                                                                   uint64_t *ctrl) {
+                                                                   uint64_t *ctrl,
+                                                                   const uint32_t *tables,
+                                                                   int ntables) {
     constexpr int NW = kStepThreads / 64;
     __shared__ TokLds<kStepThreads> lds;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int split = blockIdx.x, pair = blockIdx.y;
 
     // every split of a pair repeats the selection (it ends with a barrier)
-    select_stream<kStepThreads>(scores + (size_t)pair * n_cap, a.ctx_len, a.k, lds.sel, lds.u.s);
+    select_stream<kStepThreads>(scores + (size_t)pair * n_cap, a.ctx_len, a.k, lds.sel, lds.u.s,
+                                tables + (size_t)pair * ntables * kTableWords, ntables);
     if (split == 0)
         for (int i = threadIdx.x; i < a.k; i += kStepThreads)
             idx_out[(size_t)pair * a.k + i] = lds.sel[i];
@@ -73,6 +114,31 @@ static Geo tok_geo(const Geo &g) {
     return t;
 }
 
+// Score tiles per pair: about one workgroup per CU, rows a multiple of one
+// round of the 8 waves.
+static void tok_tiles(const Geo &g, int num_cu, int &tiles, int &rows) {
+    constexpr int kRound = (kTokScoreThreads / 64) * kScoreBatch;
+    const int cu = num_cu > 0 ? num_cu : 256;
+    tiles = g.pairs >= cu ? 1 : (cu + g.pairs - 1) / g.pairs;
+    rows = (g.ctx_len + tiles - 1) / tiles;
+    rows = (rows + kRound - 1) / kRound * kRound;
+    tiles = (g.ctx_len + rows - 1) / rows;
+}
+
+// Workspace of the token step: split partials, arrival words, scores, count
+// tables (in that order, each 256-byte aligned).
+struct TokWs {
+    size_t ctrl, scores, tables, total;
+};
+static TokWs tok_ws(const Geo &g, int nsplit, int tiles) {
+    TokWs w;
+    w.ctrl = align256(ws_for(g, nsplit));
+    w.scores = align256(w.ctrl + (nsplit > 1 ? (size_t)g.pairs * sizeof(uint64_t) : 0));
+    w.tables = align256(w.scores + (size_t)g.pairs * g.t_cap * sizeof(double));
+    w.total = w.tables + (size_t)g.pairs * tiles * kTableWords * sizeof(uint32_t);
+    return w;
+}
+
 AttnPlan plan_tok(const Geo &g, int k, int num_cu) {
     const int keff = k < g.ctx_len ? k : g.ctx_len;
     AttnPlan p;
@@ -86,9 +152,9 @@ AttnPlan plan_tok(const Geo &g, int k, int num_cu) {
     if (ns < 1) ns = 1;
     p.nsplit = ns;
     p.fused = 1;
-    // split partials, one arrival word per pair, then the scores
-    const size_t part = ns == 1 ? 0 : align256(ws_for(g, ns)) + (size_t)g.pairs * sizeof(uint64_t);
-    p.ws_bytes = align256(part) + (size_t)g.pairs * g.t_cap * sizeof(double);
+    int tiles, rows;
+    tok_tiles(g, num_cu, tiles, rows);
+    p.ws_bytes = tok_ws(g, ns, tiles).total;
     return p;
 }
 
@@ -97,18 +163,21 @@ hipError_t launch_tok_step(const Geo &g0, const void *q, const void *K, const vo
                            hipStream_t s) {
     const Geo g = tok_geo(g0);
     const AttnPlan p = plan_tok(g, k, num_cu);
+    int tiles, rows;
+    tok_tiles(g, num_cu, tiles, rows);
+    const TokWs wl = tok_ws(g, p.nsplit, tiles);
     char *w = static_cast<char *>(ws);
-    uint64_t *ctrl = p.nsplit > 1 ? reinterpret_cast<uint64_t *>(w + align256(ws_for(g, p.nsplit)))
-                                  : nullptr;
-    const size_t part = p.nsplit == 1 ? 0 : align256(ws_for(g, p.nsplit)) + g.pairs * sizeof(uint64_t);
-    double *sc = scores ? scores : reinterpret_cast<double *>(w + align256(part));
-    // kernel 1: the scores straight from K (the keys are the summaries)
-    hipError_t e = launch_score_rows(g, q, K, sc, num_cu, ctrl, s);
-    if (e != hipSuccess) return e;
+    uint64_t *ctrl = p.nsplit > 1 ? reinterpret_cast<uint64_t *>(w + wl.ctrl) : nullptr;
+    double *sc = scores ? scores : reinterpret_cast<double *>(w + wl.scores);
+    uint32_t *tables = reinterpret_cast<uint32_t *>(w + wl.tables);
     AttnArgs a;
     fill_args(a, g, p, q, K, V, nullptr, k, out, ws);
+    // kernel 1: the scores straight from K (the keys are the summaries)
+    k_tok_score<<<dim3(tiles, g.pairs), kTokScoreThreads, 0, s>>>(a, sc, rows, tables, ctrl);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     const dim3 grid(p.nsplit, g.pairs);
-    k_tok_select_attend<<<grid, kStepThreads, 0, s>>>(a, sc, g.t_cap, idx, ctrl);
+    k_tok_select_attend<<<grid, kStepThreads, 0, s>>>(a, sc, g.t_cap, idx, ctrl, tables, tiles);
     return hipGetLastError();
 }
 

@@ -59,6 +59,11 @@ class Workload:
 
     # ---- algorithmic bytes (what the method has to move, per call) ----
     def bytes_summary_scan(self) -> int:
+        """The summary rows a step must read to rank the blocks: none when
+        every block is kept (the scores cannot change the selection, and the
+        step without a scores output skips them)."""
+        if self.k_eff >= self.nb:
+            return 0
         return self.pairs * self.nb * self.head_dim * self.esize
 
     def kept_tokens(self) -> int:
@@ -77,7 +82,10 @@ class Workload:
 
     def bytes_update(self) -> int:
         """Newest-block summary update of one decode step: read the newest
-        block's keys (at most one block) and write one summary row."""
+        block's keys (at most one block) and write one summary row.  None
+        with blocks of one token (the keys are the summaries)."""
+        if self.block == 1:
+            return 0
         newest = self.ctx_len - (self.nb - 1) * self.block
         return self.pairs * (newest + 1) * self.head_dim * self.esize
 
@@ -116,6 +124,15 @@ QWEN3_32B = Workload("qwen3-32b-b32-ctx64k", batch=32, hq=64, hkv=8, ctx_len=655
 
 MAIN = [TINY, QWEN3_8B, QWEN3_14B, QWEN3_32B]
 
+# Token-level top-k (block 1): the headline decode shape with a budget of
+# 1024 tokens, and a long-context Best-of-8 shape.
+TOKEN = [
+    Workload("tok-qwen3-8b-b32-ctx32k-budget1024", batch=32, hq=32, hkv=8, ctx_len=32768,
+             block=1, topk=1024, dtype="bf16", seed=1102),
+    Workload("tok-qwen3-32b-b8-ctx128k-budget4096", batch=8, hq=64, hkv=8, ctx_len=131072,
+             block=1, topk=4096, dtype="bf16", seed=1104),
+]
+
 SWEEP_BATCH = (8, 32, 128)
 SWEEP_CTX = (8192, 32768, 131072)
 SWEEP_BLOCK = (16, 32, 64)
@@ -147,7 +164,7 @@ def sweep() -> List[Workload]:
 
 
 def by_name(name: str) -> Workload:
-    for w in MAIN + sweep():
+    for w in MAIN + TOKEN + sweep():
         if w.name == name:
             return w
     raise KeyError(name)
