@@ -212,7 +212,7 @@ def run_token(args, w):
                           step_outputs="out, idx (fp64 scores not written)"),
            "step_bytes": step_bytes, "hbm_gbs": round(gbs, 1),
            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-           "roofline": {"bound": "hbm", "kernel": "k_score_tiles + k_tok_select_attend (two "
+           "roofline": {"bound": "hbm", "kernel": "k_tok_score + k_tok_select_attend (two "
                         "launches)", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
                         "bytes_per_launch": step_bytes, "avg_us": round(ms * 1000, 2)}}
