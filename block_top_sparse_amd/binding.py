@@ -45,6 +45,18 @@ class kin_pages(ctypes.Structure):
                 ("num_pages", ctypes.c_int32)]
 
 
+class kin_shared_prompt(ctypes.Structure):
+    """Shared prompts: samples per prompt, prompt tokens, and the prompts'
+    K, V and summaries (device pointers)."""
+    _fields_ = [("n_share", ctypes.c_int32), ("prompt_len", ctypes.c_int32),
+                ("Kp", ctypes.c_void_p), ("Vp", ctypes.c_void_p), ("Sp", ctypes.c_void_p)]
+
+
+def make_share(n_share, prompt_len, Kp, Vp, Sp):
+    """A kin_shared_prompt from torch device tensors."""
+    return kin_shared_prompt(n_share, prompt_len, Kp.data_ptr(), Vp.data_ptr(), Sp.data_ptr())
+
+
 def make_pages(ctx_lens=None, page_table=None, page_size=0, max_pages=0, num_pages=0):
     """A kin_pages from torch int32 device tensors (or None)."""
     ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
@@ -68,6 +80,7 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         D, P, I, Z = ctypes.POINTER(kin_desc), ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         G = ctypes.POINTER(kin_pages)
+        H = ctypes.POINTER(kin_shared_prompt)
         sig = {
             "kin_block_summary_update": (I, [D, P, P, I, I, P]),
             "kin_block_score": (I, [D, P, P, P, P]),
@@ -85,6 +98,7 @@ def lib():
             "kin_paged_summary_update": (I, [D, G, P, P, I, I, P]),
             "kin_paged_decode_step": (I, [D, G, P, P, P, P, P, I, P, P, P, Z, P]),
             "kin_token_decode_step": (I, [D, P, P, P, P, I, P, P, P, Z, P]),
+            "kin_shared_decode_step": (I, [D, H, P, P, P, P, P, I, P, P, P, Z, P]),
             "kin_token_ws_bytes": (Z, [D, I]),
         }
         for name, (res, args) in sig.items():
@@ -100,7 +114,7 @@ def exported_names():
             "kin_decode_update_score", "kin_decode_select_attend",
             "kin_sparse_ws_bytes", "kin_dense_ws_bytes", "kin_status_str", "kin_last_error",
             "kin_version", "kin_paged_summary_update", "kin_paged_decode_step",
-            "kin_token_decode_step", "kin_token_ws_bytes"]
+            "kin_token_decode_step", "kin_token_ws_bytes", "kin_shared_decode_step"]
 
 
 def _p(t):
@@ -166,6 +180,12 @@ def kin_paged_decode_step(desc, pages, q, K, V, S, scores, k, idx, out, ws=None,
     _check(lib().kin_paged_decode_step(ctypes.byref(desc), ctypes.byref(pages), _p(q), _p(K),
                                        _p(V), _p(S), _p(scores), k, _p(idx), _p(out), _p(ws),
                                        _nbytes(ws), _s(stream)))
+
+
+def kin_shared_decode_step(desc, share, q, K, V, S, scores, k, idx, out, ws=None, stream=None):
+    _check(lib().kin_shared_decode_step(ctypes.byref(desc), ctypes.byref(share), _p(q), _p(K),
+                                        _p(V), _p(S), _p(scores), k, _p(idx), _p(out), _p(ws),
+                                        _nbytes(ws), _s(stream)))
 
 
 def kin_token_decode_step(desc, q, K, V, scores, k, idx, out, ws=None, stream=None):

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_f32(AttnArgs a) {
 // (pair, split); every split of a pair repeats the same selection)
 // ---------------------------------------------------------------------------
 
-template <int DT, int KPT, bool PAGED>
+template <int DT, int KPT, int MODE>
 __global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a0,
                                                                 const double *__restrict__ scores,
                                                                 int nb_cap, int32_t *idx_out,
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a0,
     const int cps = (a.n_chunks + a.nsplit - 1) / a.nsplit;
     const int c_beg = split * cps;
     const int c_end = min(a.n_chunks, c_beg + cps);
-    if constexpr (DT == KIN_BF16 && PAGED) {
+    if constexpr (DT == KIN_BF16 && MODE == kPaged) {
         // first row of every kept block (a block lies inside one page)
         __shared__ int64_t selrow[kStepIdxCap];
         for (int i = threadIdx.x; i < a.k; i += kStepThreads) {
@@ -117,6 +117,9 @@ __global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a0,
         const PagedRuns runs{sel, selrow, token_row(a, pair, 0), a.k, a.nb, a.block,
                              a.block_shift};
         attend_bf16<PagedRuns, NW>(a, runs, pair, c_beg, c_end, wave, NW, wave, u.m);
+    } else if constexpr (DT == KIN_BF16 && MODE == kShared) {
+        attend_bf16<SharedRuns, NW>(a, shared_runs(a, pair, sel), pair, c_beg, c_end, wave, NW,
+                                    wave, u.m);
     } else if constexpr (DT == KIN_BF16) {
         attend_bf16<ListRuns, NW>(a, list_runs(a, pair, sel), pair, c_beg, c_end, wave, NW, wave,
                                   u.m);
@@ -255,11 +258,14 @@ hipError_t launch_attention(const Geo &g, const AttnPlan &p, const void *q, cons
 template <int DT>
 static void launch_sa(const Geo &g, const AttnArgs &a, dim3 grid, const double *scores,
                       int32_t *idx, uint64_t *ctrl, uint32_t epoch, hipStream_t s) {
+#define KIN_SA_MODE(KPT, MODE)                                                                 \
+    k_select_attend<DT, KPT, MODE><<<grid, kStepThreads, 0, s>>>(a, scores, g.nb_cap, idx, ctrl, \
+                                                                 epoch)
 #define KIN_SA(KPT)                                                                            \
-    (g.pages ? k_select_attend<DT, KPT, true><<<grid, kStepThreads, 0, s>>>(a, scores, g.nb_cap, \
-                                                                            idx, ctrl, epoch)    \
-             : k_select_attend<DT, KPT, false><<<grid, kStepThreads, 0, s>>>(a, scores, g.nb_cap, \
-                                                                             idx, ctrl, epoch))
+    (DT != KIN_BF16 ? KIN_SA_MODE(KPT, kContig)                                                \
+     : g.pages      ? KIN_SA_MODE(KPT, (DT == KIN_BF16 ? kPaged : kContig))                    \
+     : g.share_n    ? KIN_SA_MODE(KPT, (DT == KIN_BF16 ? kShared : kContig))                   \
+                    : KIN_SA_MODE(KPT, kContig))
     switch (select_kpt(g.nb, kStepThreads)) {
     case 1: KIN_SA(1); break;
     case 2: KIN_SA(2); break;
@@ -269,6 +275,7 @@ static void launch_sa(const Geo &g, const AttnArgs &a, dim3 grid, const double *
     default: KIN_SA(32); break;
     }
 #undef KIN_SA
+#undef KIN_SA_MODE
 }
 
 // one arrival word per pair after the split partials (combined in-kernel)

@@ -29,7 +29,22 @@ struct AttnArgs {
     const int32_t *ctx_lens;  // [batch] tokens per sequence (clamped to [1, ctx_len])
     const int32_t *pages;     // [batch][max_pages] page of the pool per page_size tokens
     int page_shift, max_pages, num_pages;
+    // shared prompts (share_n == 0: none): sequences b = p * share_n ..
+    // p * share_n + share_n - 1 share prompt p, whose first prompt_len
+    // tokens' K/V ([prompt][hkv][prompt_len][d]) and block summaries
+    // ([prompt][hkv][prompt_len / block][d]) are stored once
+    const void *Kp, *Vp, *Sp;
+    int share_n, prompt_len, prompt_blocks;
 };
+
+// Where a pair's K/V live: one contiguous cache, a page pool, or a shared
+// prompt's arrays followed by the pair's own cache.
+enum CacheMode { kContig = 0, kPaged = 1, kShared = 2 };
+
+// The (prompt, KV head) unit whose shared rows `pair` reads.
+__device__ __forceinline__ int prompt_unit(const AttnArgs &a, int pair) {
+    return (pair / a.hkv / a.share_n) * a.hkv + pair % a.hkv;
+}
 
 // This pair's arguments: its own context length, block count and chunk
 // count when the sequences differ in length.
@@ -65,6 +80,7 @@ __device__ __forceinline__ int64_t token_row(const AttnArgs &a, int pair, int t)
 // all tokens [0, ctx_len) of one pair, contiguous cache [pair][t_cap]
 struct DenseRuns {
     static constexpr bool kPerToken = false;
+    static constexpr bool kTwoBases = false;
     int64_t row0;  // the pair's first row
     int ctx_len;
     __device__ int64_t run(int p0, bool &valid, int &t0) const {
@@ -78,6 +94,7 @@ struct DenseRuns {
 // the kept blocks `sel` (global memory or LDS) of one pair, contiguous cache
 struct ListRuns {
     static constexpr bool kPerToken = false;
+    static constexpr bool kTwoBases = false;
     int64_t row0;
     const int32_t *sel;
     int k, nb, block, block_shift;
@@ -95,6 +112,7 @@ struct ListRuns {
 // block sel[slot]'s first token (a block lies inside one page), or -1
 struct PagedRuns {
     static constexpr bool kPerToken = false;
+    static constexpr bool kTwoBases = false;
     const int32_t *sel;
     const int64_t *selrow;
     int64_t safe_row;
@@ -114,6 +132,7 @@ struct PagedRuns {
 // selection) of one pair, contiguous cache: every position has its own row
 struct TokenRuns {
     static constexpr bool kPerToken = true;
+    static constexpr bool kTwoBases = false;
     int64_t row0;
     const int32_t *sel;
     int k, ctx_len;
@@ -124,6 +143,51 @@ struct TokenRuns {
     }
     __device__ int64_t safe() const { return row0; }
 };
+
+// the kept blocks of one pair whose first prompt_blocks blocks live in the
+// prompt's shared arrays (Kp, Vp), the rest in the pair's own contiguous
+// cache: run2() also says which of the two arrays the run is in
+struct SharedRuns {
+    static constexpr bool kPerToken = false;
+    static constexpr bool kTwoBases = true;
+    int64_t row0;   // the pair's own first row (in K, V)
+    int64_t prow0;  // the prompt unit's first row (in Kp, Vp)
+    const uint16_t *Kp, *Vp;
+    const int32_t *sel;
+    int k, nb, block, block_shift, prompt_blocks;
+    __device__ int64_t run2(int p0, bool &valid, int &t0, bool &in_prompt) const {
+        const int slot = p0 >> block_shift;
+        const int id = slot < k ? sel[slot] : -1;
+        valid = id >= 0 && id < nb;
+        t0 = id * block + (p0 & (block - 1));
+        in_prompt = valid && id < prompt_blocks;
+        return (in_prompt ? prow0 : row0) + t0;
+    }
+    // rows that may always be read: the prompt's first row (the pair's own
+    // first rows belong to the prompt and hold nothing)
+    __device__ const uint16_t *safe_k() const { return Kp + prow0 * kHeadDim; }
+    __device__ const uint16_t *safe_v() const { return Vp + prow0 * kHeadDim; }
+};
+
+// Launch order of the shared-prompt step: workgroup x runs on XCD x % 8, so
+// the samples of one (prompt, KV head) unit are given consecutive slots of
+// one XCD; the prompt rows they all read then come from that XCD's L2.
+// Identity when the units do not spread evenly over the 8 XCDs.
+__device__ __forceinline__ int shared_pair(const AttnArgs &a, int x, int pairs) {
+    const int n = a.share_n;
+    const int units = pairs / n;
+    if (units % 8) return x;
+    const int xcd = x & 7, slot = x >> 3;
+    const int u = xcd + 8 * (slot / n), smp = slot % n;
+    return ((u / a.hkv) * n + smp) * a.hkv + u % a.hkv;
+}
+
+__device__ __forceinline__ SharedRuns shared_runs(const AttnArgs &a, int pair,
+                                                  const int32_t *sel) {
+    return SharedRuns{(int64_t)pair * a.t_cap, (int64_t)prompt_unit(a, pair) * a.prompt_len,
+                      static_cast<const uint16_t *>(a.Kp), static_cast<const uint16_t *>(a.Vp),
+                      sel, a.k, a.nb, a.block, a.block_shift, a.prompt_blocks};
+}
 
 // LDS the waves of one workgroup merge through: per wave, per head, the
 // running max, running sum and unnormalised output.
@@ -331,7 +395,29 @@ __device__ __forceinline__ void load_chunk(const AttnArgs &a, const Runs &runs, 
                                            const uint16_t *V, int c, int j, int g4,
                                            ChunkRegs &cr) {
     cr.ok = 0;
-    if constexpr (Runs::kPerToken) {
+    if constexpr (Runs::kTwoBases) {
+        // a run is in the prompt's arrays or in the pair's own cache
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+            bool valid, pr;
+            int t0;
+            const int64_t row0 = runs.run2(c * kChunkBf16 + 16 * tau, valid, t0, pr);
+            const uint16_t *Kb = pr ? runs.Kp : K;
+            const uint16_t *Vb = pr ? runs.Vp : V;
+            const bool okk = valid && t0 + j < a.ctx_len;
+            const uint16_t *kr = okk ? Kb + (row0 + j) * kHeadDim : runs.safe_k();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) cr.k[tau][kk] = ld_nt16(kr + 32 * kk + 8 * g4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int dv = 4 * g4 + r;
+                const bool ok = valid && t0 + dv < a.ctx_len;
+                cr.ok |= (ok ? 1u : 0u) << (4 * tau + r);
+                const uint16_t *vr = ok ? Vb + (row0 + dv) * kHeadDim : runs.safe_v();
+                cr.v[4 * tau + r] = ld_nt16(vr + 8 * j);
+            }
+        }
+    } else if constexpr (Runs::kPerToken) {
         // K: row j of each 16-token tile; V: rows 4*g4 .. 4*g4+3
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
@@ -658,6 +744,12 @@ inline void fill_args(AttnArgs &a, const Geo &g, const AttnPlan &p, const void *
     a.page_shift = g.page_shift;
     a.max_pages = g.max_pages;
     a.num_pages = g.num_pages;
+    a.Kp = g.Kp;
+    a.Vp = g.Vp;
+    a.Sp = g.Sp;
+    a.share_n = g.share_n;
+    a.prompt_len = g.prompt_len;
+    a.prompt_blocks = g.share_n ? g.prompt_len / g.block : 0;
 }
 
 }  // namespace kin

@@ -360,6 +360,38 @@ kin_status kin_paged_decode_step(const kin_desc *desc, const kin_pages *pages, c
     return decode_step(g, q, K, V, S, scores, k, idx, out, ws, ws_bytes, stream);
 }
 
+kin_status kin_shared_decode_step(const kin_desc *desc, const kin_shared_prompt *share,
+                                  const void *q, const void *K, const void *V, void *S,
+                                  double *scores, int32_t k, int32_t *idx, void *out, void *ws,
+                                  size_t ws_bytes, kin_stream stream) {
+    kin::Geo g;
+    kin_status st = check_step(desc, &g);
+    if (st != KIN_OK) return st;
+    if (!share) return fail(KIN_ERR_NULL, "share is NULL");
+    if (g.dtype != KIN_BF16) return fail(KIN_ERR_UNSUPPORTED, "shared prompts: bf16 only");
+    if (share->n_share < 1 || g.batch % share->n_share)
+        return fail(KIN_ERR_SHAPE, "n_share = %d must divide batch %d", share->n_share, g.batch);
+    if (share->prompt_len < g.block || share->prompt_len % g.block ||
+        share->prompt_len >= g.ctx_len)
+        return fail(KIN_ERR_SHAPE,
+                    "prompt_len = %d: need a multiple of block %d, at least one block, below "
+                    "ctx_len %d",
+                    share->prompt_len, g.block, g.ctx_len);
+    if (k > kin::kStepIdxCap)
+        return fail(KIN_ERR_UNSUPPORTED, "k = %d: shared-prompt steps keep at most %d blocks", k,
+                    kin::kStepIdxCap);
+    const void *Kp = share->Kp, *Vp = share->Vp, *Sp = share->Sp;
+    KIN_REQUIRE_PTR(Kp);
+    KIN_REQUIRE_PTR(Vp);
+    KIN_REQUIRE_PTR(Sp);
+    g.share_n = share->n_share;
+    g.prompt_len = share->prompt_len;
+    g.Kp = Kp;
+    g.Vp = Vp;
+    g.Sp = Sp;
+    return decode_step(g, q, K, V, S, scores, k, idx, out, ws, ws_bytes, stream);
+}
+
 // Token-level step: the descriptor with block 1 (every token its own block).
 static kin_status check_tok(const kin_desc *desc, int32_t k, kin::Geo *g) {
     if (!desc) return fail(KIN_ERR_NULL, "desc is NULL");

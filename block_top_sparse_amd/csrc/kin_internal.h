@@ -27,6 +27,9 @@ struct Geo {
     const int32_t *ctx_lens = nullptr;
     const int32_t *pages = nullptr;
     int page_shift = 0, max_pages = 0, num_pages = 0;
+    // shared prompts (share_n == 0: none; see AttnArgs)
+    const void *Kp = nullptr, *Vp = nullptr, *Sp = nullptr;
+    int share_n = 0, prompt_len = 0;
 };
 
 // Split-KV plan of one attention call.

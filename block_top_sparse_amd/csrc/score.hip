@@ -84,6 +84,10 @@ static hipError_t launch_tiles(const Geo &g, bool update, const void *q, const v
     a.nb = g.nb;
     a.k = 1;  // unused here (for_pair's chunk count)
     a.ctx_lens = g.ctx_lens;
+    a.Sp = g.Sp;
+    a.share_n = g.share_n;
+    a.prompt_len = g.prompt_len;
+    a.prompt_blocks = g.share_n ? g.prompt_len / g.block : 0;
     a.pages = g.pages;
     a.page_shift = g.page_shift;
     a.max_pages = g.max_pages;

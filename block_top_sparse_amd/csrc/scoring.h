@@ -40,15 +40,18 @@ struct NewestLds {
     uint32_t ready;
 };
 
-// Load the 16-block batch starting at j0 of the rows at `rows`: 16 lanes
-// per row, 4 rows per load (one 1 KiB request), 4 loads.  Rows past j_max
-// re-read row j_max.
-__device__ __forceinline__ void load_batch(const uint16_t *rows, int j0, int j_max, int sub,
-                                           int grp, u32x4 (&w)[4]) {
+// Load the 16-block batch starting at j0: 16 lanes per row, 4 rows per
+// load (one 1 KiB request), 4 loads.  Row j is at rows_lo + j rows below
+// j_split (a shared prompt's summaries) and at rows + j rows from there on.
+// Rows past j_max re-read row j_max.
+__device__ __forceinline__ void load_batch(const uint16_t *rows_lo, const uint16_t *rows,
+                                           int j_split, int j0, int j_max, int sub, int grp,
+                                           u32x4 (&w)[4]) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int j = min(j0 + 4 * u + grp, j_max);
-        w[u] = ld_nt16(rows + (size_t)j * kHeadDim + 8 * sub);
+        const uint16_t *base = j < j_split ? rows_lo : rows;
+        w[u] = ld_nt16(base + (size_t)j * kHeadDim + 8 * sub);
     }
 }
 
@@ -134,6 +137,12 @@ __device__ void score_blocks(const AttnArgs &a, void *Sv, int nb_cap, int pair, 
                                        : static_cast<const uint16_t *>(a.K) +
                                              token_row(a, pair, 0) * kHeadDim;
     const int j_max = j_safe >= 0 ? j_safe : 0;
+    // a shared prompt's blocks come from its own summary array
+    const int j_split = a.share_n ? a.prompt_blocks : 0;
+    const uint16_t *rows_lo =
+        a.share_n ? static_cast<const uint16_t *>(a.Sp) +
+                        (size_t)prompt_unit(a, pair) * a.prompt_blocks * kHeadDim
+                  : rows;
 
     // Issue order: query rows, this wave's share of the newest block's K
     // rows, batches 0 .. kRing - 1.
@@ -155,7 +164,7 @@ __device__ void score_blocks(const AttnArgs &a, void *Sv, int nb_cap, int pair, 
     u32x4 w[kRing][4];
 #pragma unroll
     for (int r = 0; r < kRing; ++r) {
-        load_batch(rows, jw + r * kStride, j_max, sub, grp, w[r]);
+        load_batch(rows_lo, rows, j_split, jw + r * kStride, j_max, sub, grp, w[r]);
         // keep slot order: the loop's waits assume slot 0 was issued first
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -185,7 +194,8 @@ __device__ void score_blocks(const AttnArgs &a, void *Sv, int nb_cap, int pair, 
 #pragma unroll
         for (int r = 0; r < kRing; ++r) {
             x[r] = score_batch(qs, w[r], lane);
-            load_batch(rows, jw + (i0 + r + kRing) * kStride, j_max, sub, grp, w[r]);
+            load_batch(rows_lo, rows, j_split, jw + (i0 + r + kRing) * kStride, j_max, sub, grp,
+                       w[r]);
         }
         // lane 4m + r: the score of block batch_offset(4m) of slot r's batch
         // (one emit per lane and round; -0.0 becomes +0.0)

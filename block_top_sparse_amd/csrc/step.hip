@@ -53,10 +53,12 @@ struct StepExtra {
     int nb_cap;
 };
 
-// PAGED: K/V through the page table (the kept blocks' first rows are looked
-// up once, after the selection); the sequences may differ in length either
-// way (for_pair).  NW waves; MAXNB: scores held in LDS.
-template <int KPT, bool PAGED, int NW, int MAXNB>
+// MODE kPaged: K/V through the page table (the kept blocks' first rows are
+// looked up once, after the selection); kShared: a shared prompt's blocks
+// from its own arrays (and the samples of a prompt launched next to each
+// other on one XCD); the sequences may differ in length either way
+// (for_pair).  NW waves; MAXNB: scores held in LDS.
+template <int KPT, int MODE, int NW, int MAXNB>
 __global__ __launch_bounds__(NW * 64, NW == kStepSmallWaves ? 2 : 1) void k_decode_step(
     AttnArgs a0, StepExtra x) {
     constexpr int NT = NW * 64;
@@ -74,7 +76,7 @@ __global__ __launch_bounds__(NW * 64, NW == kStepSmallWaves ? 2 : 1) void k_deco
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int pair = blockIdx.x;
+    const int pair = MODE == kShared ? shared_pair(a0, blockIdx.x, gridDim.x) : blockIdx.x;
     const AttnArgs a = for_pair(a0, pair);
     const size_t row0 = (size_t)pair * x.nb_cap;
     const int nb = a.nb;
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(NW * 64, NW == kStepSmallWaves ? 2 : 1) void k_deco
     for (int i = tid; i < a.k; i += NT) x.idx[(size_t)pair * a.k + i] = sel[i];
 
     // 4. attention over the kept blocks, then the merge of the 8 waves
-    if constexpr (PAGED) {
+    if constexpr (MODE == kPaged) {
         // first row of every kept block (a block lies inside one page); the
         // select's LDS is dead now
         for (int i = tid; i < a.k; i += NT) {
@@ -114,6 +116,9 @@ __global__ __launch_bounds__(NW * 64, NW == kStepSmallWaves ? 2 : 1) void k_deco
         const PagedRuns runs{sel, su.selrow, token_row(a, pair, 0), a.k, nb, a.block,
                              a.block_shift};
         attend_bf16<PagedRuns, NW>(a, runs, pair, 0, a.n_chunks, wave, NW, wave, u.m);
+    } else if constexpr (MODE == kShared) {
+        attend_bf16<SharedRuns, NW>(a, shared_runs(a, pair, sel), pair, 0, a.n_chunks, wave, NW,
+                                    wave, u.m);
     } else {
         attend_bf16<ListRuns, NW>(a, list_runs(a, pair, sel), pair, 0, a.n_chunks, wave, NW,
                                   wave, u.m);
@@ -137,8 +142,9 @@ static void launch_shape(const Geo &g, const AttnArgs &a, const StepExtra &x, hi
     constexpr int NT = NW * 64;
     const dim3 grid(g.pairs);
 #define KIN_STEP(KPT)                                                                          \
-    (g.pages ? k_decode_step<KPT, true, NW, MAXNB><<<grid, NT, 0, s>>>(a, x)                    \
-             : k_decode_step<KPT, false, NW, MAXNB><<<grid, NT, 0, s>>>(a, x))
+    (g.pages ? k_decode_step<KPT, kPaged, NW, MAXNB><<<grid, NT, 0, s>>>(a, x)                  \
+     : g.share_n ? k_decode_step<KPT, kShared, NW, MAXNB><<<grid, NT, 0, s>>>(a, x)             \
+                 : k_decode_step<KPT, kContig, NW, MAXNB><<<grid, NT, 0, s>>>(a, x))
     switch (select_kpt(g.nb, NT)) {
     case 1: KIN_STEP(1); break;
     case 2: KIN_STEP(2); break;

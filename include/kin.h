@@ -218,6 +218,40 @@ KIN_API kin_status kin_paged_decode_step(const kin_desc *desc, const kin_pages *
                                          double *scores, int32_t k, int32_t *idx, void *out,
                                          void *ws, size_t ws_bytes, kin_stream stream);
 
+/* Shared-prompt Best-of-N decode step.  The N samples of a prompt share its
+ * first prompt_len tokens (the prompt), whose K/V and block summaries are
+ * stored once per prompt, so their rows are read once for all N samples
+ * (rebuttal page "Kinetics: Rethinking Test-Time Scaling Law", W2 & Q2:
+ * Best-of-N decode batches; the prompt is common to the N samples).
+ * Sequences b = p * n_share .. p * n_share + n_share - 1 share prompt p.
+ *   Kp, Vp  [batch / n_share][hkv][prompt_len][head_dim], bf16: the prompts'
+ *           keys and values (read only);
+ *   Sp      [batch / n_share][hkv][prompt_len / block][head_dim]: the prompts'
+ *           block summaries (kin_block_summary_update on Kp with batch =
+ *           batch / n_share and t_cap = ctx_len = prompt_len builds them);
+ *   K, V, S as for kin_sparse_decode_step; their rows for tokens below
+ *           prompt_len (blocks below prompt_len / block) are never read.
+ * Each sequence's tokens [0, prompt_len) come from its prompt and
+ * [prompt_len, ctx_len) from its own cache; everything else is
+ * kin_sparse_decode_step (the newest block is always the sequence's own).
+ * Workspace kin_sparse_ws_bytes(desc, k).  bf16 only; prompt_len a multiple
+ * of desc->block, at least one block and below desc->ctx_len; n_share
+ * divides batch; k <= 2048.  Errors: as kin_sparse_decode_step, plus
+ * KIN_ERR_SHAPE for a share that breaks these rules and
+ * KIN_ERR_UNSUPPORTED for fp32 or k > 2048. */
+typedef struct kin_shared_prompt {
+    int32_t n_share;
+    int32_t prompt_len;
+    const void *Kp;
+    const void *Vp;
+    const void *Sp;
+} kin_shared_prompt;
+
+KIN_API kin_status kin_shared_decode_step(const kin_desc *desc, const kin_shared_prompt *share,
+                                          const void *q, const void *K, const void *V, void *S,
+                                          double *scores, int32_t k, int32_t *idx, void *out,
+                                          void *ws, size_t ws_bytes, kin_stream stream);
+
 /* Token-level top-k decode step: every token is its own block (desc->block
  * must be 1), so the keys are their own representatives and there is no
  * summary array.  TopK attention over single tokens is the variant the

@@ -29,7 +29,7 @@ def header_entry_points():
 
 def test_every_declared_entry_point_is_exported():
     declared = header_entry_points()
-    assert len(declared) == 17, declared
+    assert len(declared) == 18, declared
     lib = ctypes.CDLL(kb.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
@@ -119,6 +119,26 @@ def test_paged_calls_validate_on_the_host():
     assert step(bf, ctypes.byref(ok), k=0) == -2
     assert _raw("kin_paged_summary_update", ctypes.byref(bf), ctypes.byref(ok), FAKE, FAKE, 0,
                 300, None) == -2
+
+
+def test_shared_prompt_step_validates_on_the_host():
+    """kin_shared_prompt rules (include/kin.h): bf16, n_share divides batch,
+    prompt_len a multiple of block, >= one block, < ctx_len; k <= 2048."""
+    bf = _desc(dtype=1)  # batch 2, ctx 200, block 16
+    ok = kb.kin_shared_prompt(2, 64, FAKE, FAKE, FAKE)
+    step = lambda d, sh, k=4: _raw("kin_shared_decode_step", ctypes.byref(d), sh, FAKE,  # noqa
+                                   FAKE, FAKE, FAKE, None, k, FAKE, FAKE, None, 0, None)
+    assert step(bf, None) == -1
+    assert step(_desc(dtype=0), ctypes.byref(ok)) == -5
+    for bad in (kb.kin_shared_prompt(3, 64, FAKE, FAKE, FAKE),    # 3 does not divide 2
+                kb.kin_shared_prompt(0, 64, FAKE, FAKE, FAKE),
+                kb.kin_shared_prompt(2, 40, FAKE, FAKE, FAKE),    # not a multiple of 16
+                kb.kin_shared_prompt(2, 0, FAKE, FAKE, FAKE),
+                kb.kin_shared_prompt(2, 208, FAKE, FAKE, FAKE)):  # not below ctx_len
+        assert step(bf, ctypes.byref(bad)) == -2
+    assert step(bf, ctypes.byref(ok), k=4096) == -5
+    assert step(bf, ctypes.byref(kb.kin_shared_prompt(2, 64, None, FAKE, FAKE))) == -1
+    assert step(bf, ctypes.byref(kb.kin_shared_prompt(2, 64, FAKE, MISALIGNED, FAKE))) == -4
 
 
 def test_token_calls_validate_on_the_host():
