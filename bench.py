@@ -221,6 +221,64 @@ def run_token(args, w):
     print(json.dumps(res), flush=True)
 
 
+def run_shared(args, w):
+    """Shared-prompt Best-of-N: kin_shared_decode_step timed like the block
+    step over rotated layers (each with its own prompts and samples), and the
+    same tokens laid out as one contiguous cache per sample through
+    kin_sparse_decode_step for comparison; one JSON line."""
+    n_layers = layers_for(w, args.layers)
+    P, n_prompts = w.prompt_len, w.batch // w.share_n
+    wp = workloads.Workload(w.name + "-prompts", batch=n_prompts, hq=w.hq, hkv=w.hkv,
+                            ctx_len=P, block=w.block, topk=1, dtype=w.dtype, seed=w.seed + 1)
+    desc_p = kb.make_desc(n_prompts, w.hkv, w.gqa, P, P, w.block, torch.bfloat16)
+    layers = []
+    for l in range(n_layers):
+        own = synth.make_inputs(w, device="cuda", seed=w.seed + 7919 * l)
+        pr = synth.make_inputs(wp, device="cuda", seed=wp.seed + 7919 * l)
+        grp = torch.arange(w.batch, device="cuda") // w.share_n
+        own["K"][:, :, :P] = pr["K"][grp]  # the contiguous copy holds the prompt too
+        own["V"][:, :, :P] = pr["V"][grp]
+        bufs = LayerBuffers(w)
+        kb.kin_block_summary_update(bufs.desc, own["K"], bufs.S, 0, w.ctx_len)
+        Sp = torch.empty((n_prompts, w.hkv, P // w.block, 128), dtype=torch.bfloat16,
+                         device="cuda")
+        kb.kin_block_summary_update(desc_p, pr["K"], Sp, 0, P)
+        share = kb.make_share(w.share_n, P, pr["K"], pr["V"], Sp)
+        layers.append((own, {"bufs": bufs, "share": share, "keep": (pr, Sp)}))
+        torch.cuda.synchronize()
+        log(f"layer {l}: cache {w.cache_bytes() / 2**30:.2f} GiB ready")
+
+    def shared_step(inp, b, ev):
+        d = b["bufs"]
+        kb.kin_shared_decode_step(d.desc, b["share"], inp["q"], inp["K"], inp["V"], d.S, None,
+                                  d.k, d.idx, d.out, d.ws)
+
+    def plain_step(inp, b, ev):
+        d = b["bufs"]
+        kb.kin_sparse_decode_step(d.desc, inp["q"], inp["K"], inp["V"], d.S, None, d.k, d.idx,
+                                  d.out, d.ws)
+
+    ms, _ = time_steps(shared_step, layers, args.steps, args.warmup)
+    ms_plain, _ = time_steps(plain_step, layers, args.steps, args.warmup)
+    step_bytes = w.bytes_sparse_step()
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    plain_bytes = workloads.Workload(w.name, batch=w.batch, hq=w.hq, hkv=w.hkv, ctx_len=w.ctx_len,
+                                     block=w.block, topk=w.topk, dtype=w.dtype,
+                                     seed=w.seed).bytes_sparse_step()
+    res = {"metric": METRIC, "value": round(w.batch / (ms * 1e-3), 1), "unit": "queries/s/layer",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": w.dtype, "data": "synthetic",
+           "config": dict(w.describe(), share_n=w.share_n, prompt_len=P,
+                          layers_rotated=n_layers),
+           "step_bytes": step_bytes, "hbm_gbs": round(gbs, 1),
+           "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+           "unshared": {"ms_per_step": round(ms_plain, 5), "step_bytes": plain_bytes,
+                        "hbm_gbs": round(plain_bytes / (ms_plain * 1e-3) / 1e9, 1)},
+           "speedup_vs_unshared": round(ms_plain / ms, 3)}
+    print(json.dumps(res), flush=True)
+
+
 def cpu_baseline(w, layer, max_seqs):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     newest-block summary update + scores + selection + attention for the
@@ -279,6 +337,9 @@ def main():
     w = workloads.by_name(args.workload)
     if w.block == 1:
         run_token(args, w)
+        return
+    if w.share_n:
+        run_shared(args, w)
         return
     n_layers = layers_for(w, args.layers)
     log(f"workload {w.name}: {n_layers} layers rotated, step bytes "

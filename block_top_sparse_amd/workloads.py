@@ -28,6 +28,8 @@ class Workload:
     head_dim: int = 128
     heavy_blocks: int = 0  # blocks per pair whose keys are pushed toward q
     t_cap: int = 0         # cache capacity in tokens (0: equal to ctx_len)
+    share_n: int = 0       # samples per shared prompt (0: no shared prompt)
+    prompt_len: int = 0    # tokens of each shared prompt
 
     @property
     def gqa(self) -> int:
@@ -64,6 +66,11 @@ class Workload:
         step without a scores output skips them)."""
         if self.k_eff >= self.nb:
             return 0
+        if self.share_n:
+            # a prompt's block summaries are read once for its n_share samples
+            pb = self.prompt_len // self.block
+            units = self.pairs // self.share_n
+            return (units * pb + self.pairs * (self.nb - pb)) * self.head_dim * self.esize
         return self.pairs * self.nb * self.head_dim * self.esize
 
     def kept_tokens(self) -> int:
@@ -124,6 +131,13 @@ QWEN3_32B = Workload("qwen3-32b-b32-ctx64k", batch=32, hq=64, hkv=8, ctx_len=655
 
 MAIN = [TINY, QWEN3_8B, QWEN3_14B, QWEN3_32B]
 
+# Shared-prompt Best-of-N: 4 prompts x 8 samples on the qwen3-8b layer, a
+# 16K-token prompt common to each prompt's samples, 16K tokens of their own.
+SHARED = [
+    Workload("bon-qwen3-8b-n8-prompt16k-ctx32k", batch=32, hq=32, hkv=8, ctx_len=32768,
+             block=16, topk=64, dtype="bf16", seed=1202, share_n=8, prompt_len=16384),
+]
+
 # Token-level top-k (block 1): the headline decode shape with a budget of
 # 1024 tokens, and a long-context Best-of-8 shape.
 TOKEN = [
@@ -164,7 +178,7 @@ def sweep() -> List[Workload]:
 
 
 def by_name(name: str) -> Workload:
-    for w in MAIN + TOKEN + sweep():
+    for w in MAIN + TOKEN + SHARED + sweep():
         if w.name == name:
             return w
     raise KeyError(name)
