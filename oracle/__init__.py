@@ -44,8 +44,11 @@ def _load():
         lib.kor_block_topk.argtypes = [P, P, P, I, I, I, I, I, I]
         lib.kor_decode_attention.argtypes = [P, P, P, P, I, P, I, I, I, I, I, I, I, I, I]
         lib.kor_round.argtypes = [P, P, ctypes.c_size_t, I]
+        lib.kor_quest_summary.argtypes = [P, P, I, I, I, I, I, I, I, I, I, I]
+        lib.kor_quest_score.argtypes = [P, P, P, I, I, I, I, I, I, I, I]
         for f in ("kor_block_summary", "kor_block_score", "kor_block_topk",
-                  "kor_decode_attention", "kor_round", "kor_version"):
+                  "kor_decode_attention", "kor_round", "kor_version", "kor_quest_summary",
+                  "kor_quest_score"):
             getattr(lib, f).restype = I
         _lib = lib
     return _lib
@@ -105,6 +108,37 @@ def block_score(q, S, gqa, nb, nthreads=None):
     rc = _load().kor_block_score(_ptr(q), _ptr(S), _ptr(scores), _dt(q), b, hkv, gqa, d,
                                  nb_cap, nb, nthreads or default_threads())
     _check(rc, "block_score")
+    return scores
+
+
+def quest_summary(K, block, ctx_len, t_begin=0, t_end=None, Sq=None, nthreads=None):
+    """Quest-style summaries (reading R9 of kin_oracle.c): channel-wise minimum
+    and maximum of the keys of every block meeting [t_begin, t_end) and
+    [0, ctx_len).  Returns Sq [batch][hkv][nb_cap][2][d] in K's dtype (row 0
+    minimum, row 1 maximum); blocks outside the range keep Sq's values
+    (zeros when Sq is None)."""
+    b, hkv, t_cap, d = K.shape
+    nb_cap = nblocks(t_cap, block)
+    if t_end is None:
+        t_end = ctx_len
+    if Sq is None:
+        Sq = torch.zeros((b, hkv, nb_cap, 2, d), dtype=K.dtype)
+    rc = _load().kor_quest_summary(_ptr(K), _ptr(Sq), _dt(K), b, hkv, t_cap, d, ctx_len, block,
+                                   t_begin, t_end, nthreads or default_threads())
+    _check(rc, "quest_summary")
+    return Sq
+
+
+def quest_score(q, Sq, gqa, nb, nthreads=None):
+    """Quest bound of every block (fp64, [batch][hkv][nb_cap]) for j < nb:
+    sum over the group's heads and channels of max(q*min, q*max)."""
+    b, hq, d = q.shape
+    _, hkv, nb_cap, two, _ = Sq.shape
+    assert two == 2 and hq == hkv * gqa and q.dtype == Sq.dtype
+    scores = torch.zeros((b, hkv, nb_cap), dtype=torch.float64)
+    rc = _load().kor_quest_score(_ptr(q), _ptr(Sq), _ptr(scores), _dt(q), b, hkv, gqa, d, nb_cap,
+                                 nb, nthreads or default_threads())
+    _check(rc, "quest_score")
     return scores
 
 

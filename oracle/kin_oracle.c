@@ -266,6 +266,122 @@ int kor_block_score(const void *q, const void *S, double *scores, int dtype, int
 }
 
 /* ------------------------------------------------------------------ */
+/* O1q, O2q: Quest-style representative (reading R9)                    */
+/* ------------------------------------------------------------------ */
+/*
+ * R9 the pages name Quest as a second grouping strategy next to
+ *    Block-TopK (rebuttal, answer Q4 "KV block size and grouping
+ *    strategy", and "W2. Alternative sparse attention variants") without
+ *    defining it.  Read as the published Quest criterion: a block is
+ *    represented by the channel-wise minimum and maximum of its keys, and
+ *    ranked by the largest value q.k can take for any key inside that
+ *    box, sum over channels of max(q_c * min_c, q_c * max_c).  For a GQA
+ *    group, as in R2, the block's score is the SUM over the group's heads
+ *    of each head's bound.  Summaries keep the cache dtype (a minimum or a
+ *    maximum of stored values is itself a stored value: no rounding).
+ *
+ * Layout: Sq [batch][hkv][nb_cap][2][head_dim], row 0 = minimum, row 1 =
+ * maximum.
+ */
+
+typedef struct {
+    const void *K;
+    void *Sq;
+    int dtype, hkv, t_cap, d, ctx_len, block, nb_cap, j0, j1;
+} kor_quest_sum_ctx;
+
+static void kor_quest_sum_pair(const void *vctx, int pair)
+{
+    const kor_quest_sum_ctx *c = (const kor_quest_sum_ctx *)vctx;
+    const size_t kbase = (size_t)pair * (size_t)c->t_cap * (size_t)c->d;
+    const size_t sbase = (size_t)pair * (size_t)c->nb_cap * 2 * (size_t)c->d;
+    for (int j = c->j0; j < c->j1; ++j) {
+        int t0 = j * c->block;
+        int n = c->ctx_len - t0;
+        if (n > c->block)
+            n = c->block;
+        for (int ch = 0; ch < c->d; ++ch) {
+            double lo = kor_get(c->K, c->dtype, kbase + (size_t)t0 * c->d + ch), hi = lo;
+            for (int t = t0 + 1; t < t0 + n; ++t) {
+                double x = kor_get(c->K, c->dtype, kbase + (size_t)t * c->d + ch);
+                if (x < lo)
+                    lo = x;
+                if (x > hi)
+                    hi = x;
+            }
+            kor_put(c->Sq, c->dtype, sbase + ((size_t)j * 2 + 0) * c->d + ch, lo);
+            kor_put(c->Sq, c->dtype, sbase + ((size_t)j * 2 + 1) * c->d + ch, hi);
+        }
+    }
+}
+
+/* Channel-wise minimum and maximum of the keys of every block that
+ * intersects [t_begin, t_end) and [0, ctx_len); other blocks untouched. */
+int kor_quest_summary(const void *K, void *Sq, int dtype, int batch, int hkv, int t_cap,
+                      int head_dim, int ctx_len, int block, int t_begin, int t_end, int nthreads)
+{
+    if (!K || !Sq || batch < 1 || hkv < 1 || head_dim < 1 || block < 1)
+        return -1;
+    if (dtype != KOR_F32 && dtype != KOR_BF16)
+        return -2;
+    if (ctx_len < 1 || ctx_len > t_cap || t_begin < 0 || t_end < t_begin || t_end > t_cap)
+        return -3;
+    if (t_end > ctx_len)
+        t_end = ctx_len;
+    if (t_begin >= t_end)
+        return 0;
+    kor_quest_sum_ctx c = {K, Sq, dtype, hkv, t_cap, head_dim, ctx_len, block,
+                           kor_nblocks(t_cap, block), t_begin / block, (t_end - 1) / block + 1};
+    kor_run_pairs(batch * hkv, nthreads, kor_quest_sum_pair, &c);
+    return 0;
+}
+
+typedef struct {
+    const void *q, *Sq;
+    double *scores;
+    int dtype, hkv, gqa, d, nb_cap, nb;
+} kor_quest_score_ctx;
+
+static void kor_quest_score_pair(const void *vctx, int pair)
+{
+    const kor_quest_score_ctx *c = (const kor_quest_score_ctx *)vctx;
+    const int b = pair / c->hkv, g = pair % c->hkv;
+    const int hq = c->hkv * c->gqa;
+    for (int j = 0; j < c->nb; ++j) {
+        double sigma = 0.0;
+        const size_t lo = ((size_t)pair * c->nb_cap + j) * 2 * c->d, hi = lo + c->d;
+        for (int h = g * c->gqa; h < (g + 1) * c->gqa; ++h) {
+            size_t qo = ((size_t)b * hq + h) * c->d;
+            for (int ch = 0; ch < c->d; ++ch) {
+                double qc = kor_get(c->q, c->dtype, qo + ch);
+                double a = qc * kor_get(c->Sq, c->dtype, lo + ch);
+                double e = qc * kor_get(c->Sq, c->dtype, hi + ch);
+                sigma += a > e ? a : e;
+            }
+        }
+        if (sigma == 0.0)
+            sigma = 0.0;
+        c->scores[(size_t)pair * c->nb_cap + j] = sigma;
+    }
+}
+
+/* scores[b][g][j] = sum over the group's heads h and channels c of
+ * max(q[b][h][c] * min_jc, q[b][h][c] * max_jc), for j < nb. */
+int kor_quest_score(const void *q, const void *Sq, double *scores, int dtype, int batch, int hkv,
+                    int gqa, int head_dim, int nb_cap, int nb, int nthreads)
+{
+    if (!q || !Sq || !scores || batch < 1 || hkv < 1 || gqa < 1 || head_dim < 1)
+        return -1;
+    if (dtype != KOR_F32 && dtype != KOR_BF16)
+        return -2;
+    if (nb < 1 || nb > nb_cap)
+        return -3;
+    kor_quest_score_ctx c = {q, Sq, scores, dtype, hkv, gqa, head_dim, nb_cap, nb};
+    kor_run_pairs(batch * hkv, nthreads, kor_quest_score_pair, &c);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* O3: top-k selection, reading R5                                      */
 /* ------------------------------------------------------------------ */
 

@@ -366,3 +366,65 @@ def test_constructed_examples(name, dtype):
                 cf = _eval_form(forms[h][c], env)
                 assert cf == pytest.approx(case["out"][h][c], abs=1e-10)
                 assert out[0, h, c].item() == pytest.approx(cf, abs=1e-13)
+
+
+# ---------------------------------------------------------------- Quest-style bound
+
+QUEST_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "quest_example.json")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("block,ctx_len", [(16, 256), (16, 250), (32, 97), (4, 3), (1, 40)])
+def test_quest_summary_is_blockwise_min_and_max(dtype, block, ctx_len):
+    g = torch.Generator().manual_seed(block * 1000 + ctx_len)
+    cap = (ctx_len + block - 1) // block * block
+    K = torch.randn((2, 3, cap, 16), generator=g).to(dtype)
+    K[:, :, ctx_len:] = float("nan")  # never read
+    Sq = oracle.quest_summary(K, block, ctx_len)
+    for j in range((ctx_len + block - 1) // block):
+        part = K[:, :, j * block:min((j + 1) * block, ctx_len)].float()
+        assert torch.equal(Sq[:, :, j, 0].float(), part.amin(dim=2))
+        assert torch.equal(Sq[:, :, j, 1].float(), part.amax(dim=2))
+
+
+def test_quest_score_bounds_every_token_of_its_block():
+    # the bound is at least the group score of every key inside the block
+    g = torch.Generator().manual_seed(91)
+    q = torch.randn((2, 8, 32), generator=g)
+    K = torch.randn((2, 2, 96, 32), generator=g)
+    Sq = oracle.quest_summary(K, 16, 96)
+    sc = oracle.quest_score(q, Sq, 4, 6)
+    tok = torch.einsum("bgc,bgtc->bgt", q.double().view(2, 2, 4, 32).sum(dim=2), K.double())
+    for j in range(6):
+        worst = tok[:, :, j * 16:(j + 1) * 16].amax(dim=2)
+        assert (worst <= sc[:, :, j] + 1e-12 * sc.abs().max()).all()
+    # and each head's part is attained by the corner key that picks, per
+    # channel, the minimum or the maximum by the sign of that head's query
+    qd = q.double().view(2, 2, 4, 32)
+    lo, hi = Sq[:, :, :, 0].double(), Sq[:, :, :, 1].double()
+    corner = torch.where(qd[:, :, :, None, :] >= 0, hi[:, :, None], lo[:, :, None])
+    attained = (qd[:, :, :, None, :] * corner).sum(dim=(2, 4))
+    assert torch.allclose(attained, sc[:, :, :6], rtol=1e-13, atol=0)
+
+
+def test_quest_block_of_one_is_the_token_score():
+    # one key per block: the box is that key, the bound is q.k exactly
+    w = Workload("t", batch=1, hq=6, hkv=2, ctx_len=50, block=1, topk=5, dtype="bf16", seed=66)
+    inp = synth.make_inputs(w)
+    Sq = oracle.quest_summary(inp["K"], 1, 50)
+    S, _ = oracle.block_summary(inp["K"], 1, 50)
+    assert torch.equal(oracle.quest_score(inp["q"], Sq, 3, 50), oracle.block_score(inp["q"], S, 3, 50))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_quest_constructed_example(dtype):
+    ex = json.load(open(QUEST_GOLDEN))
+    q = torch.tensor([ex["q"]], dtype=dtype)                 # [1][2][2]
+    K = torch.tensor([[ex["K"]]], dtype=dtype)               # [1][1][6][2]
+    Sq = oracle.quest_summary(K, 2, 6)
+    assert Sq[0, 0].float().tolist() == ex["minmax"]
+    sc = oracle.quest_score(q, Sq, ex["gqa"], 3)
+    assert sc[0, 0].tolist() == ex["scores"]
+    for case in ex["cases"]:
+        idx, _ = oracle.block_topk(sc, 3, case["k"])
+        assert idx[0, 0].tolist() == case["idx"]
