@@ -221,6 +221,47 @@ def run_token(args, w):
     print(json.dumps(res), flush=True)
 
 
+def run_quest(args, w):
+    """Quest-style representative: kin_quest_decode_step timed like the
+    block step over rotated layers; one JSON line."""
+    n_layers = layers_for(w, args.layers)
+    desc = kb.make_desc(w.batch, w.hkv, w.gqa, w.cap, w.ctx_len, w.block, torch.bfloat16)
+    nws = kb.kin_quest_ws_bytes(desc, w.topk)
+    layers = []
+    for l in range(n_layers):
+        inp = synth.make_inputs(w, device="cuda", seed=w.seed + 7919 * l)
+        Sq = torch.empty((w.batch, w.hkv, w.nb_cap, 2, 128), dtype=torch.bfloat16, device="cuda")
+        kb.kin_quest_summary_update(desc, inp["K"], Sq, 0, w.ctx_len)
+        bufs = {"Sq": Sq,
+                "idx": torch.empty((w.batch, w.hkv, w.topk), dtype=torch.int32, device="cuda"),
+                "out": torch.empty((w.batch, w.hq, 128), dtype=torch.bfloat16, device="cuda"),
+                "ws": torch.empty(nws, dtype=torch.uint8, device="cuda")}
+        layers.append((inp, bufs))
+        torch.cuda.synchronize()
+        log(f"layer {l}: cache {w.cache_bytes() / 2**30:.2f} GiB ready")
+
+    def step(inp, b, ev):
+        kb.kin_quest_decode_step(desc, inp["q"], inp["K"], inp["V"], b["Sq"], None, w.topk,
+                                 b["idx"], b["out"], b["ws"])
+
+    ms, _ = time_steps(step, layers, args.steps, args.warmup)
+    step_bytes = w.bytes_sparse_step()
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    res = {"metric": METRIC, "value": round(w.batch / (ms * 1e-3), 1), "unit": "queries/s/layer",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": w.dtype, "data": "synthetic",
+           "config": dict(w.describe(), representative="quest (channel-wise min/max)",
+                          layers_rotated=n_layers),
+           "step_bytes": step_bytes, "hbm_gbs": round(gbs, 1),
+           "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+           "roofline": {"bound": "hbm", "kernel": "k_quest_tiles + k_select_attend (two "
+                        "launches)", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                        "bytes_per_launch": step_bytes, "avg_us": round(ms * 1000, 2)}}
+    print(json.dumps(res), flush=True)
+
+
 def run_shared(args, w):
     """Shared-prompt Best-of-N: kin_shared_decode_step timed like the block
     step over rotated layers (each with its own prompts and samples), and the
@@ -340,6 +381,9 @@ def main():
         return
     if w.share_n:
         run_shared(args, w)
+        return
+    if w.quest:
+        run_quest(args, w)
         return
     n_layers = layers_for(w, args.layers)
     log(f"workload {w.name}: {n_layers} layers rotated, step bytes "

@@ -99,6 +99,9 @@ def lib():
             "kin_paged_decode_step": (I, [D, G, P, P, P, P, P, I, P, P, P, Z, P]),
             "kin_token_decode_step": (I, [D, P, P, P, P, I, P, P, P, Z, P]),
             "kin_shared_decode_step": (I, [D, H, P, P, P, P, P, I, P, P, P, Z, P]),
+            "kin_quest_summary_update": (I, [D, P, P, I, I, P]),
+            "kin_quest_decode_step": (I, [D, P, P, P, P, P, I, P, P, P, Z, P]),
+            "kin_quest_ws_bytes": (Z, [D, I]),
             "kin_token_ws_bytes": (Z, [D, I]),
         }
         for name, (res, args) in sig.items():
@@ -114,7 +117,8 @@ def exported_names():
             "kin_decode_update_score", "kin_decode_select_attend",
             "kin_sparse_ws_bytes", "kin_dense_ws_bytes", "kin_status_str", "kin_last_error",
             "kin_version", "kin_paged_summary_update", "kin_paged_decode_step",
-            "kin_token_decode_step", "kin_token_ws_bytes", "kin_shared_decode_step"]
+            "kin_token_decode_step", "kin_token_ws_bytes", "kin_shared_decode_step",
+            "kin_quest_summary_update", "kin_quest_decode_step", "kin_quest_ws_bytes"]
 
 
 def _p(t):
@@ -186,6 +190,24 @@ def kin_shared_decode_step(desc, share, q, K, V, S, scores, k, idx, out, ws=None
     _check(lib().kin_shared_decode_step(ctypes.byref(desc), ctypes.byref(share), _p(q), _p(K),
                                         _p(V), _p(S), _p(scores), k, _p(idx), _p(out), _p(ws),
                                         _nbytes(ws), _s(stream)))
+
+
+def kin_quest_summary_update(desc, K, Sq, t_begin, t_end, stream=None):
+    _check(lib().kin_quest_summary_update(ctypes.byref(desc), _p(K), _p(Sq), t_begin, t_end,
+                                          _s(stream)))
+
+
+def kin_quest_decode_step(desc, q, K, V, Sq, scores, k, idx, out, ws=None, stream=None):
+    _check(lib().kin_quest_decode_step(ctypes.byref(desc), _p(q), _p(K), _p(V), _p(Sq),
+                                       _p(scores), k, _p(idx), _p(out), _p(ws), _nbytes(ws),
+                                       _s(stream)))
+
+
+def kin_quest_ws_bytes(desc, k) -> int:
+    n = lib().kin_quest_ws_bytes(ctypes.byref(desc), k)
+    if n == ctypes.c_size_t(-1).value:
+        raise KinError(-2, lib().kin_last_error().decode())
+    return n
 
 
 def kin_token_decode_step(desc, q, K, V, scores, k, idx, out, ws=None, stream=None):

@@ -392,6 +392,65 @@ kin_status kin_shared_decode_step(const kin_desc *desc, const kin_shared_prompt 
     return decode_step(g, q, K, V, S, scores, k, idx, out, ws, ws_bytes, stream);
 }
 
+kin_status kin_quest_summary_update(const kin_desc *desc, const void *K, void *Sq,
+                                   int32_t t_begin, int32_t t_end, kin_stream stream) {
+    kin::Geo g;
+    kin_status st = check_desc(desc, &g);
+    if (st != KIN_OK) return st;
+    if (g.dtype != KIN_BF16) return fail(KIN_ERR_UNSUPPORTED, "Quest summaries: bf16 only");
+    KIN_REQUIRE_PTR(K);
+    KIN_REQUIRE_PTR(Sq);
+    if (t_begin < 0 || t_end < t_begin || t_end > g.t_cap)
+        return fail(KIN_ERR_SHAPE, "need 0 <= t_begin (%d) <= t_end (%d) <= t_cap (%d)", t_begin,
+                    t_end, g.t_cap);
+    const int te = t_end < g.ctx_len ? t_end : g.ctx_len;
+    if (t_begin >= te) return ok();
+    return launched(kin::launch_quest_summary(g, K, Sq, t_begin / g.block,
+                                              (te - 1) / g.block + 1, (hipStream_t)stream),
+                    "kin_quest_summary_update");
+}
+
+kin_status kin_quest_decode_step(const kin_desc *desc, const void *q, const void *K,
+                                 const void *V, void *Sq, double *scores, int32_t k, int32_t *idx,
+                                 void *out, void *ws, size_t ws_bytes, kin_stream stream) {
+    kin::Geo g;
+    kin_status st = check_step(desc, &g);
+    if (st != KIN_OK) return st;
+    if (g.dtype != KIN_BF16) return fail(KIN_ERR_UNSUPPORTED, "Quest step: bf16 only");
+    KIN_REQUIRE_PTR(q);
+    KIN_REQUIRE_PTR(K);
+    KIN_REQUIRE_PTR(V);
+    KIN_REQUIRE_PTR(Sq);
+    if (scores && !aligned16(scores)) return fail(KIN_ERR_ALIGN, "scores is not 16-byte aligned");
+    KIN_REQUIRE_PTR(idx);
+    KIN_REQUIRE_PTR(out);
+    if (k < 1) return fail(KIN_ERR_SHAPE, "k = %d: need k >= 1", k);
+    if (k > kin::kStepIdxCap)
+        return fail(KIN_ERR_UNSUPPORTED, "k = %d: the Quest step keeps at most %d blocks", k,
+                    kin::kStepIdxCap);
+    const int cu = num_cu();
+    const kin::AttnPlan p = kin::plan_step(g, k, cu);
+    st = check_ws_size(align256(p.ws_bytes) + (scores ? 0 : step_scores_bytes(g)), ws, ws_bytes);
+    if (st != KIN_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    double *sc = scores ? scores
+                        : reinterpret_cast<double *>(static_cast<char *>(ws) +
+                                                     align256(p.ws_bytes));
+    hipError_t e = kin::launch_quest_score(g, q, K, Sq, sc, cu, kin::step_ctrl(g, p, ws), true, s);
+    if (e == hipSuccess) e = kin::launch_select_attend(g, p, q, K, V, sc, k, idx, out, ws, 0u, s);
+    return launched(e, "kin_quest_decode_step");
+}
+
+size_t kin_quest_ws_bytes(const kin_desc *desc, int32_t k) {
+    kin::Geo g;
+    if (check_step(desc, &g) != KIN_OK) return (size_t)-1;
+    if (k < 1 || k > kin::kStepIdxCap) {
+        fail(KIN_ERR_SHAPE, "k = %d: need 1 <= k <= %d", k, kin::kStepIdxCap);
+        return (size_t)-1;
+    }
+    return align256(kin::plan_step(g, k, num_cu()).ws_bytes) + step_scores_bytes(g);
+}
+
 // Token-level step: the descriptor with block 1 (every token its own block).
 static kin_status check_tok(const kin_desc *desc, int32_t k, kin::Geo *g) {
     if (!desc) return fail(KIN_ERR_NULL, "desc is NULL");

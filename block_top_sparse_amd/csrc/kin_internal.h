@@ -75,6 +75,14 @@ hipError_t launch_select_attend(const Geo &g, const AttnPlan &p, const void *q, 
 bool step_single_kernel(const Geo &g, int k, int num_cu);
 // the arrival words of a plan's in-kernel combine inside ws (nullptr: none)
 uint64_t *step_ctrl(const Geo &g, const AttnPlan &p, void *ws);
+// Quest-style summaries ([pair][nb_cap][2][head_dim]: minimum, maximum) of
+// blocks [j0, j1), and the decode step's first kernel with the Quest bound
+// (update: the newest block's rows rebuilt first); bf16
+hipError_t launch_quest_summary(const Geo &g, const void *K, void *Sq, int j0, int j1,
+                                hipStream_t s);
+hipError_t launch_quest_score(const Geo &g, const void *q, const void *K, void *Sq,
+                              double *scores, int num_cu, uint64_t *ctrl_zero, bool update,
+                              hipStream_t s);
 // token-level decode step (every token its own block; bf16): scores from K,
 // then select + attend; workspace plan_tok(...).ws_bytes
 AttnPlan plan_tok(const Geo &g, int k, int num_cu);

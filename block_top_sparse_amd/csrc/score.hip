@@ -39,7 +39,7 @@ namespace kin {
 // few pairs still spread over the whole chip.
 constexpr int kTileThreads = 512;
 
-template <bool UPDATE>
+template <bool UPDATE, bool SHARED>
 __global__ __launch_bounds__(kTileThreads) void k_score_tiles(AttnArgs a0, void *S,
                                                              double *scores, int nb_cap,
                                                              int tile_rows, uint64_t *ctrl_zero,
@@ -63,9 +63,11 @@ __global__ __launch_bounds__(kTileThreads) void k_score_tiles(AttnArgs a0, void 
     if (UPDATE && j_end == nb) {
         if (threadIdx.x == 0) nl.ready = 0u;
         __syncthreads();
-        score_blocks<NW, true>(a, S, nb_cap, pair, j_beg, nb, nl, emit);
+        score_blocks<NW, true, decltype(emit), false, SHARED>(a, S, nb_cap, pair, j_beg, nb, nl,
+                                                              emit);
     } else {
-        score_blocks<NW, false>(a, S, nb_cap, pair, j_beg, j_end, nl, emit);
+        score_blocks<NW, false, decltype(emit), false, SHARED>(a, S, nb_cap, pair, j_beg, j_end,
+                                                               nl, emit);
     }
 }
 
@@ -98,12 +100,16 @@ static hipError_t launch_tiles(const Geo &g, bool update, const void *q, const v
     int rows = (g.nb + tiles - 1) / tiles;
     rows = (rows + kRows - 1) / kRows * kRows;
     const dim3 grid(newest_only ? 1 : (g.nb + rows - 1) / rows, g.pairs);
-    if (update)
-        k_score_tiles<true><<<grid, kTileThreads, 0, s>>>(a, S, scores, g.nb_cap, rows, ctrl_zero,
-                                                          newest_only ? 1 : 0);
+    const int no = newest_only ? 1 : 0;
+    if (update && g.share_n)
+        k_score_tiles<true, true><<<grid, kTileThreads, 0, s>>>(a, S, scores, g.nb_cap, rows,
+                                                                ctrl_zero, no);
+    else if (update)
+        k_score_tiles<true, false><<<grid, kTileThreads, 0, s>>>(a, S, scores, g.nb_cap, rows,
+                                                                 ctrl_zero, no);
     else
-        k_score_tiles<false><<<grid, kTileThreads, 0, s>>>(a, S, scores, g.nb_cap, rows,
-                                                           ctrl_zero, 0);
+        k_score_tiles<false, false><<<grid, kTileThreads, 0, s>>>(a, S, scores, g.nb_cap, rows,
+                                                                  ctrl_zero, 0);
     return hipGetLastError();
 }
 

@@ -91,11 +91,13 @@ __global__ __launch_bounds__(NW * 64, NW == kStepSmallWaves ? 2 : 1) void k_deco
     // every block kept and no scores wanted: only the newest block's summary
     // is rebuilt (the range then holds just that block)
     const int j_beg = (a.k >= nb && !sc_out) ? nb - 1 : 0;
-    score_blocks<NW, true>(a, x.S, x.nb_cap, pair, j_beg, nb, nl, [&](int j, double v) {
+    auto emit = [&](int j, double v) {
         u.sc[j] = v;
         if (sc_out) sc_out[j] = v;  // scores are an optional output
         select_count(sl, v);
-    });
+    };
+    score_blocks<NW, true, decltype(emit), false, MODE == kShared>(a, x.S, x.nb_cap, pair, j_beg,
+                                                                  nb, nl, emit);
     __syncthreads();
 
     // 3. selection (reads the scores from LDS; they are dead afterwards, so

@@ -30,6 +30,7 @@ class Workload:
     t_cap: int = 0         # cache capacity in tokens (0: equal to ctx_len)
     share_n: int = 0       # samples per shared prompt (0: no shared prompt)
     prompt_len: int = 0    # tokens of each shared prompt
+    quest: bool = False    # Quest-style representative (minimum and maximum rows)
 
     @property
     def gqa(self) -> int:
@@ -66,6 +67,8 @@ class Workload:
         step without a scores output skips them)."""
         if self.k_eff >= self.nb:
             return 0
+        if self.quest:  # two summary rows per block
+            return 2 * self.pairs * self.nb * self.head_dim * self.esize
         if self.share_n:
             # a prompt's block summaries are read once for its n_share samples
             pb = self.prompt_len // self.block
@@ -93,6 +96,9 @@ class Workload:
         with blocks of one token (the keys are the summaries)."""
         if self.block == 1:
             return 0
+        if self.quest:  # the newest block's keys in, its two rows out
+            newest = self.ctx_len - (self.nb - 1) * self.block
+            return self.pairs * (newest + 2) * self.head_dim * self.esize
         newest = self.ctx_len - (self.nb - 1) * self.block
         return self.pairs * (newest + 1) * self.head_dim * self.esize
 
@@ -130,6 +136,12 @@ QWEN3_32B = Workload("qwen3-32b-b32-ctx64k", batch=32, hq=64, hkv=8, ctx_len=655
                      topk=64, dtype="bf16", seed=1004)
 
 MAIN = [TINY, QWEN3_8B, QWEN3_14B, QWEN3_32B]
+
+# Quest-style representative on the qwen3-8b decode layer.
+QUEST = [
+    Workload("quest-qwen3-8b-b32-ctx32k", batch=32, hq=32, hkv=8, ctx_len=32768, block=16,
+             topk=64, dtype="bf16", seed=1302, quest=True),
+]
 
 # Shared-prompt Best-of-N: 4 prompts x 8 samples on the qwen3-8b layer, a
 # 16K-token prompt common to each prompt's samples, 16K tokens of their own.
@@ -178,7 +190,7 @@ def sweep() -> List[Workload]:
 
 
 def by_name(name: str) -> Workload:
-    for w in MAIN + TOKEN + SHARED + sweep():
+    for w in MAIN + TOKEN + SHARED + QUEST + sweep():
         if w.name == name:
             return w
     raise KeyError(name)

@@ -252,6 +252,35 @@ KIN_API kin_status kin_shared_decode_step(const kin_desc *desc, const kin_shared
                                           double *scores, int32_t k, int32_t *idx, void *out,
                                           void *ws, size_t ws_bytes, kin_stream stream);
 
+/* Quest-style representative.  The rebuttal page "Kinetics: Rethinking
+ * Test-Time Scaling Law" (Q4 "KV block size and grouping strategy", and W2)
+ * names Quest as the second grouping strategy beside Block-TopK without
+ * defining it; it is read as the published Quest criterion.  Each block is
+ * boxed by the channel-wise minimum and maximum of its keys,
+ *   Sq [batch][hkv][nb_cap][2][head_dim], cache dtype: row 0 the minimum,
+ *      row 1 the maximum (over the block's tokens below ctx_len; exact, no
+ *      rounding),
+ * and ranked by the largest q.k inside the box, summed over the GQA group's
+ * heads: score_j = sum_h sum_c max(q_hc * min_jc, q_hc * max_jc), fp64.
+ * Selection (ties to the lower index) and attention are those of the block
+ * method.
+ *
+ * kin_quest_summary_update: the two rows of every block meeting [t_begin,
+ * t_end) and [0, ctx_len).
+ * kin_quest_decode_step: rebuilds the newest block's two rows, scores every
+ * block with the bound, keeps the k best, attends over them (two kernels on
+ * `stream`).  scores: NULL or [batch][hkv][nb_cap] fp64 (entries < nb).
+ * Workspace: kin_quest_ws_bytes(desc, k) bytes.  bf16 only; k <= 2048.
+ * Errors: as kin_sparse_decode_step, plus KIN_ERR_UNSUPPORTED for fp32 or
+ * k > 2048. */
+KIN_API kin_status kin_quest_summary_update(const kin_desc *desc, const void *K, void *Sq,
+                                            int32_t t_begin, int32_t t_end, kin_stream stream);
+KIN_API kin_status kin_quest_decode_step(const kin_desc *desc, const void *q, const void *K,
+                                         const void *V, void *Sq, double *scores, int32_t k,
+                                         int32_t *idx, void *out, void *ws, size_t ws_bytes,
+                                         kin_stream stream);
+KIN_API size_t kin_quest_ws_bytes(const kin_desc *desc, int32_t k);
+
 /* Token-level top-k decode step: every token is its own block (desc->block
  * must be 1), so the keys are their own representatives and there is no
  * summary array.  TopK attention over single tokens is the variant the

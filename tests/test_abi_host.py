@@ -29,7 +29,7 @@ def header_entry_points():
 
 def test_every_declared_entry_point_is_exported():
     declared = header_entry_points()
-    assert len(declared) == 18, declared
+    assert len(declared) == 21, declared
     lib = ctypes.CDLL(kb.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
@@ -139,6 +139,22 @@ def test_shared_prompt_step_validates_on_the_host():
     assert step(bf, ctypes.byref(ok), k=4096) == -5
     assert step(bf, ctypes.byref(kb.kin_shared_prompt(2, 64, None, FAKE, FAKE))) == -1
     assert step(bf, ctypes.byref(kb.kin_shared_prompt(2, 64, FAKE, MISALIGNED, FAKE))) == -4
+
+
+def test_quest_calls_validate_on_the_host():
+    """Quest calls (include/kin.h): bf16 only, k in 1..2048, a workspace."""
+    bf = _desc(dtype=1)
+    step = lambda d, k=4, Sq=FAKE: _raw("kin_quest_decode_step", ctypes.byref(d), FAKE, FAKE,  # noqa
+                                        FAKE, Sq, None, k, FAKE, FAKE, None, 0, None)
+    assert step(_desc(dtype=0)) == -5
+    assert step(bf, Sq=None) == -1
+    assert step(bf, k=0) == -2
+    assert step(bf, k=4096) == -5
+    assert step(bf) == -1  # no workspace (the scores live there)
+    assert kb.kin_quest_ws_bytes(bf, 4) >= 2 * 2 * 16 * 8
+    assert _raw("kin_quest_summary_update", ctypes.byref(_desc(dtype=0)), FAKE, FAKE, 0, 16,
+                None) == -5
+    assert _raw("kin_quest_summary_update", ctypes.byref(bf), FAKE, FAKE, 0, 300, None) == -2
 
 
 def test_token_calls_validate_on_the_host():
