@@ -221,6 +221,69 @@ def run_token(args, w):
     print(json.dumps(res), flush=True)
 
 
+def run_paged(args, w):
+    """Variable lengths in a paged cache: kin_paged_decode_step timed like the
+    block step over rotated layers; lengths drawn once (seeded) from
+    N(ctx_len - 3 sd, sd) clipped to [1, ctx_len]; every sequence's pages
+    scattered over one shuffled pool.  Algorithmic bytes are summed over the
+    sequences' own lengths.  One JSON line."""
+    n_layers = layers_for(w, args.layers)
+    g = torch.Generator().manual_seed(w.seed)
+    mean = w.ctx_len - 3 * w.len_std
+    lens = (torch.randn(w.batch, generator=g) * w.len_std + mean).round().clamp(1, w.ctx_len)
+    lens = lens.to(torch.int32)
+    P = w.page_size
+    max_pages = (w.ctx_len + P - 1) // P
+    cap = max_pages * P
+    desc = kb.make_desc(w.batch, w.hkv, w.gqa, cap, w.ctx_len, w.block, torch.bfloat16)
+    used = [(int(L) + P - 1) // P for L in lens.tolist()]
+    layers = []
+    for l in range(n_layers):
+        inp = synth.make_inputs(w.scaled(t_cap=cap), device="cuda", seed=w.seed + 7919 * l)
+        num_pages = sum(used)
+        perm = torch.randperm(num_pages, generator=g).tolist()
+        table = torch.zeros((w.batch, max_pages), dtype=torch.int32)
+        Kp = torch.empty((num_pages, w.hkv, P, 128), dtype=torch.bfloat16, device="cuda")
+        Vp = torch.empty_like(Kp)
+        nxt = 0
+        for b in range(w.batch):
+            for p_ in range(used[b]):
+                pg = perm[nxt]
+                nxt += 1
+                Kp[pg] = inp["K"][b, :, p_ * P:(p_ + 1) * P]
+                Vp[pg] = inp["V"][b, :, p_ * P:(p_ + 1) * P]
+                table[b, p_] = pg
+        lens_d, table_d = lens.cuda(), table.cuda()
+        pages = kb.make_pages(lens_d, table_d, P, max_pages, num_pages)
+        bufs = LayerBuffers(w.scaled(t_cap=cap))
+        kb.kin_paged_summary_update(desc, pages, Kp, bufs.S, 0, w.ctx_len)
+        q = inp["q"]
+        del inp
+        layers.append(({"q": q, "K": Kp, "V": Vp},
+                       {"bufs": bufs, "pages": pages, "keep": (lens_d, table_d)}))
+        torch.cuda.synchronize()
+        log(f"layer {l}: {num_pages} pages of {P} tokens ready")
+
+    def step(inp, b, ev):
+        d = b["bufs"]
+        kb.kin_paged_decode_step(desc, b["pages"], inp["q"], inp["K"], inp["V"], d.S, None, d.k,
+                                 d.idx, d.out, d.ws)
+
+    ms, _ = time_steps(step, layers, args.steps, args.warmup)
+    step_bytes = sum(w.scaled(batch=1, ctx_len=int(L)).bytes_sparse_step() for L in lens.tolist())
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    res = {"metric": METRIC, "value": round(w.batch / (ms * 1e-3), 1), "unit": "queries/s/layer",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": w.dtype, "data": "synthetic",
+           "config": dict(w.describe(), page_size=P, len_mean=round(float(lens.float().mean()), 1),
+                          len_std=round(float(lens.float().std()), 1), len_min=int(lens.min()),
+                          len_max=int(lens.max()), layers_rotated=n_layers),
+           "step_bytes": step_bytes, "hbm_gbs": round(gbs, 1),
+           "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    print(json.dumps(res), flush=True)
+
+
 def run_quest(args, w):
     """Quest-style representative: kin_quest_decode_step timed like the
     block step over rotated layers; one JSON line."""
@@ -320,30 +383,35 @@ def run_shared(args, w):
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(w, layer, max_seqs):
+def cpu_baseline(w, layer, max_seqs, min_seconds=10.0):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     newest-block summary update + scores + selection + attention for the
     first `max_seqs` sequences of one layer (all their KV heads), summaries
-    prebuilt outside the timed region."""
+    prebuilt outside the timed region; repeated until at least min_seconds
+    of CPU work have been timed, the rate averaged over all repetitions."""
     import oracle
 
-    inp, bufs = layer
+    inp = layer[0]
     n = min(max_seqs, w.batch)
     nthreads = oracle.default_threads()
     q = inp["q"][:n].cpu()
     K = inp["K"][:n].cpu()
     V = inp["V"][:n].cpu()
     S, _ = oracle.block_summary(K, w.block, w.ctx_len, nthreads=nthreads)
-    t0 = time.perf_counter()
-    S, _ = oracle.block_summary(K, w.block, w.ctx_len, t_begin=w.ctx_len - 1, t_end=w.ctx_len,
-                                S=S, nthreads=nthreads)
-    sc = oracle.block_score(q, S, w.gqa, w.nb, nthreads=nthreads)
-    idx, _ = oracle.block_topk(sc, w.nb, w.topk, nthreads=nthreads)
-    oracle.decode_attention(q, K, V, w.gqa, w.ctx_len, w.block, idx=idx, nthreads=nthreads)
-    dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "queries/s/layer", "cores": nthreads, "kind": "oracle",
-            "sample": f"{n} of {w.batch} sequences x {w.hkv} KV heads of one layer "
-                      f"(summary update + scores + top-k + attention, fp64), {dt:.2f} s"}
+    reps, dt = 0, 0.0
+    while dt < min_seconds:
+        t0 = time.perf_counter()
+        S, _ = oracle.block_summary(K, w.block, w.ctx_len, t_begin=w.ctx_len - 1, t_end=w.ctx_len,
+                                    S=S, nthreads=nthreads)
+        sc = oracle.block_score(q, S, w.gqa, w.nb, nthreads=nthreads)
+        idx, _ = oracle.block_topk(sc, w.nb, w.topk, nthreads=nthreads)
+        oracle.decode_attention(q, K, V, w.gqa, w.ctx_len, w.block, idx=idx, nthreads=nthreads)
+        dt += time.perf_counter() - t0
+        reps += 1
+    return {"value": n * reps / dt, "unit": "queries/s/layer", "cores": nthreads, "kind": "oracle",
+            "sample": f"{n} of {w.batch} sequences x {w.hkv} KV heads of one layer (summary "
+                      f"update + scores + top-k + attention, fp64), {reps} repetitions, "
+                      f"{dt:.1f} s"}
 
 
 def main():
@@ -384,6 +452,9 @@ def main():
         return
     if w.quest:
         run_quest(args, w)
+        return
+    if w.page_size:
+        run_paged(args, w)
         return
     n_layers = layers_for(w, args.layers)
     log(f"workload {w.name}: {n_layers} layers rotated, step bytes "

@@ -31,6 +31,8 @@ class Workload:
     share_n: int = 0       # samples per shared prompt (0: no shared prompt)
     prompt_len: int = 0    # tokens of each shared prompt
     quest: bool = False    # Quest-style representative (minimum and maximum rows)
+    page_size: int = 0     # paged K/V (tokens per page; 0: contiguous caches)
+    len_std: int = 0       # per-sequence lengths ~ N(ctx_len - 3 len_std, len_std), clipped
 
     @property
     def gqa(self) -> int:
@@ -137,6 +139,14 @@ QWEN3_32B = Workload("qwen3-32b-b32-ctx64k", batch=32, hq=64, hkv=8, ctx_len=655
 
 MAIN = [TINY, QWEN3_8B, QWEN3_14B, QWEN3_32B]
 
+# Variable lengths in a paged cache: the qwen3-8b layer with lengths of mean
+# 32K and standard deviation 2K (rebuttal, Q3 "Diverse prompt lengths"),
+# ctx_len the bound, 256-token pages in a shuffled pool.
+PAGED = [
+    Workload("paged-qwen3-8b-b32-ctx32k-sd2k", batch=32, hq=32, hkv=8, ctx_len=32768 + 6144,
+             block=16, topk=64, dtype="bf16", seed=1402, page_size=256, len_std=2048),
+]
+
 # Quest-style representative on the qwen3-8b decode layer.
 QUEST = [
     Workload("quest-qwen3-8b-b32-ctx32k", batch=32, hq=32, hkv=8, ctx_len=32768, block=16,
@@ -190,7 +200,7 @@ def sweep() -> List[Workload]:
 
 
 def by_name(name: str) -> Workload:
-    for w in MAIN + TOKEN + SHARED + QUEST + sweep():
+    for w in MAIN + TOKEN + SHARED + QUEST + PAGED + sweep():
         if w.name == name:
             return w
     raise KeyError(name)
