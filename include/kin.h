@@ -36,6 +36,12 @@
  * and out alike.  Supported: head_dim 128; block 16, 32, 64 or 128;
  * 1 <= gqa <= 16; nb <= 16384.
  *
+ * Besides the block method on contiguous caches, the library has decode
+ * steps for variable lengths and paged caches (kin_paged_*), for prompts
+ * shared by Best-of-N samples (kin_shared_decode_step), for blocks of one
+ * token (kin_token_decode_step) and for a Quest-style representative
+ * (kin_quest_*), each documented where it is declared below.
+ *
  * Conventions for every call:
  *   - The caller owns every buffer; the library allocates nothing, never
  *     synchronises, and keeps no state beyond cached device properties and a
