@@ -84,7 +84,8 @@ template <int DT, int KPT, int MODE>
 __global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a0,
                                                                 const double *__restrict__ scores,
                                                                 int nb_cap, int32_t *idx_out,
-                                                                uint64_t *ctrl, uint32_t epoch) {
+                                                                uint64_t *ctrl, uint32_t epoch,
+                                                                void *S_newest) {
     constexpr int NW = kStepThreads / 64;
     __shared__ int32_t sel[kStepIdxCap];
     __shared__ union {
@@ -93,7 +94,8 @@ __global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a0,
     } u;
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int split = blockIdx.x, pair = blockIdx.y;
+    int pair, split;
+    split_slot(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, gridDim.y, pair, split);
     const AttnArgs a = for_pair(a0, pair);  // this sequence's own length
     select_clear(u.s);
     __syncthreads();
@@ -102,6 +104,11 @@ __global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a0,
     if (split == 0)
         for (int i = threadIdx.x; i < a.k; i += kStepThreads) idx_out[(size_t)pair * a.k + i] = sel[i];
     __syncthreads();  // selection done: its LDS is free for the merge
+
+    // a step that keeps every block: the newest summary row is rebuilt here
+    // (by the wave with the fewest chunks), the step has no scoring half
+    if (DT == KIN_BF16 && S_newest && split == 0 && wave == NW - 1)
+        newest_row_bf16(a, S_newest, nb_cap, pair, threadIdx.x & 63);
 
     const int cps = (a.n_chunks + a.nsplit - 1) / a.nsplit;
     const int c_beg = split * cps;
@@ -140,8 +147,8 @@ __global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a0,
     __shared__ uint32_t last;
     __syncthreads();
     if (threadIdx.x == 0)
-        last = (epoch ? arrive_count(ctrl + pair, epoch) : arrive_add(ctrl + pair)) ==
-               (uint32_t)a.nsplit;
+        last = (epoch ? arrive_count(ctrl + pair, epoch, a.nsplit - 1)
+                      : arrive_add(ctrl + pair)) == (uint32_t)a.nsplit;
     __syncthreads();
     if (last) combine_pair<DT, kStepThreads>(a, pair);
 }
@@ -257,10 +264,11 @@ hipError_t launch_attention(const Geo &g, const AttnPlan &p, const void *q, cons
 
 template <int DT>
 static void launch_sa(const Geo &g, const AttnArgs &a, dim3 grid, const double *scores,
-                      int32_t *idx, uint64_t *ctrl, uint32_t epoch, hipStream_t s) {
+                      int32_t *idx, uint64_t *ctrl, uint32_t epoch, void *S_newest,
+                      hipStream_t s) {
 #define KIN_SA_MODE(KPT, MODE)                                                                 \
     k_select_attend<DT, KPT, MODE><<<grid, kStepThreads, 0, s>>>(a, scores, g.nb_cap, idx, ctrl, \
-                                                                 epoch)
+                                                                 epoch, S_newest)
 #define KIN_SA(KPT)                                                                            \
     (DT != KIN_BF16 ? KIN_SA_MODE(KPT, kContig)                                                \
      : g.pages      ? KIN_SA_MODE(KPT, (DT == KIN_BF16 ? kPaged : kContig))                    \
@@ -286,7 +294,8 @@ uint64_t *step_ctrl(const Geo &g, const AttnPlan &p, void *ws) {
 
 hipError_t launch_select_attend(const Geo &g, const AttnPlan &p, const void *q, const void *K,
                                 const void *V, const double *scores, int k, int32_t *idx,
-                                void *out, void *ws, uint32_t epoch, hipStream_t s) {
+                                void *out, void *ws, uint32_t epoch, hipStream_t s,
+                                void *S_newest) {
     if (!p.fused) {
         hipError_t e = launch_block_topk(g, scores, k, idx, s);
         if (e != hipSuccess) return e;
@@ -297,9 +306,9 @@ hipError_t launch_select_attend(const Geo &g, const AttnPlan &p, const void *q, 
     uint64_t *ctrl = step_ctrl(g, p, ws);
     dim3 grid(p.nsplit, g.pairs);
     if (g.dtype == KIN_BF16)
-        launch_sa<KIN_BF16>(g, a, grid, scores, idx, ctrl, epoch, s);
+        launch_sa<KIN_BF16>(g, a, grid, scores, idx, ctrl, epoch, S_newest, s);
     else
-        launch_sa<KIN_F32>(g, a, grid, scores, idx, ctrl, epoch, s);
+        launch_sa<KIN_F32>(g, a, grid, scores, idx, ctrl, epoch, nullptr, s);
     return hipGetLastError();
 }
 

@@ -182,6 +182,50 @@ __device__ __forceinline__ int shared_pair(const AttnArgs &a, int x, int pairs) 
     return ((u / a.hkv) * n + smp) * a.hkv + u % a.hkv;
 }
 
+// The newest block's mean-key summary row rebuilt by one wave from K and
+// written to S ([pair][nb_cap] rows): fp64 sum in ascending token order,
+// fp64 mean, fp32 then bf16 rounding, the arithmetic of the scoring phase's
+// rebuild, so the row is bit for bit the one that path writes.  Lane l:
+// channels 2l and 2l + 1.  `a` holds the pair's own length (for_pair).
+__device__ inline void newest_row_bf16(const AttnArgs &a, void *S, int nb_cap, int pair,
+                                       int lane) {
+    const int jn = a.nb - 1;
+    const int tn = min(a.block, a.ctx_len - jn * a.block);
+    // the block lies inside one page: its rows are consecutive
+    const uint32_t *k = static_cast<const uint32_t *>(a.K) +
+                        token_row(a, pair, jn * a.block) * (kHeadDim / 2) + lane;
+    double s0 = 0.0, s1 = 0.0;
+#pragma unroll 16
+    for (int t = 0; t < tn; ++t) {
+        const uint32_t v = k[(size_t)t * (kHeadDim / 2)];
+        s0 += (double)bf16_lo(v);
+        s1 += (double)bf16_hi(v);
+    }
+    const double cnt = (double)tn;
+    const float m0 = (float)(s0 / cnt), m1 = (float)(s1 / cnt);
+    static_cast<uint32_t *>(S)[((size_t)pair * nb_cap + jn) * (kHeadDim / 2) + lane] =
+        f32_to_bf16_bits(m0) | (f32_to_bf16_bits(m1) << 16);
+}
+
+// Launch order of a split launch (ns workgroups per pair, workgroup x =
+// blockIdx.y * ns + blockIdx.x running on XCD x % 8): the ns splits of a
+// pair are given slots of one XCD, so the pair's scores, which every split
+// reads for its selection, are fetched into that XCD's L2 once rather than
+// into ns of them (and the combine reads partials written on the same XCD).
+// The pairs past the last multiple of 8 keep the plain order.
+__device__ __forceinline__ void split_slot(int x, int ns, int pairs, int &pair, int &split) {
+    const int full = pairs & ~7;
+    if (x < full * ns) {
+        const int slot = x >> 3;
+        pair = (slot / ns) * 8 + (x & 7);
+        split = slot % ns;
+    } else {
+        const int r = x - full * ns;
+        pair = full + r / ns;
+        split = r % ns;
+    }
+}
+
 __device__ __forceinline__ SharedRuns shared_runs(const AttnArgs &a, int pair,
                                                   const int32_t *sel) {
     return SharedRuns{(int64_t)pair * a.t_cap, (int64_t)prompt_unit(a, pair) * a.prompt_len,
@@ -223,9 +267,12 @@ __device__ __forceinline__ void stores_complete() {
 // Count this workgroup's arrival at *ctr in round `epoch` (ctr holds
 // epoch << 32 | count; a word left by another round counts as zero, so the
 // word needs no clearing between calls).  Returns the count including this
-// arrival.
-__device__ inline uint32_t arrive_count(uint64_t *ctr, uint32_t epoch) {
-    uint64_t old = ld_agent(ctr);
+// arrival.  The first compare-and-swap assumes the word already counts
+// `others` arrivals of this round: right for the last arrival once the
+// others are done, which then takes a single round trip (a wrong guess
+// only costs a retry with the value the swap returned).
+__device__ inline uint32_t arrive_count(uint64_t *ctr, uint32_t epoch, uint32_t others) {
+    uint64_t old = ((uint64_t)epoch << 32) | others;
     for (;;) {
         const uint32_t c = (uint32_t)(old >> 32) == epoch ? (uint32_t)old + 1u : 1u;
         const uint64_t next = ((uint64_t)epoch << 32) | c;

@@ -279,9 +279,15 @@ static kin_status decode_step(const kin::Geo &g, const void *q, const void *K, c
     double *sc = scores ? scores
                         : reinterpret_cast<double *>(static_cast<char *>(ws) +
                                                      align256(p.ws_bytes));
-    // every block kept and no scores wanted: the first kernel only rebuilds
-    // the newest summary row; it also clears the second kernel's arrival words
+    // every block kept and no scores wanted: only the newest summary row is
+    // rebuilt, by the fused second half itself (its split partials then count
+    // their arrivals with the call's round tag)
     const bool newest_only = !scores && k >= g.nb && g.dtype == KIN_BF16;
+    if (newest_only && p.fused)
+        return launched(kin::launch_select_attend(g, p, q, K, V, sc, k, idx, out, ws,
+                                                  next_epoch(), s, S),
+                        "kin_sparse_decode_step");
+    // the first kernel also clears the second kernel's arrival words
     hipError_t e = kin::launch_update_and_score(g, q, K, S, sc, cu, s, newest_only,
                                                 kin::step_ctrl(g, p, ws));
     if (e == hipSuccess) e = kin::launch_select_attend(g, p, q, K, V, sc, k, idx, out, ws, 0u, s);

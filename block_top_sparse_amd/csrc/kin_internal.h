@@ -66,10 +66,13 @@ hipError_t launch_attention(const Geo &g, const AttnPlan &p, const void *q, cons
 // pair when the plan allows it (plan_step); otherwise separate launches
 AttnPlan plan_step(const Geo &g, int k, int num_cu);
 // (epoch: the call's round tag for the in-kernel combine of split partials;
-// 0: the arrival words at step_ctrl() were cleared by an earlier kernel)
+// 0: the arrival words at step_ctrl() were cleared by an earlier kernel;
+// S_newest: with a fused plan that keeps every block, bf16, the summaries
+// whose newest row the kernel rebuilds, so that no first half is needed)
 hipError_t launch_select_attend(const Geo &g, const AttnPlan &p, const void *q, const void *K,
                                 const void *V, const double *scores, int k, int32_t *idx,
-                                void *out, void *ws, uint32_t epoch, hipStream_t s);
+                                void *out, void *ws, uint32_t epoch, hipStream_t s,
+                                void *S_newest = nullptr);
 // the whole decode step in one kernel (one workgroup per pair); usable when
 // step_single_kernel() says so (bf16, enough pairs to cover the chip)
 bool step_single_kernel(const Geo &g, int k, int num_cu);

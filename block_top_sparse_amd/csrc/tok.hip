@@ -75,7 +75,8 @@ __global__ __launch_bounds__(kStepThreads) void k_tok_select_attend(AttnArgs a,
     constexpr int NW = kStepThreads / 64;
     __shared__ TokLds<kStepThreads> lds;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int split = blockIdx.x, pair = blockIdx.y;
+    int pair, split;
+    split_slot(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, gridDim.y, pair, split);
 
     // every split of a pair repeats the selection (it ends with a barrier)
     select_stream<kStepThreads>(scores + (size_t)pair * n_cap, a.ctx_len, a.k, lds.sel, lds.u.s,

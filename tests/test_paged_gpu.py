@@ -177,6 +177,7 @@ PAGED = [
     ("edge-g2-b16-p16", 12, 2, 2, 16, 16, 1000, 8, "edge"),
     ("few-g8-b64-p128-k1", 2, 2, 8, 64, 128, 5000, 1, "rand"),
     ("few-g5-b32-p256-kpast", 4, 2, 5, 32, 256, 2000, 40, "rand"),
+    ("few-g4-b16-p64-keepall", 3, 2, 4, 16, 64, 600, 40, "rand"),  # every block kept
     ("few-g16-b128-p128", 2, 2, 16, 128, 128, 3000, 5, "edge"),
     ("many-g4-b16-p256", 40, 8, 4, 16, 256, 4096, 64, "rand"),    # 320 pairs: one kernel
     ("many-g8-b32-p64", 36, 8, 8, 32, 64, 3000, 16, "edge"),       # 288 pairs: one kernel
@@ -194,9 +195,12 @@ def test_paged_step_against_oracle(case):
     # same tokens, contiguous caches: bit for bit the same results
     r_contig = c.run(paged=False)
     assert_same(r_paged, r_contig, c, "paged vs contiguous")
-    # no scores buffer
+    # no scores buffer (every block kept: one kernel, which also rebuilds the newest rows)
     r_ns = c.run(paged=True, no_scores=True)
     assert torch.equal(r_ns[2], r_paged[2]) and torch.equal(bits(r_ns[3]), bits(r_paged[3]))
+    for b in range(c.w.batch):
+        assert torch.equal(bits(r_ns[0][b, :, :c.nb(b)]), bits(r_paged[0][b, :, :c.nb(b)])), \
+            f"no scores: S, seq {b}"
     say(f"case {name}: max err {err:.3e}")
 
 

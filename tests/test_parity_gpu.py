@@ -170,6 +170,7 @@ NEWEST_ROW = [
     ("newest-single-nb2", 32, 64, 8, 150, 128, 1, "bf16", 256),     # one kernel, two blocks
     ("newest-few-nb1", 2, 16, 4, 90, 128, 3, "bf16", 128),          # two kernels
     ("newest-few-nb3", 2, 16, 4, 40, 16, 1, "bf16", 48),
+    ("newest-few-keepall-split", 2, 16, 4, 700, 32, 40, "bf16", 704),  # two splits per pair
     ("newest-two-kernel-f32", 2, 8, 2, 70, 64, 1, "f32", 128),      # update + score kernel
 ]
 

@@ -67,7 +67,7 @@ def build(case):
                 desc=desc, n_share=n_share, P=P, k=k)
 
 
-def run(c, shared=True):
+def run(c, shared=True, with_scores=True):
     w, k = c["w"], c["k"]
     nb_cap = w.nb_cap
     S = torch.full((w.batch, w.hkv, nb_cap, 128), NAN, dtype=torch.bfloat16, device="cuda")
@@ -83,7 +83,8 @@ def run(c, shared=True):
                      device="cuda")
     if shared:
         share = kb.make_share(c["n_share"], c["P"], c["Kp"], c["Vp"], c["Sp"])
-        kb.kin_shared_decode_step(c["desc"], share, c["q"], K, V, S, scores, k, idx, out, ws)
+        kb.kin_shared_decode_step(c["desc"], share, c["q"], K, V, S,
+                                  scores if with_scores else None, k, idx, out, ws)
     else:
         kb.kin_sparse_decode_step(c["desc"], c["q"], K, V, S, scores, k, idx, out, ws)
     torch.cuda.synchronize()
@@ -124,4 +125,9 @@ def test_shared_prompt_step_against_oracle(case):
     assert torch.equal(bits(out2), bits(out))
     assert torch.equal(bits(S2[:, :, pb:nb]), bits(S[:, :, pb:nb]))
     assert torch.equal(sc2[:, :, :nb].view(torch.int64), scores[:, :, :nb].view(torch.int64))
+    # no scores buffer: the same selection, output and rebuilt rows
+    S3, _, idx3, out3 = run(c, with_scores=False)
+    assert torch.equal(idx3, idx)
+    assert torch.equal(bits(out3), bits(out))
+    assert torch.equal(bits(S3[:, :, pb:nb]), bits(S[:, :, pb:nb]))
     say(f"  ok, max err {worst:.3e}")
