@@ -33,27 +33,31 @@ __global__ __launch_bounds__(kTokScoreThreads) void k_tok_score(AttnArgs a, doub
                                                                uint64_t *ctrl_zero) {
     constexpr int NW = kTokScoreThreads / 64;
     __shared__ NewestLds<NW> nl;  // not used: no summary to rebuild
-    __shared__ uint32_t coarse[256];
     __shared__ uint32_t fine[4096];
     const int pair = blockIdx.y, tile = blockIdx.x;
     if (ctrl_zero && tile == 0 && threadIdx.x == 0) ctrl_zero[pair] = 0ull;
     for (int i = threadIdx.x; i < 4096; i += kTokScoreThreads) fine[i] = 0u;
-    for (int i = threadIdx.x; i < 256; i += kTokScoreThreads) coarse[i] = 0u;
     __syncthreads();
     const int j_beg = tile * tile_rows;
     const int j_end = min(a.ctx_len, j_beg + tile_rows);
     double *sp = scores + (size_t)pair * a.t_cap;
+    // the scores of a pair fall into a few sign/exponent bins: one atomic per
+    // distinct bin of the wave, not one per key (the coarse table is summed
+    // from the fine one at the end)
     if (j_beg < j_end)
         score_blocks<NW, false>(a, const_cast<void *>(a.K), a.t_cap, pair, j_beg, j_end, nl,
                                 [&](int j, double v) {
             sp[j] = v;
-            const uint64_t key = order_key(v);
-            atomicAdd(&coarse[key >> 56], 1u);
-            atomicAdd(&fine[key >> 52], 1u);
+            count_wave_aggregated(fine, (uint32_t)(order_key(v) >> 52), true);
         });
     __syncthreads();
     uint32_t *t = tables + ((size_t)pair * gridDim.x + tile) * kTableWords;
-    for (int i = threadIdx.x; i < 256; i += kTokScoreThreads) t[i] = coarse[i];
+    for (int i = threadIdx.x; i < 256; i += kTokScoreThreads) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c += fine[16 * i + r];
+        t[i] = c;
+    }
     for (int i = threadIdx.x; i < 4096; i += kTokScoreThreads) t[256 + i] = fine[i];
 }
 
