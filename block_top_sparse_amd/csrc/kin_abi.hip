@@ -435,10 +435,13 @@ kin_status kin_quest_decode_step(const kin_desc *desc, const void *q, const void
         return fail(KIN_ERR_UNSUPPORTED, "k = %d: the Quest step keeps at most %d blocks", k,
                     kin::kStepIdxCap);
     const int cu = num_cu();
+    hipStream_t s = (hipStream_t)stream;
+    if (kin::step_single_kernel(g, k, cu))
+        return launched(kin::launch_decode_step(g, q, K, V, Sq, scores, k, idx, out, cu, s, true),
+                        "kin_quest_decode_step");
     const kin::AttnPlan p = kin::plan_step(g, k, cu);
     st = check_ws_size(align256(p.ws_bytes) + (scores ? 0 : step_scores_bytes(g)), ws, ws_bytes);
     if (st != KIN_OK) return st;
-    hipStream_t s = (hipStream_t)stream;
     double *sc = scores ? scores
                         : reinterpret_cast<double *>(static_cast<char *>(ws) +
                                                      align256(p.ws_bytes));

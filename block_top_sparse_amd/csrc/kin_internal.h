@@ -92,9 +92,11 @@ AttnPlan plan_tok(const Geo &g, int k, int num_cu);
 hipError_t launch_tok_step(const Geo &g, const void *q, const void *K, const void *V,
                            double *scores, int k, int32_t *idx, void *out, void *ws, int num_cu,
                            hipStream_t s);
+// (quest: S holds the Quest-style [pair][nb_cap][2][head_dim] summaries and
+// the blocks are ranked by the Quest bound; contiguous caches only)
 hipError_t launch_decode_step(const Geo &g, const void *q, const void *K, const void *V, void *S,
                               double *scores, int k, int32_t *idx, void *out, int num_cu,
-                              hipStream_t s);
+                              hipStream_t s, bool quest = false);
 
 // ---------------------------------------------------------------------------
 // device helpers (bf16 is carried as its raw 16 bits)

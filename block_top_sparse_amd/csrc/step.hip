@@ -57,12 +57,15 @@ struct StepExtra {
 // looked up once, after the selection); kShared: a shared prompt's blocks
 // from its own arrays (and the samples of a prompt launched next to each
 // other on one XCD); the sequences may differ in length either way
-// (for_pair).  NW waves; MAXNB: scores held in LDS.
-template <int KPT, int MODE, int NW, int MAXNB>
+// (for_pair).  QUEST: S holds two rows per block (channel-wise minimum and
+// maximum of its keys) and a block's score is the Quest bound (scoring.h).
+// NW waves; MAXNB: scores held in LDS.
+template <int KPT, int MODE, int NW, int MAXNB, bool QUEST>
 __global__ __launch_bounds__(NW * 64, NW == kStepSmallWaves ? 2 : 1) void k_decode_step(
     AttnArgs a0, StepExtra x) {
     constexpr int NT = NW * 64;
     static_assert(NW == kStepSmallWaves || NewestLds<NW>::kMaxBlock >= 128, "every block size");
+    static_assert(!QUEST || MODE == kContig, "Quest summaries: contiguous caches");
     __shared__ int32_t sel[kStepIdxCap];
     __shared__ union {
         SelectLds<KPT, NT> sl;
@@ -96,7 +99,7 @@ __global__ __launch_bounds__(NW * 64, NW == kStepSmallWaves ? 2 : 1) void k_deco
         if (sc_out) sc_out[j] = v;  // scores are an optional output
         select_count(sl, v);
     };
-    score_blocks<NW, true, decltype(emit), false, MODE == kShared>(a, x.S, x.nb_cap, pair, j_beg,
+    score_blocks<NW, true, decltype(emit), QUEST, MODE == kShared>(a, x.S, x.nb_cap, pair, j_beg,
                                                                   nb, nl, emit);
     __syncthreads();
 
@@ -139,14 +142,21 @@ bool step_single_kernel(const Geo &g, int k, int num_cu) {
     return g.dtype == KIN_BF16 && g.nb <= kStepMaxBlocks && k <= kStepIdxCap && g.pairs >= cu;
 }
 
-template <int NW, int MAXNB>
+template <int NW, int MAXNB, bool QUEST>
 static void launch_shape(const Geo &g, const AttnArgs &a, const StepExtra &x, hipStream_t s) {
     constexpr int NT = NW * 64;
     const dim3 grid(g.pairs);
 #define KIN_STEP(KPT)                                                                          \
-    (g.pages ? k_decode_step<KPT, kPaged, NW, MAXNB><<<grid, NT, 0, s>>>(a, x)                  \
-     : g.share_n ? k_decode_step<KPT, kShared, NW, MAXNB><<<grid, NT, 0, s>>>(a, x)             \
-                 : k_decode_step<KPT, kContig, NW, MAXNB><<<grid, NT, 0, s>>>(a, x))
+    do {                                                                                       \
+        if constexpr (QUEST)                                                                   \
+            k_decode_step<KPT, kContig, NW, MAXNB, true><<<grid, NT, 0, s>>>(a, x);            \
+        else if (g.pages)                                                                      \
+            k_decode_step<KPT, kPaged, NW, MAXNB, false><<<grid, NT, 0, s>>>(a, x);            \
+        else if (g.share_n)                                                                    \
+            k_decode_step<KPT, kShared, NW, MAXNB, false><<<grid, NT, 0, s>>>(a, x);           \
+        else                                                                                   \
+            k_decode_step<KPT, kContig, NW, MAXNB, false><<<grid, NT, 0, s>>>(a, x);           \
+    } while (0)
     switch (select_kpt(g.nb, NT)) {
     case 1: KIN_STEP(1); break;
     case 2: KIN_STEP(2); break;
@@ -161,7 +171,7 @@ static void launch_shape(const Geo &g, const AttnArgs &a, const StepExtra &x, hi
 
 hipError_t launch_decode_step(const Geo &g, const void *q, const void *K, const void *V, void *S,
                               double *scores, int k, int32_t *idx, void *out, int num_cu,
-                              hipStream_t s) {
+                              hipStream_t s, bool quest) {
     AttnPlan p;
     const int keff = k < g.nb ? k : g.nb;
     p.n_tokens = keff * g.block;
@@ -172,10 +182,15 @@ hipError_t launch_decode_step(const Geo &g, const void *q, const void *K, const 
     AttnArgs a;
     fill_args(a, g, p, q, K, V, nullptr, k, out, nullptr);
     const StepExtra x{S, scores, idx, g.nb_cap};
-    if (step_small(g, num_cu > 0 ? num_cu : 256))
-        launch_shape<kStepSmallWaves, kStepSmallBlocks>(g, a, x, s);
+    const bool small = step_small(g, num_cu > 0 ? num_cu : 256);
+    if (quest && small)
+        launch_shape<kStepSmallWaves, kStepSmallBlocks, true>(g, a, x, s);
+    else if (quest)
+        launch_shape<kStepThreads / 64, kStepMaxBlocks, true>(g, a, x, s);
+    else if (small)
+        launch_shape<kStepSmallWaves, kStepSmallBlocks, false>(g, a, x, s);
     else
-        launch_shape<kStepThreads / 64, kStepMaxBlocks>(g, a, x, s);
+        launch_shape<kStepThreads / 64, kStepMaxBlocks, false>(g, a, x, s);
     return hipGetLastError();
 }
 

@@ -39,6 +39,10 @@ QUEST = [
     ("q-g4-b16-kpast", 2, 8, 2, 200, 16, 20, 208),           # k > nb
     ("q-g8-b128-short", 2, 16, 2, 100, 128, 2, 128),         # one partial block
     ("q-g5-b16-nb8192", 1, 10, 2, 131072, 16, 300, 131072),
+    # at least as many pairs as CUs: the whole step in one kernel
+    ("q-single-4w-g4-b16", 128, 16, 4, 2000, 16, 20, 2048),   # 512 pairs: the 4-wave step
+    ("q-single-g4-b64-keepall", 64, 16, 4, 1000, 64, 20, 1024),
+    ("q-single-g2-b16-nb8192", 64, 8, 4, 131072, 16, 300, 131072),  # 256 pairs, 8192 blocks
 ]
 
 
