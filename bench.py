@@ -153,6 +153,19 @@ def single_kernel(w, num_cu):
     return w.dtype == "bf16" and w.pairs >= num_cu and w.nb <= 8192 and w.topk <= 2048
 
 
+def step_kernels(w, num_cu):
+    """The launches of one kin_sparse_decode_step without a scores output, as
+    the library plans them: "one" (the whole step per pair), "one-split" (a
+    step that keeps every block, few pairs: select + split attention alone),
+    "two" (score tiles, then select + split attention), "four" (more than
+    2048 kept blocks: scores or the newest row, top-k, attention, combine)."""
+    if single_kernel(w, num_cu):
+        return "one"
+    if w.topk > 2048:
+        return "four"
+    return "one-split" if w.topk >= w.nb and w.dtype == "bf16" else "two"
+
+
 def run_sweep(args):
     """The budget/length grid: per point, kin_sparse_decode_step timed back to
     back over rotated layers, as for the headline workload."""
@@ -176,7 +189,7 @@ def run_sweep(args):
                           "layers_rotated": n_layers, "ms_per_step": round(ms, 5),
                           "queries_per_s": round(w.batch / (ms * 1e-3), 1),
                           "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-                          "kernels": "one" if single_kernel(w, num_cu) else "two"}), flush=True)
+                          "kernels": step_kernels(w, num_cu)}), flush=True)
         del layers
         torch.cuda.empty_cache()
 
