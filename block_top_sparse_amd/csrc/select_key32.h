@@ -1,0 +1,263 @@
+// select_key32.h -- top-k selection over the keys of one pair, by one
+// workgroup, from the top 32 bits of each score's order key held in LDS
+// (the token-level step in one kernel: 32768 keys fit in 128 KiB, where
+// their fp64 scores would not).
+//
+// The kept set is the one select.h defines: the k largest fp64 scores,
+// ties to the lower index, indices ascending, then -1 (token-level TopK is
+// the block method with blocks of one token: rebuttal "Kinetics: Rethinking
+// Test-Time Scaling Law", Q2).
+//
+// The top 32 bits of a key (sign, exponent, 20 mantissa bits) order the
+// keys except inside one 32-bit bin.  The radix select runs over them: the
+// sign/exponent bin of the k-th key from a 4096-bin table counted while the
+// scores were made, then digits of 8, 8 and 4 bits (one LDS histogram and
+// one barrier per pass), stopping as soon as the bin holding the k-th key
+// holds exactly the keys still needed.  If all 32 bits are used up, only
+// the keys whose top word equals the k-th key's can still be in question;
+// their low 32 bits are recomputed from K for exactly those keys, with the
+// streaming loop's own arithmetic (exact_score_row), and ranked in four
+// more 8-bit passes; keys equal in all 64 bits keep the lower indices.  The
+// ordered compaction takes two sweeps (per (round, wave) counts of the keys
+// kept for sure and of the exact ties, a workgroup scan, then the writes).
+#pragma once
+
+#include "attn_impl.h"
+#include "select_stream.h"
+
+namespace kin {
+
+constexpr int kKey32MaxLen = 32768;
+constexpr int kKey32Batch = 8;  // keys of one thread read from LDS together
+
+// LDS of the selection after the exponent table has been read (it may
+// overlay that table).
+template <int NT>
+struct Key32Scratch {
+    static constexpr int kRounds = (kKey32MaxLen + NT - 1) / NT;
+    uint32_t hist[3][256];
+    uint32_t cnt[kRounds * (NT / 64)];
+    uint32_t cnt_tie[kRounds * (NT / 64)];
+    uint32_t wsum[2][NT / 64];
+    double qsum[kHeadDim];  // the group query sum, for the low words
+};
+
+// The fp64 score of one bf16 key row against the group query sum (qsum:
+// per channel, the heads added in ascending order from +0.0), with the
+// arithmetic of the streaming loop: per 8-channel slice s an FMA chain in
+// channel order (slice_dot), then the pairing tree of fold4 over the 16
+// slices -- x_i = (p_i + p_{i+8}) + (p_{7-i} + p_{15-i}), score =
+// (x_0 + x_1) + (x_2 + x_3) -- and -0.0 made +0.0.  So it is bit for bit
+// the score that loop made for the same row.
+__device__ __noinline__ double exact_score_row(const uint16_t *row, const double *qsum) {
+    double p[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(row + 8 * s);
+        double acc = 0.0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc = fma(qsum[8 * s + 2 * e], (double)bf16_lo(w[e]), acc);
+            acc = fma(qsum[8 * s + 2 * e + 1], (double)bf16_hi(w[e]), acc);
+        }
+        p[s] = acc;
+    }
+    double x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (p[i] + p[i + 8]) + (p[7 - i] + p[15 - i]);
+    double v = (x[0] + x[1]) + (x[2] + x[3]);
+    if (v == 0.0) v = 0.0;
+    return v;
+}
+
+// Top words of keys j0 + u * NT + threadIdx.x, u < kKey32Batch (slots past n
+// re-read key 0; callers ignore them).
+template <int NT>
+__device__ __forceinline__ void key32_batch(const uint32_t *key, int n, int j0,
+                                            uint32_t (&x)[kKey32Batch]) {
+#pragma unroll
+    for (int u = 0; u < kKey32Batch; ++u) {
+        const int j = j0 + u * NT + (int)threadIdx.x;
+        x[u] = key[j < n ? j : 0];
+    }
+}
+
+// Write out[0..k): the min(k, n) largest keys of the pair, their indices
+// ascending, then -1.  key[0..n): top words of the order keys (LDS); fine:
+// the 4096-bin count of their top 12 bits (LDS, may share memory with sc);
+// row0: the pair's first K row (bf16 rows of kHeadDim) and qp: its first
+// query head, for the low words.  Every thread of the NT-thread workgroup
+// calls this; it ends with a barrier after the last write of `out`.
+// Requires 1 <= k and n <= kKey32MaxLen.
+template <int NT>
+__device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
+                             const uint32_t *fine, Key32Scratch<NT> &sc, const uint16_t *row0,
+                             const uint16_t *qp, int gqa) {
+    constexpr int NW = NT / 64;
+    constexpr int B = kKey32Batch;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int keff = min(k, n);
+    const int R = (n + NT - 1) / NT;
+
+    for (int i = keff + tid; i < k; i += NT) out[i] = -1;
+    if (keff == n) {  // every key is kept
+        for (int i = tid; i < n; i += NT) out[i] = i;
+        __syncthreads();
+        return;
+    }
+
+    // sign and exponent of the k-th key: coarse bins (16 fine bins each)
+    // summed here, then the 16 fine bins under the chosen one
+    uint32_t krem = (uint32_t)keff;
+    uint32_t c[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t *f = fine + 16 * (255 - 4 * lane - r);
+        uint32_t s = 0;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) s += f[t];
+        c[r] = s;
+    }
+    const BinHit h1 = find_bin(c, krem, 255u, lane);
+    krem -= h1.above;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) c[r] = lane < 4 ? fine[16 * h1.digit + 15 - 4 * lane - r] : 0u;
+    const BinHit h2 = find_bin(c, krem, 16u * h1.digit + 15u, lane);
+    krem -= h2.above;
+    uint32_t prefix = h2.digit << 20, pmask = 0xFFFu << 20;
+    bool resolved = h2.in_bin == krem;
+    __syncthreads();  // every wave has read the table: the scratch may overwrite it
+    for (int i = tid; i < 256; i += NT) sc.hist[0][i] = 0u;
+    __syncthreads();
+
+    // digits of the top word: bits 19..12, 11..4, then 3..0
+    int buf = 0, lo = 12, width = 8;
+    while (!resolved) {
+        uint32_t *h = sc.hist[buf];
+        const int nbuf = buf == 2 ? 0 : buf + 1;
+        const uint32_t dmask = (1u << width) - 1u;
+        for (int j0 = 0; j0 < n; j0 += B * NT) {
+            uint32_t x[B];
+            key32_batch<NT>(key, n, j0, x);
+#pragma unroll
+            for (int u = 0; u < B; ++u)
+                if (j0 + u * NT + tid < n && (x[u] & pmask) == prefix)
+                    atomicAdd(&h[(x[u] >> lo) & dmask], 1u);
+        }
+        for (int i = tid; i < 256; i += NT) sc.hist[nbuf][i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) c[r] = h[255 - 4 * lane - r];
+        const BinHit hb = find_bin(c, krem, 255u, lane);
+        buf = nbuf;
+        krem -= hb.above;
+        prefix |= hb.digit << lo;
+        pmask |= dmask << lo;
+        if (hb.in_bin == krem) {
+            resolved = true;
+            break;
+        }
+        if (lo == 0) break;  // all 32 top bits used
+        if (lo >= 8) {
+            lo -= 8;
+        } else {
+            width = lo;
+            lo = 0;
+        }
+    }
+
+    // Not settled by the top words: prefix is now the k-th key's whole top
+    // word, and krem keys are still needed among those equal to it.  Rank
+    // them on their recomputed low words.
+    uint32_t lprefix = 0, lmask = 0;
+    bool lresolved = resolved;
+    if (!resolved) {
+        if (tid < kHeadDim) {
+            double s = 0.0;
+            for (int hh = 0; hh < gqa; ++hh) s += (double)bf16_lo((uint32_t)qp[hh * kHeadDim + tid]);
+            sc.qsum[tid] = s;
+        }
+        __syncthreads();
+        for (int llo = 24;; llo -= 8) {
+            uint32_t *h = sc.hist[buf];
+            const int nbuf = buf == 2 ? 0 : buf + 1;
+            for (int j0 = 0; j0 < n; j0 += B * NT) {
+                uint32_t x[B];
+                key32_batch<NT>(key, n, j0, x);
+#pragma unroll
+                for (int u = 0; u < B; ++u) {
+                    const int j = j0 + u * NT + tid;
+                    if (j < n && x[u] == prefix) {
+                        const uint32_t w = (uint32_t)order_key(
+                            exact_score_row(row0 + (size_t)j * kHeadDim, sc.qsum));
+                        if ((w & lmask) == lprefix) atomicAdd(&h[(w >> llo) & 255u], 1u);
+                    }
+                }
+            }
+            for (int i = tid; i < 256; i += NT) sc.hist[nbuf][i] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < 4; ++r) c[r] = h[255 - 4 * lane - r];
+            const BinHit hb = find_bin(c, krem, 255u, lane);
+            buf = nbuf;
+            krem -= hb.above;
+            lprefix |= hb.digit << llo;
+            lmask |= 255u << llo;
+            if (hb.in_bin == krem) {
+                lresolved = true;
+                break;
+            }
+            if (llo == 0) break;  // all 64 bits used: the rest are exact ties
+        }
+    }
+
+    // Class of key j: 2 = kept for sure, 1 = equal in all 64 bits to the
+    // k-th key (the first krem of these in index order are kept), 0 = not.
+    auto cls = [&](int j, uint32_t x) -> int {
+        if (resolved) return x >= prefix ? 2 : 0;  // prefix: zeros below its mask
+        if (x != prefix) return x > prefix ? 2 : 0;
+        const uint32_t w =
+            (uint32_t)order_key(exact_score_row(row0 + (size_t)j * kHeadDim, sc.qsum));
+        if (lresolved) return w >= lprefix ? 2 : 0;
+        return w > lprefix ? 2 : (w == lprefix ? 1 : 0);
+    };
+
+    // ordered compaction: counts per (round, wave), a scan, then the writes
+    for (int j0 = 0; j0 < n; j0 += B * NT) {
+        uint32_t x[B];
+        key32_batch<NT>(key, n, j0, x);
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const int r = j0 / NT + u;
+            if (r >= R) break;  // uniform
+            const int j = r * NT + tid;
+            const int cl = j < n ? cls(j, x[u]) : 0;
+            const uint64_t ma = __ballot(cl == 2), mt = __ballot(cl == 1);
+            if (lane == 0) {
+                sc.cnt[r * NW + wave] = (uint32_t)__popcll(ma);
+                sc.cnt_tie[r * NW + wave] = (uint32_t)__popcll(mt);
+            }
+        }
+    }
+    __syncthreads();
+    block_exclusive_scan2<NT>(sc.cnt, sc.cnt_tie, R * NW, sc.wsum);
+    for (int j0 = 0; j0 < n; j0 += B * NT) {
+        uint32_t x[B];
+        key32_batch<NT>(key, n, j0, x);
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const int r = j0 / NT + u;
+            if (r >= R) break;  // uniform
+            const int j = r * NT + tid;
+            const int cl = j < n ? cls(j, x[u]) : 0;
+            const uint64_t ma = __ballot(cl == 2), mt = __ballot(cl == 1);
+            const uint32_t gt_before = sc.cnt[r * NW + wave] + rank_below(ma);
+            const uint32_t tie_before = sc.cnt_tie[r * NW + wave] + rank_below(mt);
+            if (cl == 2 || (cl == 1 && tie_before < krem)) out[gt_before + min(tie_before, krem)] = j;
+        }
+    }
+    __syncthreads();
+}
+
+}  // namespace kin

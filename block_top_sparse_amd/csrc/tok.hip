@@ -11,6 +11,11 @@
 //            online softmax), split over several workgroups when there are
 //            fewer pairs than CUs, the splits combined in-kernel.
 //
+// With at least as many pairs as CUs, a context of at most 32768 tokens and
+// at most 2048 kept, the whole step runs in one kernel (k_tok_step), one
+// workgroup per pair: the scores' top words stay in LDS and nothing per
+// token is written to memory (select_key32.h).
+//
 // The method is TopK attention over single tokens, the variant the
 // rebuttal "Kinetics: Rethinking Test-Time Scaling Law" (Q2) names next to
 // Block-TopK; here it is the block method with blocks of one token: score
@@ -18,6 +23,7 @@
 // to the lower index, softmax(q . k / sqrt(d)) over the kept tokens.
 #include "attn_impl.h"
 #include "scoring.h"
+#include "select_key32.h"
 #include "select_stream.h"
 
 namespace kin {
@@ -110,6 +116,60 @@ __global__ __launch_bounds__(kStepThreads) void k_tok_select_attend(AttnArgs a,
     if (last) combine_pair<KIN_BF16, kStepThreads>(a, pair);
 }
 
+// The whole token-level step for one pair per workgroup: the score of every
+// key (the streaming loop over K), its order key's top word kept in LDS and
+// its sign/exponent counted; the selection from those words (low words
+// recomputed only for keys that share the k-th key's top word); then the
+// attention over the kept tokens and the merge of the waves.  The fp64
+// scores are written only when asked for.
+constexpr int kTokStepMaxLen = kKey32MaxLen;
+constexpr int kTokStepMaxK = kStepIdxCap;
+
+__global__ __launch_bounds__(kStepThreads) void k_tok_step(AttnArgs a, double *scores,
+                                                          int32_t *idx_out) {
+    constexpr int NW = kStepThreads / 64;
+    __shared__ union {
+        uint32_t key[kTokStepMaxLen];
+        MergeLds<NW> m;  // after the selection
+    } u;
+    __shared__ union {
+        uint32_t fine[4096];
+        Key32Scratch<kStepThreads> s;  // once the table has been read
+    } v;
+    __shared__ int32_t sel[kTokStepMaxK];
+    __shared__ NewestLds<NW> nl;  // not used: no summary to rebuild
+    const int pair = blockIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int i = threadIdx.x; i < 4096; i += kStepThreads) v.fine[i] = 0u;
+    __syncthreads();
+    const int L = a.ctx_len;
+    double *sp = scores ? scores + (size_t)pair * a.t_cap : nullptr;
+    score_blocks<NW, false>(a, const_cast<void *>(a.K), a.t_cap, pair, 0, L, nl,
+                            [&](int j, double x) {
+        const uint32_t top = (uint32_t)(order_key(x) >> 32);
+        u.key[j] = top;
+        count_wave_aggregated(v.fine, top >> 20, true);
+        if (sp) sp[j] = x;  // scores are an optional output
+    });
+    __syncthreads();
+    const int b = pair / a.hkv, g = pair % a.hkv;
+    const uint16_t *row0 = static_cast<const uint16_t *>(a.K) + (size_t)pair * a.t_cap * kHeadDim;
+    const uint16_t *qp = static_cast<const uint16_t *>(a.q) +
+                         ((size_t)b * a.hkv * a.gqa + (size_t)g * a.gqa) * kHeadDim;
+    select_key32<kStepThreads>(u.key, L, a.k, sel, v.fine, v.s, row0, qp, a.gqa);
+    for (int i = threadIdx.x; i < a.k; i += kStepThreads) idx_out[(size_t)pair * a.k + i] = sel[i];
+    // the keys are dead: the merge area overlays them
+    const TokenRuns runs{(int64_t)pair * a.t_cap, sel, a.k, L};
+    attend_bf16<TokenRuns, NW>(a, runs, pair, 0, a.n_chunks, wave, NW, wave, u.m);
+    __syncthreads();
+    merge_waves_and_store<KIN_BF16, NW>(a, u.m, pair, 0);
+}
+
+static bool tok_single_kernel(const Geo &g, int k, int num_cu) {
+    const int cu = num_cu > 0 ? num_cu : 256;
+    return g.pairs >= cu && g.ctx_len <= kTokStepMaxLen && k <= kTokStepMaxK;
+}
+
 // Token geometry: block 1, one "block" per token.
 static Geo tok_geo(const Geo &g) {
     Geo t = g;
@@ -167,6 +227,17 @@ hipError_t launch_tok_step(const Geo &g0, const void *q, const void *K, const vo
                            double *scores, int k, int32_t *idx, void *out, void *ws, int num_cu,
                            hipStream_t s) {
     const Geo g = tok_geo(g0);
+    if (tok_single_kernel(g, k, num_cu)) {
+        AttnPlan p{};
+        p.n_tokens = k < g.ctx_len ? k : g.ctx_len;
+        p.n_chunks = (p.n_tokens + kChunkBf16 - 1) / kChunkBf16;
+        p.nsplit = 1;
+        p.fused = 1;
+        AttnArgs a;
+        fill_args(a, g, p, q, K, V, nullptr, k, out, nullptr);
+        k_tok_step<<<g.pairs, kStepThreads, 0, s>>>(a, scores, idx);
+        return hipGetLastError();
+    }
     const AttnPlan p = plan_tok(g, k, num_cu);
     int tiles, rows;
     tok_tiles(g, num_cu, tiles, rows);

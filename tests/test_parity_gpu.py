@@ -345,7 +345,8 @@ def test_full_size_workloads(w):
 
 SWEEP_SAMPLE = ["sweep-b8-ctx131072-blk16-budget8192", "sweep-b128-ctx8192-blk64-budget256",
                 "sweep-b32-ctx32768-blk32-budget1024", "sweep-b8-ctx8192-blk32-allblocks",
-                "sweep-b32-ctx131072-blk64-budget4096"]
+                "sweep-b32-ctx131072-blk64-budget4096",
+                "sweep-b8-ctx131072-blk16-allblocks"]  # 8192 kept blocks: four launches
 
 
 @pytest.mark.parametrize("name", SWEEP_SAMPLE)
@@ -362,6 +363,11 @@ def test_sweep_points(name):
     step = run_gpu(w, inp, step=True)
     assert torch.equal(step.idx, bufs.idx)
     check_sequences(w, inp, step, seqs)
+    # the benchmarked call: no scores output (a step that keeps every block
+    # then has no scoring launch at all when the pairs are few)
+    quiet = run_gpu(w, inp, step=True, no_scores=True)
+    assert torch.equal(quiet.idx, bufs.idx)
+    check_sequences(w, inp, quiet, seqs, check_scores=False)
     say(f"  ok {r}")
 
 

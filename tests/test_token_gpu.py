@@ -9,6 +9,7 @@ are kept).
 """
 import zlib
 
+import numpy as np
 import pytest
 import torch
 
@@ -75,6 +76,10 @@ TOKEN = [
     ("tok-long-g2-k2048", 1, 4, 2, 131072, 2048, 131072),  # 256 rounds of the select
     ("tok-kmax-g4", 2, 4, 1, 40000, 8192, 40000),          # the largest k
     ("tok-g16-short", 2, 32, 2, 33, 32, 48),               # one round, ragged
+    # at least as many pairs as CUs, at most 32768 tokens and 2048 kept: one kernel
+    ("tok-single-g8-k2048-L32768", 32, 64, 8, 32768, 2048, 32768),
+    ("tok-single-g1-kpast", 128, 2, 2, 700, 900, 704),     # k > ctx: all kept, -1 after
+    ("tok-single-g2-k1-ragged", 128, 4, 2, 1001, 1, 1024),
 ]
 
 
@@ -108,3 +113,92 @@ def test_token_step_exact_ties_keep_lowest_indices():
     want = torch.arange(300, dtype=torch.int32, device="cuda").expand(2, 2, 300)
     assert torch.equal(idx, want)
     check(w, inp, 300, idx, out, sc, [0, 1], certify=False)
+
+
+def test_token_single_kernel_exact_ties_keep_lowest_indices():
+    """256 pairs (the one-kernel step): every key of a pair equal, so all
+    top words tie, the low words are recomputed for every key and tie as
+    well; the k lowest indices are kept."""
+    w = Workload("tok-single-ties", batch=128, hq=8, hkv=2, ctx_len=3000, block=1, topk=300,
+                 dtype="bf16", seed=4243, t_cap=3072)
+    inp = synth.make_inputs(w, device="cuda", tail_fill=float("nan"))
+    inp["K"][:, :, :3000] = inp["K"][:, :, :1].clone()
+    idx, out, sc = run_token(w, inp, 300)
+    want = torch.arange(300, dtype=torch.int32, device="cuda").expand(128, 2, 300)
+    assert torch.equal(idx, want)
+    check(w, inp, 300, idx, out, sc, [0, 127], certify=False)
+
+
+def _order_key_top(x):
+    """Top 32 bits of the order-preserving key of fp64 values (numpy)."""
+    u = x.view(np.uint64)
+    neg = (u >> np.uint64(63)) == 1
+    key = np.where(neg, ~u, u | np.uint64(1 << 63))
+    return key >> np.uint64(32)
+
+
+def _plant_near_tie(inp, w, b, g, k, exact, above=False):
+    """Overwrite a low-ranked key of pair (b, g) with the rank-k key (exact)
+    or with that key moved by one bf16 step in two channels whose effects on
+    the score nearly cancel: a score that agrees with the k-th in its top 32
+    key bits and lies just above it (above) or just below it."""
+    L = w.ctx_len
+    q = inp["q"][b, g * w.gqa:(g + 1) * w.gqa].cpu().double().numpy()
+    qs = q.sum(0)
+    Kp = inp["K"][b, g, :L].cpu()
+    sc = Kp.double().numpy() @ qs
+    order = np.argsort(-sc, kind="stable")
+    a, c = int(order[k - 1]), int(order[k + 20])
+    row = Kp[a].clone()
+    if not exact:
+        bits16 = row.view(torch.int16).numpy().astype(np.int32)
+        vals = row.double().numpy()
+        steps = []  # per channel, the change of one bf16 step up or down in the bits
+        for s in (1, -1):
+            stepped = torch.from_numpy((bits16 + s).astype(np.int16)).view(torch.bfloat16)
+            steps.append((stepped.double().numpy() - vals, s))
+        cand = []
+        for dv1, s1 in steps:
+            for dv2, s2 in steps:
+                d = np.add.outer(qs * dv1, qs * dv2)  # channel c1 moved by s1, c2 by s2
+                np.fill_diagonal(d, np.nan)
+                cand.append((d, s1, s2))
+        target = abs(sc[a])
+        pick = None
+        for d, s1, s2 in cand:
+            # below the top word's resolution (2^-20 relative), far above fp64 rounding
+            ok = np.isfinite(d) & (np.abs(d) > 1e-12 * target) & (np.abs(d) < 4e-7 * target)
+            ii = np.argwhere(ok)
+            for c1, c2 in ii[:200]:
+                new = row.view(torch.int16).clone()
+                new[c1] += s1
+                new[c2] += s2
+                nv = float(new.view(torch.bfloat16).double().numpy() @ qs)
+                if _order_key_top(np.array([nv])) == _order_key_top(np.array([sc[a]])) \
+                        and (nv > sc[a] if above else nv < sc[a]):
+                    pick = new.view(torch.bfloat16)
+                    break
+            if pick is not None:
+                break
+        assert pick is not None, "no near tie found"
+        row = pick
+    inp["K"][b, g, c] = row.cuda()
+
+
+def test_token_single_kernel_near_ties_below_the_top_word():
+    """256 pairs (the one-kernel step) with planted keys whose scores equal
+    the k-th score in the top 32 bits of the order key (near ties: they
+    differ below; exact ties: they do not): the recomputed low words must
+    order them as the oracle does."""
+    w = Workload("tok-single-near", batch=64, hq=16, hkv=4, ctx_len=2000, block=1, topk=100,
+                 dtype="bf16", seed=4244, t_cap=2048)
+    inp = synth.make_inputs(w, device="cuda", tail_fill=float("nan"))
+    # (sequence, KV head, exact tie, planted key just above the k-th)
+    planted = [(0, 0, False, False), (0, 1, True, False), (31, 2, False, True),
+               (63, 3, True, False), (63, 0, False, True)]
+    for b, g, exact, above in planted:
+        _plant_near_tie(inp, w, b, g, 100, exact, above)
+    idx, out, sc = run_token(w, inp, 100)
+    check(w, inp, 100, idx, out, sc, sorted({p[0] for p in planted}), certify=False)
+    idx2, out2, _ = run_token(w, inp, 100, scores=False)
+    assert torch.equal(idx2, idx)
