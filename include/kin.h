@@ -274,8 +274,9 @@ KIN_API kin_status kin_shared_decode_step(const kin_desc *desc, const kin_shared
  * kin_quest_summary_update: the two rows of every block meeting [t_begin,
  * t_end) and [0, ctx_len).
  * kin_quest_decode_step: rebuilds the newest block's two rows, scores every
- * block with the bound, keeps the k best, attends over them (two kernels on
- * `stream`).  scores: NULL or [batch][hkv][nb_cap] fp64 (entries < nb).
+ * block with the bound, keeps the k best, attends over them (one kernel on
+ * `stream` when batch * hkv covers the device's compute units, else two).
+ * scores: NULL or [batch][hkv][nb_cap] fp64 (entries < nb).
  * Workspace: kin_quest_ws_bytes(desc, k) bytes.  bf16 only; k <= 2048.
  * Errors: as kin_sparse_decode_step, plus KIN_ERR_UNSUPPORTED for fp32 or
  * k > 2048. */
@@ -299,11 +300,14 @@ KIN_API size_t kin_quest_ws_bytes(const kin_desc *desc, int32_t k);
  *   K, V      [batch][hkv][t_cap][head_dim], bf16 (read only).
  *   scores    NULL, or [batch][hkv][t_cap] fp64: entries t < ctx_len get the
  *             scores (the others are left alone).
- *   ws        kin_token_ws_bytes(desc, k) bytes of device scratch (the scores
- *             live there when scores is NULL).
+ *   ws        kin_token_ws_bytes(desc, k) bytes of device scratch (the
+ *             two-kernel form keeps its scores there when scores is NULL).
  * bf16 only; 1 <= k <= 8192; ctx_len <= 262144.  Errors: KIN_ERR_SHAPE for
  * block != 1 or k < 1, KIN_ERR_UNSUPPORTED for fp32, k > 8192 or longer
- * contexts, plus the checks of the other calls.  Two kernels on `stream`. */
+ * contexts, plus the checks of the other calls.  One kernel on `stream` when
+ * batch * hkv covers the device's compute units, ctx_len <= 32768 and k <=
+ * 2048 (no per-token score is written unless scores is given); two kernels
+ * otherwise. */
 KIN_API kin_status kin_token_decode_step(const kin_desc *desc, const void *q, const void *K,
                                          const void *V, double *scores, int32_t k, int32_t *idx,
                                          void *out, void *ws, size_t ws_bytes, kin_stream stream);
