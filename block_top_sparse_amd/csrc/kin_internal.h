@@ -16,7 +16,7 @@ constexpr int kChunkBf16 = 32;  // tokens per wave iteration, bf16 attention
 constexpr int kChunkF32 = 64;   // tokens per wave iteration, fp32 attention
 constexpr int kStepIdxCap = 2048;  // kept blocks the select+attend kernels hold in LDS
 constexpr int kTokIdxCap = 8192;   // kept tokens of the token-level step (LDS)
-constexpr int kTokMaxLen = 262144;  // tokens of one pair the streaming select takes
+constexpr int kTokMaxLen = 262144;  // tokens of one pair the two-kernel token step takes
 
 // Geometry shared by the launchers (all derived from a validated desc).
 struct Geo {

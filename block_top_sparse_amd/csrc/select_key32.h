@@ -1,7 +1,8 @@
 // select_key32.h -- top-k selection over the keys of one pair, by one
-// workgroup, from the top 32 bits of each score's order key held in LDS
+// workgroup, from the top 32 bits of each score's order key: held in LDS
 // (the token-level step in one kernel: 32768 keys fit in 128 KiB, where
-// their fp64 scores would not).
+// their fp64 scores would not) or streamed from memory (the two-kernel
+// token step: half the bytes of fp64 scores, written and read).
 //
 // The kept set is the one select.h defines: the k largest fp64 scores,
 // ties to the lower index, indices ascending, then -1 (token-level TopK is
@@ -23,18 +24,20 @@
 #pragma once
 
 #include "attn_impl.h"
-#include "select_stream.h"
 
 namespace kin {
 
-constexpr int kKey32MaxLen = 32768;
-constexpr int kKey32Batch = 8;  // keys of one thread read from LDS together
+// keys of one thread read together: from LDS, or from memory (enough bytes
+// in flight per workgroup to cover the memory latency)
+constexpr int kKey32BatchLds = 8;
+constexpr int kKey32BatchMem = 32;
+constexpr int kExpBins = 4096;  // the sign/exponent count table (top 12 bits)
 
-// LDS of the selection after the exponent table has been read (it may
-// overlay that table).
-template <int NT>
+// LDS of the selection over at most MAXN keys after the exponent table has
+// been read (it may overlay that table).
+template <int NT, int MAXN>
 struct Key32Scratch {
-    static constexpr int kRounds = (kKey32MaxLen + NT - 1) / NT;
+    static constexpr int kRounds = (MAXN + NT - 1) / NT;
     uint32_t hist[3][256];
     uint32_t cnt[kRounds * (NT / 64)];
     uint32_t cnt_tie[kRounds * (NT / 64)];
@@ -70,31 +73,78 @@ __device__ __noinline__ double exact_score_row(const uint16_t *row, const double
     return v;
 }
 
-// Top words of keys j0 + u * NT + threadIdx.x, u < kKey32Batch (slots past n
-// re-read key 0; callers ignore them).
+// Exclusive prefix sums, in place, of a[0..n) and b[0..n) over the whole
+// workgroup (each thread scans a contiguous segment).  Ends with a barrier.
 template <int NT>
+__device__ void block_exclusive_scan2(uint32_t *a, uint32_t *b, int n,
+                                      uint32_t (&wsum)[2][NT / 64]) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int m = (n + NT - 1) / NT;
+    const int s0 = min(tid * m, n), s1 = min(s0 + m, n);
+    uint32_t sa = 0, sb = 0;
+    for (int i = s0; i < s1; ++i) {
+        sa += a[i];
+        sb += b[i];
+    }
+    const uint32_t ia = wave_incl_scan(sa), ib = wave_incl_scan(sb);
+    if (lane == 63) {
+        wsum[0][wave] = ia;
+        wsum[1][wave] = ib;
+    }
+    __syncthreads();
+    uint32_t oa = ia - sa, ob = ib - sb;
+    for (int w = 0; w < wave; ++w) {
+        oa += wsum[0][w];
+        ob += wsum[1][w];
+    }
+    for (int i = s0; i < s1; ++i) {
+        const uint32_t va = a[i], vb = b[i];
+        a[i] = oa;
+        b[i] = ob;
+        oa += va;
+        ob += vb;
+    }
+    __syncthreads();
+}
+
+// Top words of keys j0 + u * NT + threadIdx.x, u < B (slots past n re-read
+// key 0; callers ignore them).
+template <int NT, int B>
 __device__ __forceinline__ void key32_batch(const uint32_t *key, int n, int j0,
-                                            uint32_t (&x)[kKey32Batch]) {
+                                            uint32_t (&x)[B]) {
 #pragma unroll
-    for (int u = 0; u < kKey32Batch; ++u) {
+    for (int u = 0; u < B; ++u) {
         const int j = j0 + u * NT + (int)threadIdx.x;
         x[u] = key[j < n ? j : 0];
     }
 }
 
+// f(j0, x) for every batch of keys j0 + u * NT + threadIdx.x (u < B), in
+// order.  (Issuing the next batch's loads before f works on the current one
+// measured no faster: the sweeps are bound by their per-key work.)
+template <int NT, int B, class F>
+__device__ __forceinline__ void key32_sweep(const uint32_t *key, int n, F f) {
+    for (int j0 = 0; j0 < n; j0 += B * NT) {
+        uint32_t x[B];
+        key32_batch<NT, B>(key, n, j0, x);
+        f(j0, x);
+    }
+}
+
 // Write out[0..k): the min(k, n) largest keys of the pair, their indices
-// ascending, then -1.  key[0..n): top words of the order keys (LDS); fine:
-// the 4096-bin count of their top 12 bits (LDS, may share memory with sc);
-// row0: the pair's first K row (bf16 rows of kHeadDim) and qp: its first
-// query head, for the low words.  Every thread of the NT-thread workgroup
-// calls this; it ends with a barrier after the last write of `out`.
-// Requires 1 <= k and n <= kKey32MaxLen.
-template <int NT>
+// ascending, then -1.  key[0..n): top words of the order keys (LDS or global
+// memory); fine: the kExpBins-bin count of their top 12 bits (LDS, may share
+// memory with sc); row0: the pair's first K row (bf16 rows of kHeadDim) and
+// qp: its first query head, for the low words.  Every thread of the
+// NT-thread workgroup calls this; it ends with a barrier after the last
+// write of `out`.  Requires 1 <= k and n <= MAXN.  B: keys per thread read
+// together (kKey32BatchLds or kKey32BatchMem).
+template <int NT, int MAXN, int B>
 __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
-                             const uint32_t *fine, Key32Scratch<NT> &sc, const uint16_t *row0,
-                             const uint16_t *qp, int gqa) {
+                             const uint32_t *fine, Key32Scratch<NT, MAXN> &sc,
+                             const uint16_t *row0, const uint16_t *qp, int gqa) {
     constexpr int NW = NT / 64;
-    constexpr int B = kKey32Batch;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int keff = min(k, n);
@@ -137,14 +187,12 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
         uint32_t *h = sc.hist[buf];
         const int nbuf = buf == 2 ? 0 : buf + 1;
         const uint32_t dmask = (1u << width) - 1u;
-        for (int j0 = 0; j0 < n; j0 += B * NT) {
-            uint32_t x[B];
-            key32_batch<NT>(key, n, j0, x);
+        key32_sweep<NT, B>(key, n, [&](int j0, const uint32_t (&x)[B]) {
 #pragma unroll
             for (int u = 0; u < B; ++u)
                 if (j0 + u * NT + tid < n && (x[u] & pmask) == prefix)
                     atomicAdd(&h[(x[u] >> lo) & dmask], 1u);
-        }
+        });
         for (int i = tid; i < 256; i += NT) sc.hist[nbuf][i] = 0u;
         __syncthreads();
 #pragma unroll
@@ -182,9 +230,7 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
         for (int llo = 24;; llo -= 8) {
             uint32_t *h = sc.hist[buf];
             const int nbuf = buf == 2 ? 0 : buf + 1;
-            for (int j0 = 0; j0 < n; j0 += B * NT) {
-                uint32_t x[B];
-                key32_batch<NT>(key, n, j0, x);
+            key32_sweep<NT, B>(key, n, [&](int j0, const uint32_t (&x)[B]) {
 #pragma unroll
                 for (int u = 0; u < B; ++u) {
                     const int j = j0 + u * NT + tid;
@@ -194,7 +240,7 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
                         if ((w & lmask) == lprefix) atomicAdd(&h[(w >> llo) & 255u], 1u);
                     }
                 }
-            }
+            });
             for (int i = tid; i < 256; i += NT) sc.hist[nbuf][i] = 0u;
             __syncthreads();
 #pragma unroll
@@ -224,9 +270,7 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
     };
 
     // ordered compaction: counts per (round, wave), a scan, then the writes
-    for (int j0 = 0; j0 < n; j0 += B * NT) {
-        uint32_t x[B];
-        key32_batch<NT>(key, n, j0, x);
+    key32_sweep<NT, B>(key, n, [&](int j0, const uint32_t (&x)[B]) {
 #pragma unroll
         for (int u = 0; u < B; ++u) {
             const int r = j0 / NT + u;
@@ -239,12 +283,10 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
                 sc.cnt_tie[r * NW + wave] = (uint32_t)__popcll(mt);
             }
         }
-    }
+    });
     __syncthreads();
     block_exclusive_scan2<NT>(sc.cnt, sc.cnt_tie, R * NW, sc.wsum);
-    for (int j0 = 0; j0 < n; j0 += B * NT) {
-        uint32_t x[B];
-        key32_batch<NT>(key, n, j0, x);
+    key32_sweep<NT, B>(key, n, [&](int j0, const uint32_t (&x)[B]) {
 #pragma unroll
         for (int u = 0; u < B; ++u) {
             const int r = j0 / NT + u;
@@ -256,7 +298,7 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
             const uint32_t tie_before = sc.cnt_tie[r * NW + wave] + rank_below(mt);
             if (cl == 2 || (cl == 1 && tie_before < krem)) out[gt_before + min(tie_before, krem)] = j;
         }
-    }
+    });
     __syncthreads();
 }
 

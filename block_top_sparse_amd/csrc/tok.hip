@@ -4,12 +4,13 @@
 //
 //   kernel 1 (k_tok_score): the group score of every key, fp64, streamed
 //            straight from K in tiles spread over the chip (the scoring loop
-//            of scoring.h), and each tile's sign/exponent counts;
-//   kernel 2 (k_tok_select_attend): the k best tokens (select_stream.h, the
-//            scores read from memory, its first pass taken from the counts),
-//            then attention over those tokens' K/V (MFMA,
-//            online softmax), split over several workgroups when there are
-//            fewer pairs than CUs, the splits combined in-kernel.
+//            of scoring.h); the top 32 bits of each score's order key
+//            written out, and each tile's sign/exponent counts;
+//   kernel 2 (k_tok_select_attend): the k best tokens (select_key32.h over
+//            those words, read from memory, low words recomputed from K
+//            only where they decide), then attention over those tokens' K/V
+//            (MFMA, online softmax), split over several workgroups when
+//            there are fewer pairs than CUs, the splits combined in-kernel.
 //
 // With at least as many pairs as CUs, a context of at most 32768 tokens and
 // at most 2048 kept, the whole step runs in one kernel (k_tok_step), one
@@ -24,18 +25,19 @@
 #include "attn_impl.h"
 #include "scoring.h"
 #include "select_key32.h"
-#include "select_stream.h"
 
 namespace kin {
 
 constexpr int kTokScoreThreads = 512;
 
-// Kernel 1: the group score of every key of one tile of a pair's tokens,
-// written out, and the tile's sign/exponent counts (the selection's first
-// pass) written to `tables` ([pair][tile][kTableWords]).  Also clears the
+// Kernel 1: the group score of every key of one tile of a pair's tokens;
+// the top word of its order key written to `keys` ([pair][t_cap]), the
+// score itself to `scores` when asked for, and the tile's sign/exponent
+// counts written to `tables` ([pair][tile][kExpBins]).  Also clears the
 // pair's arrival word for kernel 2's combine.
-__global__ __launch_bounds__(kTokScoreThreads) void k_tok_score(AttnArgs a, double *scores,
-                                                               int tile_rows, uint32_t *tables,
+__global__ __launch_bounds__(kTokScoreThreads) void k_tok_score(AttnArgs a, uint32_t *keys,
+                                                               double *scores, int tile_rows,
+                                                               uint32_t *tables,
                                                                uint64_t *ctrl_zero) {
     constexpr int NW = kTokScoreThreads / 64;
     __shared__ NewestLds<NW> nl;  // not used: no summary to rebuild
@@ -46,39 +48,36 @@ __global__ __launch_bounds__(kTokScoreThreads) void k_tok_score(AttnArgs a, doub
     __syncthreads();
     const int j_beg = tile * tile_rows;
     const int j_end = min(a.ctx_len, j_beg + tile_rows);
-    double *sp = scores + (size_t)pair * a.t_cap;
+    uint32_t *kp = keys + (size_t)pair * a.t_cap;
+    double *sp = scores ? scores + (size_t)pair * a.t_cap : nullptr;
     // the scores of a pair fall into a few sign/exponent bins: one atomic per
-    // distinct bin of the wave, not one per key (the coarse table is summed
-    // from the fine one at the end)
+    // distinct bin of the wave, not one per key
     if (j_beg < j_end)
         score_blocks<NW, false>(a, const_cast<void *>(a.K), a.t_cap, pair, j_beg, j_end, nl,
                                 [&](int j, double v) {
-            sp[j] = v;
-            count_wave_aggregated(fine, (uint32_t)(order_key(v) >> 52), true);
+            const uint32_t top = (uint32_t)(order_key(v) >> 32);
+            kp[j] = top;
+            count_wave_aggregated(fine, top >> 20, true);
+            if (sp) sp[j] = v;  // scores are an optional output
         });
     __syncthreads();
-    uint32_t *t = tables + ((size_t)pair * gridDim.x + tile) * kTableWords;
-    for (int i = threadIdx.x; i < 256; i += kTokScoreThreads) {
-        uint32_t c = 0;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) c += fine[16 * i + r];
-        t[i] = c;
-    }
-    for (int i = threadIdx.x; i < 4096; i += kTokScoreThreads) t[256 + i] = fine[i];
+    uint32_t *t = tables + ((size_t)pair * gridDim.x + tile) * kExpBins;
+    for (int i = threadIdx.x; i < kExpBins; i += kTokScoreThreads) t[i] = fine[i];
 }
 
 template <int NT>
 struct TokLds {
     int32_t sel[kTokIdxCap];
     union {
-        StreamSelectLds<NT> s;
-        MergeLds<NT / 64> m;
+        uint32_t fine[kExpBins];           // the pair's sign/exponent counts
+        Key32Scratch<NT, kTokMaxLen> s;    // once they have been read
+        MergeLds<NT / 64> m;               // after the selection
     } u;
 };
 
 __global__ __launch_bounds__(kStepThreads) void k_tok_select_attend(AttnArgs a,
-                                                                   const double *__restrict__ scores,
-                                                                   int n_cap, int32_t *idx_out,
+                                                                   const uint32_t *__restrict__ keys,
+                                                                   int32_t *idx_out,
                                                                    uint64_t *ctrl,
                                                                    const uint32_t *tables,
                                                                    int ntables) {
@@ -88,9 +87,22 @@ __global__ __launch_bounds__(kStepThreads) void k_tok_select_attend(AttnArgs a,
     int pair, split;
     split_slot(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, gridDim.y, pair, split);
 
+    // the pair's counts: its tiles' tables summed
+    const uint32_t *tp = tables + (size_t)pair * ntables * kExpBins;
+    for (int i = threadIdx.x; i < kExpBins; i += kStepThreads) {
+        uint32_t c = 0;
+        for (int t = 0; t < ntables; ++t) c += tp[(size_t)t * kExpBins + i];
+        lds.u.fine[i] = c;
+    }
+    __syncthreads();
     // every split of a pair repeats the selection (it ends with a barrier)
-    select_stream<kStepThreads>(scores + (size_t)pair * n_cap, a.ctx_len, a.k, lds.sel, lds.u.s,
-                                tables + (size_t)pair * ntables * kTableWords, ntables);
+    const int b = pair / a.hkv, g = pair % a.hkv;
+    const uint16_t *row0 = static_cast<const uint16_t *>(a.K) + (size_t)pair * a.t_cap * kHeadDim;
+    const uint16_t *qp = static_cast<const uint16_t *>(a.q) +
+                         ((size_t)b * a.hkv * a.gqa + (size_t)g * a.gqa) * kHeadDim;
+    select_key32<kStepThreads, kTokMaxLen, kKey32BatchMem>(keys + (size_t)pair * a.t_cap,
+                                                           a.ctx_len, a.k, lds.sel, lds.u.fine,
+                                                           lds.u.s, row0, qp, a.gqa);
     if (split == 0)
         for (int i = threadIdx.x; i < a.k; i += kStepThreads)
             idx_out[(size_t)pair * a.k + i] = lds.sel[i];
@@ -122,7 +134,7 @@ __global__ __launch_bounds__(kStepThreads) void k_tok_select_attend(AttnArgs a,
 // recomputed only for keys that share the k-th key's top word); then the
 // attention over the kept tokens and the merge of the waves.  The fp64
 // scores are written only when asked for.
-constexpr int kTokStepMaxLen = kKey32MaxLen;
+constexpr int kTokStepMaxLen = 32768;
 constexpr int kTokStepMaxK = kStepIdxCap;
 
 __global__ __launch_bounds__(kStepThreads) void k_tok_step(AttnArgs a, double *scores,
@@ -133,14 +145,14 @@ __global__ __launch_bounds__(kStepThreads) void k_tok_step(AttnArgs a, double *s
         MergeLds<NW> m;  // after the selection
     } u;
     __shared__ union {
-        uint32_t fine[4096];
-        Key32Scratch<kStepThreads> s;  // once the table has been read
+        uint32_t fine[kExpBins];
+        Key32Scratch<kStepThreads, kTokStepMaxLen> s;  // once the table has been read
     } v;
     __shared__ int32_t sel[kTokStepMaxK];
     __shared__ NewestLds<NW> nl;  // not used: no summary to rebuild
     const int pair = blockIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    for (int i = threadIdx.x; i < 4096; i += kStepThreads) v.fine[i] = 0u;
+    for (int i = threadIdx.x; i < kExpBins; i += kStepThreads) v.fine[i] = 0u;
     __syncthreads();
     const int L = a.ctx_len;
     double *sp = scores ? scores + (size_t)pair * a.t_cap : nullptr;
@@ -156,7 +168,8 @@ __global__ __launch_bounds__(kStepThreads) void k_tok_step(AttnArgs a, double *s
     const uint16_t *row0 = static_cast<const uint16_t *>(a.K) + (size_t)pair * a.t_cap * kHeadDim;
     const uint16_t *qp = static_cast<const uint16_t *>(a.q) +
                          ((size_t)b * a.hkv * a.gqa + (size_t)g * a.gqa) * kHeadDim;
-    select_key32<kStepThreads>(u.key, L, a.k, sel, v.fine, v.s, row0, qp, a.gqa);
+    select_key32<kStepThreads, kTokStepMaxLen, kKey32BatchLds>(u.key, L, a.k, sel, v.fine, v.s,
+                                                               row0, qp, a.gqa);
     for (int i = threadIdx.x; i < a.k; i += kStepThreads) idx_out[(size_t)pair * a.k + i] = sel[i];
     // the keys are dead: the merge area overlays them
     const TokenRuns runs{(int64_t)pair * a.t_cap, sel, a.k, L};
@@ -190,17 +203,17 @@ static void tok_tiles(const Geo &g, int num_cu, int &tiles, int &rows) {
     tiles = (g.ctx_len + rows - 1) / rows;
 }
 
-// Workspace of the token step: split partials, arrival words, scores, count
-// tables (in that order, each 256-byte aligned).
+// Workspace of the two-kernel token step: split partials, arrival words,
+// the keys' top words, count tables (in that order, each 256-byte aligned).
 struct TokWs {
-    size_t ctrl, scores, tables, total;
+    size_t ctrl, keys, tables, total;
 };
 static TokWs tok_ws(const Geo &g, int nsplit, int tiles) {
     TokWs w;
     w.ctrl = align256(ws_for(g, nsplit));
-    w.scores = align256(w.ctrl + (nsplit > 1 ? (size_t)g.pairs * sizeof(uint64_t) : 0));
-    w.tables = align256(w.scores + (size_t)g.pairs * g.t_cap * sizeof(double));
-    w.total = w.tables + (size_t)g.pairs * tiles * kTableWords * sizeof(uint32_t);
+    w.keys = align256(w.ctrl + (nsplit > 1 ? (size_t)g.pairs * sizeof(uint64_t) : 0));
+    w.tables = align256(w.keys + (size_t)g.pairs * g.t_cap * sizeof(uint32_t));
+    w.total = w.tables + (size_t)g.pairs * tiles * kExpBins * sizeof(uint32_t);
     return w;
 }
 
@@ -244,16 +257,17 @@ hipError_t launch_tok_step(const Geo &g0, const void *q, const void *K, const vo
     const TokWs wl = tok_ws(g, p.nsplit, tiles);
     char *w = static_cast<char *>(ws);
     uint64_t *ctrl = p.nsplit > 1 ? reinterpret_cast<uint64_t *>(w + wl.ctrl) : nullptr;
-    double *sc = scores ? scores : reinterpret_cast<double *>(w + wl.scores);
+    uint32_t *keys = reinterpret_cast<uint32_t *>(w + wl.keys);
     uint32_t *tables = reinterpret_cast<uint32_t *>(w + wl.tables);
     AttnArgs a;
     fill_args(a, g, p, q, K, V, nullptr, k, out, ws);
     // kernel 1: the scores straight from K (the keys are the summaries)
-    k_tok_score<<<dim3(tiles, g.pairs), kTokScoreThreads, 0, s>>>(a, sc, rows, tables, ctrl);
+    k_tok_score<<<dim3(tiles, g.pairs), kTokScoreThreads, 0, s>>>(a, keys, scores, rows, tables,
+                                                                  ctrl);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 grid(p.nsplit, g.pairs);
-    k_tok_select_attend<<<grid, kStepThreads, 0, s>>>(a, sc, g.t_cap, idx, ctrl, tables, tiles);
+    k_tok_select_attend<<<grid, kStepThreads, 0, s>>>(a, keys, idx, ctrl, tables, tiles);
     return hipGetLastError();
 }
 

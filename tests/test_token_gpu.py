@@ -185,17 +185,20 @@ def _plant_near_tie(inp, w, b, g, k, exact, above=False):
     inp["K"][b, g, c] = row.cuda()
 
 
-def test_token_single_kernel_near_ties_below_the_top_word():
-    """256 pairs (the one-kernel step) with planted keys whose scores equal
-    the k-th score in the top 32 bits of the order key (near ties: they
-    differ below; exact ties: they do not): the recomputed low words must
-    order them as the oracle does."""
-    w = Workload("tok-single-near", batch=64, hq=16, hkv=4, ctx_len=2000, block=1, topk=100,
-                 dtype="bf16", seed=4244, t_cap=2048)
+@pytest.mark.parametrize("batch", [64, 2], ids=["one-kernel", "two-kernel"])
+def test_token_near_ties_below_the_top_word(batch):
+    """Planted keys whose scores equal the k-th score in the top 32 bits of
+    the order key (near ties: they differ below; exact ties: they do not):
+    the recomputed low words must order them as the oracle does, in the
+    one-kernel step (256 pairs: the top words in LDS) and in the two-kernel
+    step (8 pairs: the top words handed over in memory)."""
+    w = Workload(f"tok-near-b{batch}", batch=batch, hq=16, hkv=4, ctx_len=2000, block=1,
+                 topk=100, dtype="bf16", seed=4244, t_cap=2048)
     inp = synth.make_inputs(w, device="cuda", tail_fill=float("nan"))
+    last = batch - 1
     # (sequence, KV head, exact tie, planted key just above the k-th)
-    planted = [(0, 0, False, False), (0, 1, True, False), (31, 2, False, True),
-               (63, 3, True, False), (63, 0, False, True)]
+    planted = [(0, 0, False, False), (0, 1, True, False), (last, 2, False, True),
+               (last, 3, True, False), (last, 0, False, True)]
     for b, g, exact, above in planted:
         _plant_near_tie(inp, w, b, g, 100, exact, above)
     idx, out, sc = run_token(w, inp, 100)
