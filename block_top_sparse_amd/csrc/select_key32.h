@@ -121,8 +121,7 @@ __device__ __forceinline__ void key32_batch(const uint32_t *key, int n, int j0,
 }
 
 // f(j0, x) for every batch of keys j0 + u * NT + threadIdx.x (u < B), in
-// order.  (Issuing the next batch's loads before f works on the current one
-// measured no faster: the sweeps are bound by their per-key work.)
+// order.
 template <int NT, int B, class F>
 __device__ __forceinline__ void key32_sweep(const uint32_t *key, int n, F f) {
     for (int j0 = 0; j0 < n; j0 += B * NT) {
@@ -258,10 +257,48 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
         }
     }
 
+    if (resolved) {
+        // settled by the top words: kept = top word >= prefix (zeros below
+        // its mask); no ties, no low words.  Lane u of a wave carries the
+        // count (then the offset) of round j0 / NT + u of the batch, so a
+        // round costs a compare, a ballot and a bit count.
+        static_assert(B <= 64, "one lane per round of a batch");
+        key32_sweep<NT, B>(key, n, [&](int j0, const uint32_t (&x)[B]) {
+            const int r0 = j0 / NT;
+            const bool full = j0 + B * NT <= n;  // uniform: no bound checks
+            uint32_t mine = 0;
+#pragma unroll
+            for (int u = 0; u < B; ++u) {
+                const bool keep = (full || j0 + u * NT + tid < n) && x[u] >= prefix;
+                const uint32_t c = (uint32_t)__popcll(__ballot(keep));
+                mine = lane == u ? c : mine;
+            }
+            if (lane < B && r0 + lane < R) {
+                sc.cnt[(r0 + lane) * NW + wave] = mine;
+                sc.cnt_tie[(r0 + lane) * NW + wave] = 0u;
+            }
+        });
+        __syncthreads();
+        block_exclusive_scan2<NT>(sc.cnt, sc.cnt_tie, R * NW, sc.wsum);
+        key32_sweep<NT, B>(key, n, [&](int j0, const uint32_t (&x)[B]) {
+            const int r0 = j0 / NT;
+            const bool full = j0 + B * NT <= n;
+            const uint32_t base = lane < B && r0 + lane < R ? sc.cnt[(r0 + lane) * NW + wave] : 0u;
+#pragma unroll
+            for (int u = 0; u < B; ++u) {
+                const int j = j0 + u * NT + tid;
+                const bool keep = (full || j < n) && x[u] >= prefix;
+                const uint32_t pos = lane_value(base, u) + rank_below(__ballot(keep));
+                if (keep) out[pos] = j;
+            }
+        });
+        __syncthreads();
+        return;
+    }
+
     // Class of key j: 2 = kept for sure, 1 = equal in all 64 bits to the
     // k-th key (the first krem of these in index order are kept), 0 = not.
     auto cls = [&](int j, uint32_t x) -> int {
-        if (resolved) return x >= prefix ? 2 : 0;  // prefix: zeros below its mask
         if (x != prefix) return x > prefix ? 2 : 0;
         const uint32_t w =
             (uint32_t)order_key(exact_score_row(row0 + (size_t)j * kHeadDim, sc.qsum));

@@ -87,13 +87,20 @@ __global__ __launch_bounds__(kStepThreads) void k_tok_select_attend(AttnArgs a,
     int pair, split;
     split_slot(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, gridDim.y, pair, split);
 
-    // the pair's counts: its tiles' tables summed
-    const uint32_t *tp = tables + (size_t)pair * ntables * kExpBins;
-    for (int i = threadIdx.x; i < kExpBins; i += kStepThreads) {
-        uint32_t c = 0;
-        for (int t = 0; t < ntables; ++t) c += tp[(size_t)t * kExpBins + i];
-        lds.u.fine[i] = c;
+    // the pair's counts: its tiles' tables summed (one table's bins of this
+    // thread loaded together)
+    constexpr int kBinsPerThread = kExpBins / kStepThreads;
+    const uint32_t *tp = tables + (size_t)pair * ntables * kExpBins + threadIdx.x;
+    uint32_t c[kBinsPerThread] = {};
+    for (int t = 0; t < ntables; ++t) {
+        uint32_t v[kBinsPerThread];
+#pragma unroll
+        for (int e = 0; e < kBinsPerThread; ++e) v[e] = tp[(size_t)t * kExpBins + e * kStepThreads];
+#pragma unroll
+        for (int e = 0; e < kBinsPerThread; ++e) c[e] += v[e];
     }
+#pragma unroll
+    for (int e = 0; e < kBinsPerThread; ++e) lds.u.fine[threadIdx.x + e * kStepThreads] = c[e];
     __syncthreads();
     // every split of a pair repeats the selection (it ends with a barrier)
     const int b = pair / a.hkv, g = pair % a.hkv;
