@@ -120,6 +120,27 @@ __device__ __forceinline__ void key32_batch(const uint32_t *key, int n, int j0,
     }
 }
 
+// coarse[i] = fine[16 i] + ... + fine[16 i + 15] for the kExpBins / 16
+// coarse bins, by the whole NT-thread workgroup without LDS bank conflicts:
+// consecutive lanes read consecutive bins, and each 16-lane row adds its 16
+// bins with DPP row shifts (lane 15 of the row ends with the sum).  Every
+// thread calls this; a barrier must follow before coarse is read.
+template <int NT>
+__device__ __forceinline__ void coarse_from_fine(const uint32_t *fine, uint32_t *coarse) {
+    static_assert(kExpBins % NT == 0 && NT % 64 == 0, "whole waves over the table");
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i0 = 0; i0 < kExpBins; i0 += NT) {
+        const int i = i0 + (int)threadIdx.x;
+        uint32_t v = fine[i];
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+        if ((lane & 15) == 15) coarse[i >> 4] = v;
+    }
+}
+
 // f(j0, x) for every batch of keys j0 + u * NT + threadIdx.x (u < B), in
 // order.
 template <int NT, int B, class F>
@@ -138,10 +159,11 @@ __device__ __forceinline__ void key32_sweep(const uint32_t *key, int n, F f) {
 // qp: its first query head, for the low words.  Every thread of the
 // NT-thread workgroup calls this; it ends with a barrier after the last
 // write of `out`.  Requires 1 <= k and n <= MAXN.  B: keys per thread read
-// together (kKey32BatchLds or kKey32BatchMem).
+// together (kKey32BatchLds or kKey32BatchMem); coarse: kExpBins / 16 words
+// of LDS apart from fine and sc.
 template <int NT, int MAXN, int B>
 __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
-                             const uint32_t *fine, Key32Scratch<NT, MAXN> &sc,
+                             const uint32_t *fine, uint32_t *coarse, Key32Scratch<NT, MAXN> &sc,
                              const uint16_t *row0, const uint16_t *qp, int gqa) {
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -156,18 +178,14 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
         return;
     }
 
-    // sign and exponent of the k-th key: coarse bins (16 fine bins each)
-    // summed here, then the 16 fine bins under the chosen one
+    // sign and exponent of the k-th key: the coarse bins (16 fine bins
+    // each), then the 16 fine bins under the chosen one
+    coarse_from_fine<NT>(fine, coarse);
+    __syncthreads();
     uint32_t krem = (uint32_t)keff;
     uint32_t c[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const uint32_t *f = fine + 16 * (255 - 4 * lane - r);
-        uint32_t s = 0;
-#pragma unroll
-        for (int t = 0; t < 16; ++t) s += f[t];
-        c[r] = s;
-    }
+    for (int r = 0; r < 4; ++r) c[r] = coarse[255 - 4 * lane - r];
     const BinHit h1 = find_bin(c, krem, 255u, lane);
     krem -= h1.above;
 #pragma unroll

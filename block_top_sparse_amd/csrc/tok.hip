@@ -68,6 +68,7 @@ __global__ __launch_bounds__(kTokScoreThreads) void k_tok_score(AttnArgs a, uint
 template <int NT>
 struct TokLds {
     int32_t sel[kTokIdxCap];
+    uint32_t coarse[kExpBins / 16];
     union {
         uint32_t fine[kExpBins];           // the pair's sign/exponent counts
         Key32Scratch<NT, kTokMaxLen> s;    // once they have been read
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(kStepThreads) void k_tok_select_attend(AttnArgs a,
                          ((size_t)b * a.hkv * a.gqa + (size_t)g * a.gqa) * kHeadDim;
     select_key32<kStepThreads, kTokMaxLen, kKey32BatchMem>(keys + (size_t)pair * a.t_cap,
                                                            a.ctx_len, a.k, lds.sel, lds.u.fine,
-                                                           lds.u.s, row0, qp, a.gqa);
+                                                           lds.coarse, lds.u.s, row0, qp, a.gqa);
     if (split == 0)
         for (int i = threadIdx.x; i < a.k; i += kStepThreads)
             idx_out[(size_t)pair * a.k + i] = lds.sel[i];
@@ -156,6 +157,7 @@ __global__ __launch_bounds__(kStepThreads) void k_tok_step(AttnArgs a, double *s
         Key32Scratch<kStepThreads, kTokStepMaxLen> s;  // once the table has been read
     } v;
     __shared__ int32_t sel[kTokStepMaxK];
+    __shared__ uint32_t coarse[kExpBins / 16];
     __shared__ NewestLds<NW> nl;  // not used: no summary to rebuild
     const int pair = blockIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -175,8 +177,8 @@ __global__ __launch_bounds__(kStepThreads) void k_tok_step(AttnArgs a, double *s
     const uint16_t *row0 = static_cast<const uint16_t *>(a.K) + (size_t)pair * a.t_cap * kHeadDim;
     const uint16_t *qp = static_cast<const uint16_t *>(a.q) +
                          ((size_t)b * a.hkv * a.gqa + (size_t)g * a.gqa) * kHeadDim;
-    select_key32<kStepThreads, kTokStepMaxLen, kKey32BatchLds>(u.key, L, a.k, sel, v.fine, v.s,
-                                                               row0, qp, a.gqa);
+    select_key32<kStepThreads, kTokStepMaxLen, kKey32BatchLds>(u.key, L, a.k, sel, v.fine, coarse,
+                                                               v.s, row0, qp, a.gqa);
     for (int i = threadIdx.x; i < a.k; i += kStepThreads) idx_out[(size_t)pair * a.k + i] = sel[i];
     // the keys are dead: the merge area overlays them
     const TokenRuns runs{(int64_t)pair * a.t_cap, sel, a.k, L};
