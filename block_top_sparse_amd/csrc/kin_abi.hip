@@ -287,10 +287,14 @@ static kin_status decode_step(const kin::Geo &g, const void *q, const void *K, c
         return launched(kin::launch_select_attend(g, p, q, K, V, sc, k, idx, out, ws,
                                                   next_epoch(), s, S),
                         "kin_sparse_decode_step");
-    // the first kernel also clears the second kernel's arrival words
+    // the bf16 scoring kernel also clears the second kernel's arrival words;
+    // the fp32 one does not, so there the splits count with a round tag
+    const bool clears = g.dtype == KIN_BF16;
     hipError_t e = kin::launch_update_and_score(g, q, K, S, sc, cu, s, newest_only,
-                                                kin::step_ctrl(g, p, ws));
-    if (e == hipSuccess) e = kin::launch_select_attend(g, p, q, K, V, sc, k, idx, out, ws, 0u, s);
+                                                clears ? kin::step_ctrl(g, p, ws) : nullptr);
+    if (e == hipSuccess)
+        e = kin::launch_select_attend(g, p, q, K, V, sc, k, idx, out, ws,
+                                      clears ? 0u : next_epoch(), s);
     return launched(e, "kin_sparse_decode_step");
 }
 

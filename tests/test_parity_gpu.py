@@ -229,6 +229,39 @@ def test_two_kernel_step_without_scores_buffer(case):
     say(f"  ok {r}")
 
 
+F32_SPLIT = [
+    # name, batch, hq, hkv, ctx, block, k, dtype, t_cap  (few pairs, several splits)
+    ("f32split-g1-b16-k292", 3, 2, 2, 4730, 16, 292, "f32", 4793),
+    ("f32split-g4-b128-k14", 2, 8, 2, 5401, 128, 14, "f32", 5500),
+    ("f32split-g5-b16-keepall", 3, 10, 2, 5936, 16, 371, "f32", 5999),
+]
+
+
+@pytest.mark.parametrize("case", F32_SPLIT, ids=[c[0] for c in F32_SPLIT])
+def test_f32_two_kernel_step_splits_on_a_stale_workspace(case):
+    """The fp32 two-kernel step with its attention split over several
+    workgroups per pair: the splits' arrivals are counted with a round tag,
+    so a workspace holding bytes of earlier calls (here all ones, then the
+    first call's own) gives the same result."""
+    name, b, hq, hkv, L, B, k, dt, cap = case
+    w = Workload(name, batch=b, hq=hq, hkv=hkv, ctx_len=L, block=B, topk=k, dtype=dt,
+                 seed=zlib.crc32(name.encode()) % 10000, t_cap=cap)
+    say(f"case {name}: {w.describe()}")
+    inp = gpu_inputs(w)
+    bufs = LayerBuffers(w, k=k)
+    assert bufs.ws is not None, "the plan must split (a workspace is needed)"
+    bufs.ws.fill_(0xFF)
+    step = run_gpu(w, inp, step=True, bufs=bufs)
+    r = check_sequences(w, inp, step, range(b))
+    first = (step.idx.clone(), step.out.clone())
+    again = run_gpu(w, inp, step=True, bufs=bufs)  # the workspace as the first call left it
+    assert torch.equal(again.idx, first[0])
+    assert torch.equal(bits(again.out), bits(first[1]))
+    quiet = run_gpu(w, inp, step=True, no_scores=True)
+    assert torch.equal(bits(quiet.out), bits(first[1]))
+    say(f"  ok {r}")
+
+
 def test_tiny_workload_full_parity():
     w = workloads.TINY
     say(f"workload {w.name}")
