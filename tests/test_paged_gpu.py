@@ -185,8 +185,9 @@ PAGED = [
 ]
 
 
-@pytest.mark.parametrize("case", PAGED, ids=[c[0] for c in PAGED])
-def test_paged_step_against_oracle(case):
+def check_paged_case(case):
+    """One paged, variable-length step against the oracle, then the same
+    tokens in contiguous caches (bit for bit) and without a scores buffer."""
     name, batch, hkv, gqa, block, ps, L, k, kind = case
     c = Case(name, batch, hkv, gqa, block, ps, L, k, kind)
     say(f"case {name}: pairs {batch * hkv}, lens {c.lens[:12]}")
@@ -202,6 +203,11 @@ def test_paged_step_against_oracle(case):
         assert torch.equal(bits(r_ns[0][b, :, :c.nb(b)]), bits(r_paged[0][b, :, :c.nb(b)])), \
             f"no scores: S, seq {b}"
     say(f"case {name}: max err {err:.3e}")
+
+
+@pytest.mark.parametrize("case", PAGED, ids=[c[0] for c in PAGED])
+def test_paged_step_against_oracle(case):
+    check_paged_case(case)
 
 
 def test_paged_table_entries_past_the_length_are_not_used():

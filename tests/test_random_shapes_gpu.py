@@ -1,11 +1,11 @@
 """GPU parity on seeded random shapes: the decode steps (block, token-level,
-Quest-style) over drawn batch sizes, GQA ratios, block sizes, context
-lengths and budgets, so that every launch form the library picks (one
-kernel with 8 or 4 waves, two kernels with split attention, the separate
-calls past 2048 kept blocks, fp32) meets shapes no hand-written case names.
-Each case checks a few sequences against the oracle with the rules of the
-other parity tests, and the call without a scores buffer bit for bit
-against the call with one.
+Quest-style, paged with variable lengths, shared prompts) over drawn batch
+sizes, GQA ratios, block and page sizes, context lengths and budgets, so
+that every launch form the library picks (one kernel with 8 or 4 waves,
+two kernels with split attention, the separate calls past 2048 kept
+blocks, fp32) meets shapes no hand-written case names.  Each case checks
+sequences against the oracle with the rules of the other parity tests, and
+the call without a scores buffer bit for bit against the call with one.
 """
 import random
 import zlib
@@ -19,6 +19,8 @@ from block_top_sparse_amd import synth
 from block_top_sparse_amd.workloads import Workload
 
 from parity_util import GAP_MIN, TOL, bits, check_sequences, gpu_inputs, run_gpu, say
+from test_paged_gpu import check_paged_case
+from test_shared_gpu import check_shared_case
 
 pytestmark = pytest.mark.gpu
 
@@ -201,3 +203,57 @@ def test_random_quest_step(case):
     assert torch.equal(idx2, idx)
     assert torch.equal(bits(out2), bits(out))
     say("  ok")
+
+
+def _draw_paged_case(rng, i):
+    kind = rng.choice(["few", "few", "many", "many4w"])
+    block = rng.choice([16, 32, 64, 128])
+    gqa = rng.choice([1, 2, 3, 4, 8, 16])
+    if kind == "few":
+        batch, hkv, max_len = rng.randint(1, 6), rng.choice([1, 2, 4]), rng.randint(1, 6000)
+    elif kind == "many":  # at least as many pairs as CUs: one kernel
+        hkv = 8
+        batch, max_len = 32 + rng.randint(0, 6), rng.randint(1, 2500)
+    else:  # two pairs per CU: the 4-wave shape
+        hkv, block = 8, rng.choice([16, 32, 64])
+        batch, max_len = 64 + rng.randint(0, 4), rng.randint(1, 1500)
+    page = max(16, block) << rng.randint(0, 3)
+    nb = (max_len + block - 1) // block
+    k = min(rng.randint(1, nb + 3), 2048)
+    lens = rng.choice(["rand", "edge"])
+    return (f"paged{i}-{kind}-b{batch}-g{gqa}-kv{hkv}-B{block}-P{page}-L{max_len}-k{k}-{lens}",
+            batch, hkv, gqa, block, page, max_len, k, lens)
+
+
+PAGED_CASES = [_draw_paged_case(random.Random(9300 + i), i) for i in range(8)]
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=[c[0] for c in PAGED_CASES])
+def test_random_paged_step(case):
+    check_paged_case(case)
+
+
+def _draw_shared_case(rng, i):
+    block = rng.choice([16, 32, 64, 128])
+    gqa = rng.choice([1, 2, 4, 5, 8])
+    if rng.random() < 0.5:  # at least as many pairs as CUs
+        hkv = 8
+        n_prompts, n_share = rng.choice([(4, 8), (8, 4), (2, 16), (3, 11)])
+        ctx = rng.randint(2 * block, 3000)
+    else:
+        hkv = rng.choice([1, 2, 4])
+        n_prompts, n_share = rng.randint(1, 3), rng.randint(1, 4)
+        ctx = rng.randint(2 * block, 5000)
+    prompt = block * rng.randint(1, (ctx - 1) // block)
+    nb = (ctx + block - 1) // block
+    k = min(rng.randint(1, nb + 3), 2048)
+    return (f"shared{i}-p{n_prompts}x{n_share}-g{gqa}-kv{hkv}-B{block}-P{prompt}-L{ctx}-k{k}",
+            n_prompts, n_share, hkv, gqa, block, prompt, ctx, k)
+
+
+SHARED_CASES = [_draw_shared_case(random.Random(9400 + i), i) for i in range(8)]
+
+
+@pytest.mark.parametrize("case", SHARED_CASES, ids=[c[0] for c in SHARED_CASES])
+def test_random_shared_step(case):
+    check_shared_case(case)

@@ -91,8 +91,10 @@ def run(c, shared=True, with_scores=True):
     return S, scores, idx, out
 
 
-@pytest.mark.parametrize("case", SHARED, ids=[c[0] for c in SHARED])
-def test_shared_prompt_step_against_oracle(case):
+def check_shared_case(case):
+    """One shared-prompt step against the oracle on each sample's full
+    cache, then the same tokens in contiguous caches (bit for bit) and
+    without a scores buffer."""
     c = build(case)
     w, k, P = c["w"], c["k"], c["P"]
     say(f"case {w.name}: pairs {w.pairs}, prompt {P} of {w.ctx_len}")
@@ -131,3 +133,8 @@ def test_shared_prompt_step_against_oracle(case):
     assert torch.equal(bits(out3), bits(out))
     assert torch.equal(bits(S3[:, :, pb:nb]), bits(S[:, :, pb:nb]))
     say(f"  ok, max err {worst:.3e}")
+
+
+@pytest.mark.parametrize("case", SHARED, ids=[c[0] for c in SHARED])
+def test_shared_prompt_step_against_oracle(case):
+    check_shared_case(case)
