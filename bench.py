@@ -141,6 +141,28 @@ def time_steps(fn, layers, steps, warmup, n_events=0):
     return total_ms / steps, stage_ms
 
 
+def read_peak(nbytes=4 * 2**30, reps=20):
+    """Measured read bandwidth of this device: kin_hbm_read_probe (a plain
+    streaming read of every 16-byte word once) over a buffer far larger than
+    the Infinity Cache, the median of `reps` timed launches.  Returns GB/s."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        kb.kin_hbm_read_probe(buf, nbytes, sink)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record()
+        kb.kin_hbm_read_probe(buf, nbytes, sink)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)[reps // 2]
+    del buf
+    torch.cuda.empty_cache()
+    return nbytes / (ms * 1e-3) / 1e9
+
+
 def layers_for(w, requested=0):
     """Layers rotated: enough that one round of steps moves >= 1 GiB (so the
     Infinity Cache holds no previous step's bytes), within 150 GiB of HBM."""
@@ -526,6 +548,12 @@ def main():
                         "ms_per_step": round(dms, 5),
                         "hbm_gbs": round(dbytes / (dms * 1e-3) / 1e9, 1)}
         res["speedup_vs_dense"] = round(dms / ms, 2)
+
+    # the step against this device's measured read bandwidth as well
+    peak = read_peak()
+    res["read_peak"] = {"kernel": "k_read_probe", "gbs": round(peak, 1),
+                        "frac_of_published": round(peak / PEAK_HBM_GBS, 4),
+                        "step_frac": round(gbs / peak, 4)}
 
     if args.calib_copy:
         # a plain copy kernel of known size: reads 1 GiB and writes 1 GiB, so

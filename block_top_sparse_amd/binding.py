@@ -92,6 +92,7 @@ def lib():
             "kin_decode_select_attend": (I, [D, P, P, P, P, I, P, P, P, Z, P]),
             "kin_sparse_ws_bytes": (Z, [D, I]),
             "kin_dense_ws_bytes": (Z, [D]),
+            "kin_hbm_read_probe": (I, [P, Z, P, P]),
             "kin_status_str": (ctypes.c_char_p, [I]),
             "kin_last_error": (ctypes.c_char_p, []),
             "kin_version": (I, []),
@@ -118,7 +119,8 @@ def exported_names():
             "kin_sparse_ws_bytes", "kin_dense_ws_bytes", "kin_status_str", "kin_last_error",
             "kin_version", "kin_paged_summary_update", "kin_paged_decode_step",
             "kin_token_decode_step", "kin_token_ws_bytes", "kin_shared_decode_step",
-            "kin_quest_summary_update", "kin_quest_decode_step", "kin_quest_ws_bytes"]
+            "kin_quest_summary_update", "kin_quest_decode_step", "kin_quest_ws_bytes",
+            "kin_hbm_read_probe"]
 
 
 def _p(t):
@@ -237,6 +239,11 @@ def kin_sparse_ws_bytes(desc, k) -> int:
     if n == ctypes.c_size_t(-1).value:
         raise KinError(-2, lib().kin_last_error().decode())
     return n
+
+
+def kin_hbm_read_probe(buf, nbytes, sink, stream=None):
+    """Stream nbytes of buf (a measurement helper); XOR-folds into sink."""
+    _check(lib().kin_hbm_read_probe(_p(buf), nbytes, _p(sink), _s(stream)))
 
 
 def kin_dense_ws_bytes(desc) -> int:

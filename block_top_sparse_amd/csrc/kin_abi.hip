@@ -528,6 +528,15 @@ size_t kin_sparse_ws_bytes(const kin_desc *desc, int32_t k) {
     return a > b ? a : b;
 }
 
+kin_status kin_hbm_read_probe(const void *buf, size_t bytes, void *sink, kin_stream stream) {
+    KIN_REQUIRE_PTR(buf);
+    KIN_REQUIRE_PTR(sink);
+    if (bytes == 0 || bytes % 16)
+        return fail(KIN_ERR_SHAPE, "bytes = %zu: need a positive multiple of 16", bytes);
+    return launched(kin::launch_read_probe(buf, bytes, sink, num_cu(), (hipStream_t)stream),
+                    "kin_hbm_read_probe");
+}
+
 size_t kin_dense_ws_bytes(const kin_desc *desc) {
     kin::Geo g;
     if (check_desc(desc, &g) != KIN_OK) return (size_t)-1;

@@ -92,6 +92,10 @@ AttnPlan plan_tok(const Geo &g, int k, int num_cu);
 hipError_t launch_tok_step(const Geo &g, const void *q, const void *K, const void *V,
                            double *scores, int k, int32_t *idx, void *out, void *ws, int num_cu,
                            hipStream_t s);
+// measurement helper: stream `bytes` (a multiple of 16) of buf, XOR-folding
+// them into the 16-byte sink
+hipError_t launch_read_probe(const void *buf, size_t bytes, void *sink, int num_cu,
+                             hipStream_t s);
 // (quest: S holds the Quest-style [pair][nb_cap][2][head_dim] summaries and
 // the blocks are ranked by the Quest bound; contiguous caches only)
 hipError_t launch_decode_step(const Geo &g, const void *q, const void *K, const void *V, void *S,

@@ -320,6 +320,16 @@ KIN_API size_t kin_token_ws_bytes(const kin_desc *desc, int32_t k);
 KIN_API size_t kin_sparse_ws_bytes(const kin_desc *desc, int32_t k);
 KIN_API size_t kin_dense_ws_bytes(const kin_desc *desc);
 
+/* Measurement helper, not a step of the method: stream `bytes` bytes of the
+ * device buffer `buf` with plain 16-byte reads (every word once) on `stream`,
+ * as a measured read-bandwidth ceiling to quote the decode step against,
+ * next to the published peak.  The reads are XOR-folded into the 16-byte
+ * device buffer `sink` (four 32-bit words, XOR-accumulated: zero it first to
+ * read the buffer's XOR back).  buf and sink 16-byte aligned; bytes a
+ * positive multiple of 16 (KIN_ERR_SHAPE otherwise). */
+KIN_API kin_status kin_hbm_read_probe(const void *buf, size_t bytes, void *sink,
+                                      kin_stream stream);
+
 /* Name of a status code, and the detail of the last error on this thread. */
 KIN_API const char *kin_status_str(kin_status status);
 KIN_API const char *kin_last_error(void);

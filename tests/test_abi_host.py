@@ -29,7 +29,7 @@ def header_entry_points():
 
 def test_every_declared_entry_point_is_exported():
     declared = header_entry_points()
-    assert len(declared) == 21, declared
+    assert len(declared) == 22, declared
     lib = ctypes.CDLL(kb.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
@@ -189,3 +189,18 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(kb, "_lib", None)
     with pytest.raises(ImportError):
         kb.kin_version()
+
+
+def test_read_probe_argument_checks():
+    """kin_hbm_read_probe rejects NULL or misaligned buffers and sizes that are
+    not a positive multiple of 16, before any launch."""
+    L = ctypes.CDLL(kb.LIB_PATH)
+    f = L.kin_hbm_read_probe
+    f.restype = ctypes.c_int32
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    null, shape, align = -1, -2, -4
+    assert f(None, 64, FAKE, None) == null
+    assert f(FAKE, 64, None, None) == null
+    assert f(MISALIGNED, 64, FAKE, None) == align
+    assert f(FAKE, 0, FAKE, None) == shape
+    assert f(FAKE, 40, FAKE, None) == shape
