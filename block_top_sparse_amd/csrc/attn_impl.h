@@ -685,16 +685,25 @@ __device__ void attend_f32(const AttnArgs &a, const int32_t *sel, int pair, int 
         float s[kMaxGqa];
 #pragma unroll
         for (int h = 0; h < kMaxGqa; ++h) s[h] = 0.f;
+        // the key row in batches of kKBatch 16-byte loads, all in flight
+        // before their FMAs (channel order unchanged)
+        constexpr int kKBatch = 8;
         const f32x4 *kr = reinterpret_cast<const f32x4 *>(Kp + (size_t)row * kHeadDim);
-        for (int c4 = 0; c4 < kHeadDim / 4; ++c4) {
-            const f32x4 kv = kr[c4];
+        for (int c0 = 0; c0 < kHeadDim / 4; c0 += kKBatch) {
+            f32x4 kv[kKBatch];
 #pragma unroll
-            for (int h = 0; h < kMaxGqa; ++h) {
-                if (h < G) {
-                    s[h] = fmaf(fl.q[h][4 * c4 + 0], kv[0], s[h]);
-                    s[h] = fmaf(fl.q[h][4 * c4 + 1], kv[1], s[h]);
-                    s[h] = fmaf(fl.q[h][4 * c4 + 2], kv[2], s[h]);
-                    s[h] = fmaf(fl.q[h][4 * c4 + 3], kv[3], s[h]);
+            for (int u = 0; u < kKBatch; ++u) kv[u] = kr[c0 + u];
+#pragma unroll
+            for (int u = 0; u < kKBatch; ++u) {
+                const int c4 = c0 + u;
+#pragma unroll
+                for (int h = 0; h < kMaxGqa; ++h) {
+                    if (h < G) {
+                        s[h] = fmaf(fl.q[h][4 * c4 + 0], kv[u][0], s[h]);
+                        s[h] = fmaf(fl.q[h][4 * c4 + 1], kv[u][1], s[h]);
+                        s[h] = fmaf(fl.q[h][4 * c4 + 2], kv[u][2], s[h]);
+                        s[h] = fmaf(fl.q[h][4 * c4 + 3], kv[u][3], s[h]);
+                    }
                 }
             }
         }
@@ -716,16 +725,25 @@ __device__ void attend_f32(const AttnArgs &a, const int32_t *sel, int pair, int 
             fl.p[slot][h][lane] = pz;
         }
         wave_lds_sync();  // p / row entries of this wave are complete
-        // p . v: lane owns channels 2*lane, 2*lane+1
-        for (int t = 0; t < kChunkF32; ++t) {
-            const float2 v =
-                reinterpret_cast<const float2 *>(Vp + (size_t)fl.row[slot][t] * kHeadDim)[lane];
+        // p . v: lane owns channels 2*lane, 2*lane+1; the value rows in
+        // batches of kVBatch tokens, all loads in flight before their FMAs
+        // (token order unchanged)
+        constexpr int kVBatch = 16;
+        for (int t0 = 0; t0 < kChunkF32; t0 += kVBatch) {
+            float2 v[kVBatch];
 #pragma unroll
-            for (int h = 0; h < kMaxGqa; ++h) {
-                if (h < G) {
-                    const float pt = fl.p[slot][h][t];
-                    o0[h] = fmaf(pt, v.x, o0[h]);
-                    o1[h] = fmaf(pt, v.y, o1[h]);
+            for (int u = 0; u < kVBatch; ++u)
+                v[u] = reinterpret_cast<const float2 *>(Vp + (size_t)fl.row[slot][t0 + u] *
+                                                                 kHeadDim)[lane];
+#pragma unroll
+            for (int u = 0; u < kVBatch; ++u) {
+#pragma unroll
+                for (int h = 0; h < kMaxGqa; ++h) {
+                    if (h < G) {
+                        const float pt = fl.p[slot][h][t0 + u];
+                        o0[h] = fmaf(pt, v[u].x, o0[h]);
+                        o1[h] = fmaf(pt, v[u].y, o1[h]);
+                    }
                 }
             }
         }
