@@ -469,9 +469,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the path shards by sequence or KV head with no "
-              "exchange, and multi-GPU runs are not part of this build (use --gpus 1).",
-              file=sys.stderr)
+        print("bench.py measures one GPU (use --gpus 1): the step shards by sequence or KV "
+              "head with no exchange between GPUs, and runs on several GPUs are not "
+              "measured here.", file=sys.stderr)
         sys.exit(2)
 
     torch.cuda.set_device(0)
