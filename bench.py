@@ -508,7 +508,12 @@ def main():
     gbs = step_bytes / (ms * 1e-3) / 1e9
     num_cu = torch.cuda.get_device_properties(0).multi_processor_count
     single = single_kernel(w, num_cu)
-    kern = "k_decode_step" if single else "k_block_score + k_select_attend (two launches)"
+    kern = {"one": "k_decode_step",
+            "one-split": "k_select_attend (one launch)",
+            "two": ("k_score_tiles + k_select_attend (two launches)" if w.dtype == "bf16"
+                    else "k_block_score + k_select_attend (two launches)"),
+            "four": "scores or newest row, top-k, attention, combine (four launches)"}[
+                step_kernels(w, num_cu)]
     kbytes, kus = step_bytes, ms * 1000
     achieved = kbytes / (kus * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": kern, "achieved": round(achieved, 1),
