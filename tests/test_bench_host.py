@@ -26,3 +26,31 @@ def test_a_multi_rank_launch_is_refused():
     r = _run([], env={"WORLD_SIZE": "2"})
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_launch_form_labels_follow_the_dispatch_rules():
+    """step_kernels names the launches kin_sparse_decode_step makes (bf16, no
+    scores output): one kernel when the pairs cover the chip (at most 8192
+    blocks and 2048 kept), the split select + attend alone when few pairs
+    keep every block, score tiles + select/attend for few pairs otherwise,
+    and four launches past 2048 kept blocks."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from block_top_sparse_amd import workloads
+
+    cu = 256
+    form = {w.name: bench.step_kernels(w, cu) for w in workloads.sweep()}
+    assert bench.step_kernels(workloads.QWEN3_8B, cu) == "one"
+    assert form["sweep-b32-ctx32768-blk16-budget1024"] == "one"        # 256 pairs
+    assert form["sweep-b8-ctx32768-blk16-budget8192"] == "two"         # 64 pairs, 512 of 2048
+    assert form["sweep-b8-ctx8192-blk16-allblocks"] == "one-split"     # 64 pairs, all 512 kept
+    assert form["sweep-b32-ctx131072-blk16-allblocks"] == "four"       # 8192 kept blocks
+    for w in workloads.sweep():
+        f = form[w.name]
+        if w.topk > 2048:
+            assert f == "four", w.name
+        elif w.pairs >= cu and w.nb <= 8192:
+            assert f == "one", w.name
+        else:
+            assert f in ("two", "one-split"), w.name
+            assert (f == "one-split") == (w.topk >= w.nb), w.name
