@@ -98,3 +98,42 @@ def test_quest_step_repeated_on_one_workspace():
     _repeat(lambda: kb.kin_quest_decode_step(desc, inp["q"], inp["K"], inp["V"], Sq, None, 60,
                                              idx, out, ws),
             lambda: (idx, out))
+
+
+def test_two_streams_at_once_match_one_after_the_other():
+    """Two different few-pair problems (a bf16 two-kernel step and a keep-all
+    one-launch step), each with its own workspace, stepped 20 times on two
+    streams at once: the results equal those of the same calls made one
+    after the other on the default stream (the library keeps no state
+    between calls besides the caller's buffers)."""
+    cases = [("conc-a", 3, 16, 2, 5000, 16, 100, 5120), ("conc-b", 2, 16, 4, 2000, 16, 125, 2048)]
+    jobs = []
+    for name, b, hq, hkv, L, B, k, cap in cases:
+        w = Workload(name, batch=b, hq=hq, hkv=hkv, ctx_len=L, block=B, topk=k, dtype="bf16",
+                     seed=zlib.crc32(name.encode()) % 10000, t_cap=cap)
+        inp = gpu_inputs(w)
+        bufs = LayerBuffers(w, k=k)
+        kb.kin_block_summary_update(bufs.desc, inp["K"], bufs.S, 0, (w.nb - 1) * B)
+        jobs.append((w, inp, bufs, k))
+
+    def step(job, stream=None):
+        w, inp, bufs, k = job
+        kb.kin_sparse_decode_step(bufs.desc, inp["q"], inp["K"], inp["V"], bufs.S, None, k,
+                                  bufs.idx, bufs.out, bufs.ws, stream=stream)
+
+    for job in jobs:
+        step(job)
+    torch.cuda.synchronize()
+    want = [(j[2].idx.clone(), j[2].out.clone()) for j in jobs]
+    for j in jobs:
+        j[2].idx.fill_(-7)
+        j[2].out.fill_(float("nan"))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for _ in range(20):
+        for job, st in zip(jobs, streams):
+            step(job, stream=st)
+    torch.cuda.synchronize()
+    for (idx, out), job in zip(want, jobs):
+        assert torch.equal(job[2].idx, idx)
+        assert torch.equal(bits(job[2].out), bits(out))
