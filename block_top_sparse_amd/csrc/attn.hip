@@ -146,9 +146,14 @@ __global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a0,
     stores_complete();
     __shared__ uint32_t last;
     __syncthreads();
-    if (threadIdx.x == 0)
+    if (threadIdx.x == 0) {
         last = (epoch ? arrive_count(ctrl + pair, epoch, a.nsplit - 1)
                       : arrive_add(ctrl + pair)) == (uint32_t)a.nsplit;
+        // every split of the pair has arrived: the word starts the next call
+        // at zero (a replayed graph repeats this call's round tag; zero
+        // matches no tag)
+        if (last) st_agent(ctrl + pair, (uint64_t)0);
+    }
     __syncthreads();
     if (last) combine_pair<DT, kStepThreads>(a, pair);
 }

@@ -54,6 +54,10 @@
  *     surface at the caller's next synchronisation, as with any HIP work.
  *   - Pointers must be 16-byte aligned.  The values read must be finite.
  *   - No C++ exception crosses this interface.
+ *   - The calls launch kernels only (no memset, copy or allocation), so they
+ *     can be captured into a HIP graph and replayed; a workspace carries no
+ *     state from one call or replay to the next that it needs cleared.  Calls
+ *     that overlap in time must not share a workspace.
  */
 #ifndef KIN_H
 #define KIN_H

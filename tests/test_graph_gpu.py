@@ -1,0 +1,112 @@
+"""The decode steps captured in a HIP graph (torch.cuda.CUDAGraph) and
+replayed: the library allocates nothing, never synchronises and records no
+memset, so a captured step replays; a replay repeats the round tag chosen at
+capture, so the split forms must leave their arrival words ready for it.
+Each form is replayed four times back to back, with new query values
+written eagerly before each replay, and every replay must equal an eager
+call on the same inputs bit for bit."""
+import zlib
+
+import pytest
+import torch
+
+from block_top_sparse_amd import binding as kb
+from block_top_sparse_amd import synth
+from block_top_sparse_amd.buffers import LayerBuffers
+from block_top_sparse_amd.workloads import Workload
+
+from parity_util import bits, gpu_inputs, say
+
+pytestmark = pytest.mark.gpu
+
+REPLAYS = 4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kb.lib()
+
+
+def _check_replays(call, q, outs, seed):
+    """Replays back to back (new queries written eagerly before each, no
+    eager step in between, so each replay finds the words the previous
+    replay left with the same round tag), then the eager references."""
+    call()  # eager warm-up (the library caches the device's CU count)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    qs = [torch.randn(q.shape, generator=gen, device="cuda").to(q.dtype) for _ in range(REPLAYS)]
+    got = []
+    for r in range(REPLAYS):
+        q.copy_(qs[r])  # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got.append([t.clone() for t in outs()])
+    for r in range(REPLAYS):
+        q.copy_(qs[r])
+        call()
+        torch.cuda.synchronize()
+        for a, b in zip(got[r], outs()):
+            assert torch.equal(bits(a) if a.is_floating_point() else a,
+                               bits(b) if b.is_floating_point() else b), f"replay {r}"
+    say(f"  {REPLAYS} replays equal eager calls")
+
+
+BLOCK = [
+    # name, batch, hq, hkv, ctx, block, k, dtype, t_cap, scores
+    ("graph-one-kernel", 64, 16, 4, 2000, 16, 20, "bf16", 2048, False),   # 256 pairs
+    ("graph-two-kernel", 3, 16, 2, 5000, 16, 100, "bf16", 5120, True),
+    ("graph-keepall", 2, 16, 4, 2000, 16, 125, "bf16", 2048, False),       # round-tagged splits
+    ("graph-f32-split", 3, 2, 2, 4730, 16, 292, "f32", 4793, True),        # round-tagged splits
+]
+
+
+@pytest.mark.parametrize("case", BLOCK, ids=[c[0] for c in BLOCK])
+def test_block_step_replayed_from_a_graph(case):
+    name, b, hq, hkv, L, B, k, dt, cap, with_scores = case
+    w = Workload(name, batch=b, hq=hq, hkv=hkv, ctx_len=L, block=B, topk=k, dtype=dt,
+                 seed=zlib.crc32(name.encode()) % 10000, t_cap=cap)
+    say(f"case {name}: pairs {w.pairs}")
+    inp = gpu_inputs(w)
+    bufs = LayerBuffers(w, k=k)
+    kb.kin_block_summary_update(bufs.desc, inp["K"], bufs.S, 0, (w.nb - 1) * B)
+
+    def call():
+        kb.kin_sparse_decode_step(bufs.desc, inp["q"], inp["K"], inp["V"], bufs.S,
+                                  bufs.scores if with_scores else None, k, bufs.idx, bufs.out,
+                                  bufs.ws)
+
+    _check_replays(call, inp["q"], lambda: (bufs.idx, bufs.out), w.seed)
+
+
+def test_token_step_replayed_from_a_graph():
+    w = Workload("graph-token", batch=2, hq=8, hkv=2, ctx_len=20000, block=1, topk=500,
+                 dtype="bf16", seed=915, t_cap=20000)
+    inp = synth.make_inputs(w, device="cuda")
+    desc = kb.make_desc(w.batch, w.hkv, w.gqa, w.cap, w.ctx_len, 1, torch.bfloat16)
+    idx = torch.empty((w.batch, w.hkv, 500), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.batch, w.hq, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(kb.kin_token_ws_bytes(desc, 500), dtype=torch.uint8, device="cuda")
+    _check_replays(lambda: kb.kin_token_decode_step(desc, inp["q"], inp["K"], inp["V"], None,
+                                                    500, idx, out, ws),
+                   inp["q"], lambda: (idx, out), 915)
+
+
+def test_quest_step_replayed_from_a_graph():
+    w = Workload("graph-quest", batch=3, hq=16, hkv=2, ctx_len=4000, block=16, topk=60,
+                 dtype="bf16", seed=916, t_cap=4096)
+    inp = synth.make_inputs(w, device="cuda")
+    desc = kb.make_desc(w.batch, w.hkv, w.gqa, w.cap, w.ctx_len, 16, torch.bfloat16)
+    Sq = torch.empty((w.batch, w.hkv, w.nb_cap, 2, 128), dtype=torch.bfloat16, device="cuda")
+    kb.kin_quest_summary_update(desc, inp["K"], Sq, 0, w.ctx_len)
+    idx = torch.empty((w.batch, w.hkv, 60), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.batch, w.hq, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(kb.kin_quest_ws_bytes(desc, 60), dtype=torch.uint8, device="cuda")
+    _check_replays(lambda: kb.kin_quest_decode_step(desc, inp["q"], inp["K"], inp["V"], Sq, None,
+                                                    60, idx, out, ws),
+                   inp["q"], lambda: (idx, out), 916)
