@@ -110,3 +110,39 @@ def test_quest_step_replayed_from_a_graph():
     _check_replays(lambda: kb.kin_quest_decode_step(desc, inp["q"], inp["K"], inp["V"], Sq, None,
                                                     60, idx, out, ws),
                    inp["q"], lambda: (idx, out), 916)
+
+
+def test_paged_keepall_step_replayed_from_a_graph():
+    """Variable lengths in a paged pool, few pairs, every block kept and no
+    scores: the one-launch form with round-tagged splits."""
+    from test_paged_gpu import Case
+
+    c = Case("graph-paged-keepall", 3, 2, 4, 16, 64, 600, 40, "rand")
+    pg = c.pages()
+    kb.kin_paged_summary_update(c.desc, pg, c.Kp, c.S, 0, c.w.ctx_len)
+
+    def call():
+        kb.kin_paged_decode_step(c.desc, pg, c.q, c.Kp, c.Vp, c.S, None, c.k, c.idx, c.out, c.ws)
+
+    _check_replays(call, c.q, lambda: (c.idx, c.out), 917)
+
+
+def test_shared_prompt_step_replayed_from_a_graph():
+    """Samples sharing a prompt, few pairs (two kernels)."""
+    from test_shared_gpu import build
+
+    c = build(("graph-shared", 2, 2, 2, 8, 64, 512, 3000, 10))
+    w, k, P = c["w"], c["k"], c["P"]
+    S = torch.empty((w.batch, w.hkv, w.nb_cap, 128), dtype=torch.bfloat16, device="cuda")
+    kb.kin_block_summary_update(c["desc"], c["K"], S, P, w.ctx_len)
+    idx = torch.empty((w.batch, w.hkv, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.batch, w.hq, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(kb.kin_sparse_ws_bytes(c["desc"], k), 16), dtype=torch.uint8,
+                     device="cuda")
+    share = kb.make_share(c["n_share"], P, c["Kp"], c["Vp"], c["Sp"])
+
+    def call():
+        kb.kin_shared_decode_step(c["desc"], share, c["q"], c["K"], c["V"], S, None, k, idx, out,
+                                  ws)
+
+    _check_replays(call, c["q"], lambda: (idx, out), 918)
