@@ -24,7 +24,10 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libkin_oracle.so")
+# KIN_ORACLE_LIB: another build of the same source to load instead (the
+# mutation test points it at copies with a planted mistake, which the pins
+# must then catch)
+_LIB_PATH = os.environ.get("KIN_ORACLE_LIB") or os.path.join(_HERE, "libkin_oracle.so")
 _lib = None
 
 F32, BF16 = 0, 1
