@@ -1,7 +1,8 @@
 """The pins catch plausible mistakes in the oracle (CPU).  Each case plants
 one mistake in a copy of oracle/kin_oracle.c (the tie-break, the
 partial-block mean, the bf16 rounding, the softmax scale, the GQA sum, the
-ranking direction, the token range of a block, the Quest bound), builds it
+ranking direction, the token range of a block, the Quest bound, the
+attended token range, the block count), builds it
 with the oracle's own flags, and runs the pin suite against that build: at
 least one pin must fail.  The planted mistakes live only in temporary
 copies."""
@@ -45,6 +46,12 @@ MUTANTS = [
     ("quest-bound-takes-minimum",
      "sigma += a > e ? a : e;",
      "sigma += a < e ? a : e;"),
+    ("newest-token-not-attended",
+     "t < (sel[i] + 1) * c->block && t < c->ctx_len; ++t)",
+     "t < (sel[i] + 1) * c->block && t < c->ctx_len - 1; ++t)"),
+    ("block-count-rounded-down",
+     "static int kor_nblocks(int len, int block) { return (len + block - 1) / block; }",
+     "static int kor_nblocks(int len, int block) { return len / block > 0 ? len / block : 1; }"),
 ]
 
 
