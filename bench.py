@@ -32,19 +32,28 @@ METRIC = "sparse decode-attn queries/s/layer + achieved HBM GB/s vs peak (1 GPU)
 PEAK_HBM_GBS = 8000.0
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_decode_step_qwen3-8b_counters.md")
+# committed HBM counter summaries of the step kernel, per workload
+TRAFFIC_FILES = {
+    workloads.QWEN3_8B.name: "k_decode_step_qwen3-8b_counters.md",
+    workloads.QWEN3_14B.name: "k_decode_step_qwen3-14b_counters.md",
+    workloads.QWEN3_32B.name: "k_decode_step_qwen3-32b_counters.md",
+}
 
 
 def stored_traffic(w):
-    """HBM bytes per launch of k_decode_step from the committed counter
-    summary, only for the workload it was taken on and only while the kernel
-    sources still hash to the recorded value (else None)."""
+    """HBM bytes per launch of k_decode_step from the committed rocprofv3
+    counter summary under profiles/ (FETCH_SIZE + WRITE_SIZE, each scaled by
+    a plain copy's reading), only for the workload it was taken on and only
+    while the kernel sources still hash to the recorded value; else None.
+    Returns (bytes, file name)."""
     import hashlib
 
-    if w.name != workloads.QWEN3_8B.name or not os.path.exists(TRAFFIC_FILE):
-        return None
+    name = TRAFFIC_FILES.get(w.name)
+    path = os.path.join(ROOT, "profiles", name) if name else None
+    if not path or not os.path.exists(path):
+        return None, None
     fields = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith(("#", "|", "`")):
             key, _, val = line.partition(":")
             fields[key.strip()] = val.strip()
@@ -54,10 +63,10 @@ def stored_traffic(w):
         for src in srcs:
             h.update(open(os.path.join(ROOT, src), "rb").read())
         if h.hexdigest() != fields["kernel_source_sha256"]:
-            return None
-        return int(fields["traffic_bytes_per_launch"])
+            return None, None
+        return int(fields["traffic_bytes_per_launch"]), "profiles/" + name
     except (KeyError, OSError, ValueError):
-        return None
+        return None, None
 
 
 def log(msg):
@@ -139,6 +148,29 @@ def time_steps(fn, layers, steps, warmup, n_events=0):
         for i in range(n_events - 1):
             stage_ms.append(sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)) / steps)
     return total_ms / steps, stage_ms
+
+
+def step_distribution(fn, layers, steps):
+    """A second pass of `steps` steps with an event recorded before each step
+    and after the last one (same stream, no host gap): per-step durations in
+    microseconds -> median, p10, p90 (nearest rank), mean, std."""
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for s_ in range(steps):
+        evs[s_].record()
+        fn(*layers[s_ % len(layers)], None)
+    evs[steps].record()
+    torch.cuda.synchronize()
+    us = sorted(evs[i].elapsed_time(evs[i + 1]) * 1000.0 for i in range(steps))
+    n = len(us)
+
+    def rank(p):
+        return us[min(n - 1, max(0, math.ceil(p * n) - 1))]
+
+    mean = sum(us) / n
+    std = math.sqrt(sum((x - mean) ** 2 for x in us) / max(1, n - 1))
+    return {"n": n, "median_us": round(rank(0.5), 2), "p10_us": round(rank(0.1), 2),
+            "p90_us": round(rank(0.9), 2), "mean_us": round(mean, 2), "std_us": round(std, 2)}
 
 
 def read_peak(nbytes=4 * 2**30, reps=20):
@@ -227,7 +259,7 @@ def run_token(args, w):
         inp = synth.make_inputs(w, device="cuda", seed=w.seed + 7919 * l)
         bufs = {"idx": torch.empty((w.batch, w.hkv, w.topk), dtype=torch.int32, device="cuda"),
                 "out": torch.empty((w.batch, w.hq, 128), dtype=torch.bfloat16, device="cuda"),
-                "ws": torch.empty(nws, dtype=torch.uint8, device="cuda")}
+                "ws": torch.zeros(nws, dtype=torch.uint8, device="cuda")}
         layers.append((inp, bufs))
         torch.cuda.synchronize()
         log(f"layer {l}: cache {w.cache_bytes() / 2**30:.2f} GiB ready")
@@ -333,7 +365,7 @@ def run_quest(args, w):
         bufs = {"Sq": Sq,
                 "idx": torch.empty((w.batch, w.hkv, w.topk), dtype=torch.int32, device="cuda"),
                 "out": torch.empty((w.batch, w.hq, 128), dtype=torch.bfloat16, device="cuda"),
-                "ws": torch.empty(nws, dtype=torch.uint8, device="cuda")}
+                "ws": torch.zeros(nws, dtype=torch.uint8, device="cuda")}
         layers.append((inp, bufs))
         torch.cuda.synchronize()
         log(f"layer {l}: cache {w.cache_bytes() / 2**30:.2f} GiB ready")
@@ -418,21 +450,24 @@ def run_shared(args, w):
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(w, layer, max_seqs, min_seconds=10.0):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    newest-block summary update + scores + selection + attention for the
-    first `max_seqs` sequences of one layer (all their KV heads), summaries
-    prebuilt outside the timed region; repeated until at least min_seconds
-    of CPU work have been timed, the rate averaged over all repetitions."""
+def cpu_share():
+    """Threads the oracle may use: the CPUs this process may run on, at most
+    16 (the host CPU share that comes with one GPU; the host's other CPUs
+    belong to other GPUs' work).  Returns (threads, host CPUs, usable CPUs)."""
+    host = os.cpu_count() or 1
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = host
+    return max(1, min(16, usable)), host, usable
+
+
+def _oracle_rate(w, q, K, V, S, nthreads, min_seconds):
+    """Time the oracle's step (newest-block summary update + scores + top-k +
+    attention) over the given sequences until min_seconds have passed."""
     import oracle
 
-    inp = layer[0]
-    n = min(max_seqs, w.batch)
-    nthreads = oracle.default_threads()
-    q = inp["q"][:n].cpu()
-    K = inp["K"][:n].cpu()
-    V = inp["V"][:n].cpu()
-    S, _ = oracle.block_summary(K, w.block, w.ctx_len, nthreads=nthreads)
+    n = q.shape[0]
     reps, dt = 0, 0.0
     while dt < min_seconds:
         t0 = time.perf_counter()
@@ -443,10 +478,74 @@ def cpu_baseline(w, layer, max_seqs, min_seconds=10.0):
         oracle.decode_attention(q, K, V, w.gqa, w.ctx_len, w.block, idx=idx, nthreads=nthreads)
         dt += time.perf_counter() - t0
         reps += 1
-    return {"value": n * reps / dt, "unit": "queries/s/layer", "cores": nthreads, "kind": "oracle",
+    return n * reps / dt, reps, dt
+
+
+def cpu_baseline(w, layer, max_seqs, min_seconds=10.0, single_seqs=2, single_seconds=5.0):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    newest-block summary update + scores + selection + attention for the
+    first `max_seqs` sequences of one layer (all their KV heads), summaries
+    prebuilt outside the timed region; repeated until at least min_seconds
+    of CPU work have been timed, the rate averaged over all repetitions.
+    Run on the host's CPU share (cpu_share), and once more on one thread
+    over the first `single_seqs` sequences."""
+    import oracle
+
+    inp = layer[0]
+    n = min(max_seqs, w.batch)
+    nthreads, host, usable = cpu_share()
+    q = inp["q"][:n].cpu()
+    K = inp["K"][:n].cpu()
+    V = inp["V"][:n].cpu()
+    S, _ = oracle.block_summary(K, w.block, w.ctx_len, nthreads=nthreads)
+    rate, reps, dt = _oracle_rate(w, q, K, V, S, nthreads, min_seconds)
+    n1 = min(single_seqs, n)
+    rate1, reps1, dt1 = _oracle_rate(w, q[:n1].contiguous(), K[:n1].contiguous(),
+                                     V[:n1].contiguous(), S[:n1].contiguous(), 1, single_seconds)
+    return {"value": rate, "unit": "queries/s/layer", "cores": nthreads, "kind": "oracle",
             "sample": f"{n} of {w.batch} sequences x {w.hkv} KV heads of one layer (summary "
                       f"update + scores + top-k + attention, fp64), {reps} repetitions, "
-                      f"{dt:.1f} s"}
+                      f"{dt:.1f} s on {nthreads} threads",
+            "host_cpus": host, "usable_cpus": usable,
+            "single_thread": {"value": rate1, "unit": "queries/s/layer", "cores": 1,
+                              "sample": f"{n1} sequences x {w.hkv} KV heads, {reps1} "
+                                        f"repetitions, {dt1:.1f} s"}}
+
+
+KERNEL_NAMES = {"one": "k_decode_step",
+                "one-split": "k_select_attend (one launch)",
+                "two": "k_score_tiles + k_select_attend (two launches)",
+                "two-f32": "k_block_score + k_select_attend (two launches)",
+                "four": "scores or newest row, top-k, attention, combine (four launches)"}
+
+
+def measure(w, args, layers, num_cu):
+    """Time kin_sparse_decode_step on workload w over the rotated layers:
+    the K timed steps bracketed by one event pair (ms_per_step), then a
+    second pass with an event between steps for the per-step spread."""
+    step = lambda i, b, e: sparse_step(w, i, b, None)  # noqa: E731
+    ms, _ = time_steps(step, layers, args.steps, args.warmup)
+    dist = step_distribution(step, layers, args.steps)
+    step_bytes = w.bytes_sparse_step()
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    form = step_kernels(w, num_cu)
+    kern = KERNEL_NAMES["two-f32" if form == "two" and w.dtype == "f32" else form]
+    traffic, traffic_src = stored_traffic(w) if form == "one" else (None, None)
+    # the step is one launch of the dominant kernel when form == "one": its
+    # average launch duration is the event time over the K back-to-back steps
+    roofline = {"bound": "hbm", "kernel": kern, "achieved": round(gbs, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                "traffic": traffic, "bytes_per_launch": step_bytes, "avg_us": round(ms * 1000, 2),
+                "avg_us_source": "HIP events on the launch stream around the K timed steps"}
+    if traffic is not None:
+        roofline["traffic_source"] = (f"{traffic_src}: rocprofv3 FETCH_SIZE + WRITE_SIZE of this "
+                                      "kernel, copy-calibrated, sources hash-matched")
+    return {"value": round(w.batch / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
+            "per_step": dist, "step_bytes": step_bytes, "hbm_gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "kernels": form, "roofline": roofline}
+
+
+OTHER_WORKLOADS = [workloads.QWEN3_8B.name, workloads.QWEN3_32B.name, workloads.TINY.name]
 
 
 def main():
@@ -454,11 +553,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default=workloads.QWEN3_8B.name)
+    ap.add_argument("--workload", default=workloads.QWEN3_14B.name)
+    ap.add_argument("--others", default=",".join(OTHER_WORKLOADS),
+                    help="comma-separated workloads also timed (same protocol) and reported "
+                         "under 'other_workloads'; empty for none")
     ap.add_argument("--layers", type=int, default=0, help="layers rotated (0: auto)")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip the read-bandwidth probe")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--cpu-seqs", type=int, default=32)
@@ -491,44 +594,26 @@ def main():
     if w.page_size:
         run_paged(args, w)
         return
+    num_cu = torch.cuda.get_device_properties(0).multi_processor_count
     n_layers = layers_for(w, args.layers)
     log(f"workload {w.name}: {n_layers} layers rotated, step bytes "
         f"{w.bytes_sparse_step() / 2**20:.1f} MiB")
     layers = make_layers(w, n_layers, with_dense=not args.no_dense)
 
     # timed region: K steps of kin_sparse_decode_step back to back on one
-    # stream, one HIP event pair around all of them (events between the
-    # launches would add their own packets to every step).  When the step is
-    # one kernel, the average launch duration of that kernel is the same
-    # quotient: consecutive launches leave no gap (the profiler's kernel
-    # duration agrees).
-    ms, _ = time_steps(lambda i, b, e: sparse_step(w, i, b, None), layers, args.steps,
-                       args.warmup)
-    step_bytes = w.bytes_sparse_step()
-    gbs = step_bytes / (ms * 1e-3) / 1e9
-    num_cu = torch.cuda.get_device_properties(0).multi_processor_count
-    single = single_kernel(w, num_cu)
-    kern = {"one": "k_decode_step",
-            "one-split": "k_select_attend (one launch)",
-            "two": ("k_score_tiles + k_select_attend (two launches)" if w.dtype == "bf16"
-                    else "k_block_score + k_select_attend (two launches)"),
-            "four": "scores or newest row, top-k, attention, combine (four launches)"}[
-                step_kernels(w, num_cu)]
-    kbytes, kus = step_bytes, ms * 1000
-    achieved = kbytes / (kus * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "kernel": kern, "achieved": round(achieved, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": stored_traffic(w) if single else None, "bytes_per_launch": kbytes,
-                "avg_us": round(kus, 2)}
-
-    res = {"metric": METRIC, "value": round(w.batch / (ms * 1e-3), 1), "unit": "queries/s/layer",
-           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": w.dtype, "data": "synthetic",
+    # stream, one HIP event pair around all of them (measure()); the
+    # per-step spread comes from a second pass with an event between steps
+    m = measure(w, args, layers, num_cu)
+    res = {"metric": METRIC, "value": m["value"], "unit": "queries/s/layer",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": m["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
            "config": dict(w.describe(), layers_rotated=n_layers,
                           step_outputs="out, idx, S row (fp64 scores not written)"),
-           "step_bytes": step_bytes, "hbm_gbs": round(gbs, 1),
-           "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "roofline": roofline}
+           "per_step": m["per_step"], "step_bytes": m["step_bytes"], "hbm_gbs": m["hbm_gbs"],
+           "hbm_frac": m["hbm_frac"], "kernels": m["kernels"], "roofline": m["roofline"]}
+    gbs = m["hbm_gbs"]
+    ms = m["ms_per_step"]
 
     # the same step also writing the fp64 scores (an inspection output)
     sms, _ = time_steps(lambda i, b, e: sparse_step(w, i, b, None, scores=True), layers,
@@ -545,20 +630,15 @@ def main():
         ums, _ = time_steps(lambda i, b, e: unfused_step(w, i, b, e), layers, n, 2)
         res["four_call_ms_per_step"] = round(ums, 5)
 
+    dense_gbs = None
     if not args.no_dense:
         dms, _ = time_steps(lambda i, b, e: dense_step(w, i, b), layers,
                             max(5, args.steps // 5), 2)
         dbytes = w.bytes_dense()
+        dense_gbs = dbytes / (dms * 1e-3) / 1e9
         res["dense"] = {"queries_per_s": round(w.batch / (dms * 1e-3), 1),
-                        "ms_per_step": round(dms, 5),
-                        "hbm_gbs": round(dbytes / (dms * 1e-3) / 1e9, 1)}
+                        "ms_per_step": round(dms, 5), "hbm_gbs": round(dense_gbs, 1)}
         res["speedup_vs_dense"] = round(dms / ms, 2)
-
-    # the step against this device's measured read bandwidth as well
-    peak = read_peak()
-    res["read_peak"] = {"kernel": "k_read_probe", "gbs": round(peak, 1),
-                        "frac_of_published": round(peak / PEAK_HBM_GBS, 4),
-                        "step_frac": round(gbs / peak, 4)}
 
     if args.calib_copy:
         # a plain copy kernel of known size: reads 1 GiB and writes 1 GiB, so
@@ -569,9 +649,42 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         res["calib_copy_bytes"] = 2**30
+        del src, dst
 
+    cpu_layer = layers[0]
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(w, layers[0], args.cpu_seqs)
+        res["cpu_baseline"] = cpu_baseline(w, cpu_layer, args.cpu_seqs)
+    del layers, cpu_layer
+    torch.cuda.empty_cache()
+
+    # the other configurations, same protocol, one entry each
+    others = {}
+    for name in [x for x in args.others.split(",") if x]:
+        wo = workloads.by_name(name)
+        if wo.name == w.name:
+            continue
+        nl = layers_for(wo, args.layers)
+        lo = make_layers(wo, nl, with_dense=False)
+        mo = measure(wo, args, lo, num_cu)
+        mo["config"] = dict(wo.describe(), layers_rotated=nl)
+        others[wo.name] = mo
+        del lo
+        torch.cuda.empty_cache()
+    if others:
+        res["other_workloads"] = others
+
+    # the step against this device's measured streaming rate as well: the
+    # read probe, or the in-house dense attention when that streamed faster
+    if not args.no_probe:
+        peak = read_peak()
+        best, src = (peak, "k_read_probe")
+        if dense_gbs is not None and dense_gbs > best:
+            best, src = (dense_gbs, "dense attention (kin_dense_decode_attn)")
+        res["read_peak"] = {"probe_gbs": round(peak, 1),
+                            "dense_gbs": round(dense_gbs, 1) if dense_gbs else None,
+                            "gbs": round(best, 1), "source": src,
+                            "frac_of_published": round(best / PEAK_HBM_GBS, 4),
+                            "step_frac": round(gbs / best, 4)}
     print(json.dumps(res), flush=True)
 
 

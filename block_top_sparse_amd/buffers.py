@@ -22,10 +22,10 @@ class LayerBuffers:
         self.idx = torch.empty((w.batch, w.hkv, self.k), device=device, dtype=torch.int32)
         self.out = torch.empty((w.batch, w.hq, w.head_dim), device=device, dtype=dt)
         n = kb.kin_sparse_ws_bytes(self.desc, self.k)
-        self.ws = torch.empty(max(n, 16), device=device, dtype=torch.uint8) if n else None
+        self.ws = torch.zeros(max(n, 16), device=device, dtype=torch.uint8) if n else None
         self.out_dense = None
         self.ws_dense = None
         if with_dense:
             self.out_dense = torch.empty_like(self.out)
             nd = kb.kin_dense_ws_bytes(self.desc)
-            self.ws_dense = torch.empty(max(nd, 16), device=device, dtype=torch.uint8) if nd else None
+            self.ws_dense = torch.zeros(max(nd, 16), device=device, dtype=torch.uint8) if nd else None

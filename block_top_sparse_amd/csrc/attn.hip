@@ -84,8 +84,7 @@ template <int DT, int KPT, int MODE>
 __global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a0,
                                                                 const double *__restrict__ scores,
                                                                 int nb_cap, int32_t *idx_out,
-                                                                uint64_t *ctrl, uint32_t epoch,
-                                                                void *S_newest) {
+                                                                uint64_t *ctrl, void *S_newest) {
     constexpr int NW = kStepThreads / 64;
     __shared__ int32_t sel[kStepIdxCap];
     __shared__ union {
@@ -147,11 +146,9 @@ __global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a0,
     __shared__ uint32_t last;
     __syncthreads();
     if (threadIdx.x == 0) {
-        last = (epoch ? arrive_count(ctrl + pair, epoch, a.nsplit - 1)
-                      : arrive_add(ctrl + pair)) == (uint32_t)a.nsplit;
-        // every split of the pair has arrived: the word starts the next call
-        // at zero (a replayed graph repeats this call's round tag; zero
-        // matches no tag)
+        last = arrive_add(ctrl + pair) == (uint32_t)a.nsplit;
+        // every split of the pair has arrived: the word is left at zero for
+        // the next call (or graph replay) on this workspace
         if (last) st_agent(ctrl + pair, (uint64_t)0);
     }
     __syncthreads();
@@ -209,7 +206,7 @@ AttnPlan plan_attention(const Geo &g, int k, bool dense, int num_cu) {
     if (ns < 1) ns = 1;
     p.nsplit = ns;
     p.fused = 0;
-    p.ws_bytes = ws_for(g, ns);
+    p.ws_bytes = ws_total(ws_for(g, ns));
     return p;
 }
 
@@ -227,12 +224,22 @@ AttnPlan plan_step(const Geo &g, int k, int num_cu) {
     const int max_ns = p.n_chunks / 8;
     if (ns > max_ns) ns = max_ns;
     if (ns > 64) ns = 64;
-    if (ns < 1) ns = 1;
+    // one arrival word per pair for the in-kernel combine
+    if (ns < 1 || g.pairs > kCtrlWords) ns = 1;
     p.nsplit = ns;
     p.fused = 1;
-    // split partials, then one arrival word per pair for the in-kernel combine
-    p.ws_bytes = ns == 1 ? 0 : align256(ws_for(g, ns)) + (size_t)g.pairs * sizeof(uint64_t);
+    // the arrival words, then the split partials
+    p.ws_bytes = ws_total(ws_for(g, ns));
     return p;
+}
+
+double *step_scores_in_ws(const Geo &g, const AttnPlan &p, void *ws) {
+    return reinterpret_cast<double *>(ws_body(ws) + align256(ws_for(g, p.nsplit)));
+}
+
+size_t step_ws_with_scores(const Geo &g, const AttnPlan &p) {
+    return kCtrlBytes + align256(ws_for(g, p.nsplit)) +
+           (size_t)g.pairs * (size_t)g.nb_cap * sizeof(double);
 }
 
 static hipError_t launch_combine(const Geo &g, const AttnArgs &a, void *out, int nsplit,
@@ -269,11 +276,10 @@ hipError_t launch_attention(const Geo &g, const AttnPlan &p, const void *q, cons
 
 template <int DT>
 static void launch_sa(const Geo &g, const AttnArgs &a, dim3 grid, const double *scores,
-                      int32_t *idx, uint64_t *ctrl, uint32_t epoch, void *S_newest,
-                      hipStream_t s) {
+                      int32_t *idx, uint64_t *ctrl, void *S_newest, hipStream_t s) {
 #define KIN_SA_MODE(KPT, MODE)                                                                 \
     k_select_attend<DT, KPT, MODE><<<grid, kStepThreads, 0, s>>>(a, scores, g.nb_cap, idx, ctrl, \
-                                                                 epoch, S_newest)
+                                                                 S_newest)
 #define KIN_SA(KPT)                                                                            \
     (DT != KIN_BF16 ? KIN_SA_MODE(KPT, kContig)                                                \
      : g.pages      ? KIN_SA_MODE(KPT, (DT == KIN_BF16 ? kPaged : kContig))                    \
@@ -291,16 +297,15 @@ static void launch_sa(const Geo &g, const AttnArgs &a, dim3 grid, const double *
 #undef KIN_SA_MODE
 }
 
-// one arrival word per pair after the split partials (combined in-kernel)
-uint64_t *step_ctrl(const Geo &g, const AttnPlan &p, void *ws) {
+// one arrival word per pair at the start of the workspace (combined in-kernel)
+uint64_t *step_ctrl(const AttnPlan &p, void *ws) {
     if (!p.fused || p.nsplit <= 1) return nullptr;
-    return reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + align256(ws_for(g, p.nsplit)));
+    return static_cast<uint64_t *>(ws);
 }
 
 hipError_t launch_select_attend(const Geo &g, const AttnPlan &p, const void *q, const void *K,
                                 const void *V, const double *scores, int k, int32_t *idx,
-                                void *out, void *ws, uint32_t epoch, hipStream_t s,
-                                void *S_newest) {
+                                void *out, void *ws, hipStream_t s, void *S_newest) {
     if (!p.fused) {
         hipError_t e = launch_block_topk(g, scores, k, idx, s);
         if (e != hipSuccess) return e;
@@ -308,12 +313,12 @@ hipError_t launch_select_attend(const Geo &g, const AttnPlan &p, const void *q, 
     }
     AttnArgs a;
     fill_args(a, g, p, q, K, V, nullptr, k, out, ws);
-    uint64_t *ctrl = step_ctrl(g, p, ws);
+    uint64_t *ctrl = step_ctrl(p, ws);
     dim3 grid(p.nsplit, g.pairs);
     if (g.dtype == KIN_BF16)
-        launch_sa<KIN_BF16>(g, a, grid, scores, idx, ctrl, epoch, S_newest, s);
+        launch_sa<KIN_BF16>(g, a, grid, scores, idx, ctrl, S_newest, s);
     else
-        launch_sa<KIN_F32>(g, a, grid, scores, idx, ctrl, epoch, nullptr, s);
+        launch_sa<KIN_F32>(g, a, grid, scores, idx, ctrl, nullptr, s);
     return hipGetLastError();
 }
 

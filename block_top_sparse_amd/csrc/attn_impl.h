@@ -264,26 +264,9 @@ __device__ __forceinline__ void stores_complete() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Count this workgroup's arrival at *ctr in round `epoch` (ctr holds
-// epoch << 32 | count; a word left by another round counts as zero, so the
-// word needs no clearing between calls).  Returns the count including this
-// arrival.  The first compare-and-swap assumes the word already counts
-// `others` arrivals of this round: right for the last arrival once the
-// others are done, which then takes a single round trip (a wrong guess
-// only costs a retry with the value the swap returned).
-__device__ inline uint32_t arrive_count(uint64_t *ctr, uint32_t epoch, uint32_t others) {
-    uint64_t old = ((uint64_t)epoch << 32) | others;
-    for (;;) {
-        const uint32_t c = (uint32_t)(old >> 32) == epoch ? (uint32_t)old + 1u : 1u;
-        const uint64_t next = ((uint64_t)epoch << 32) | c;
-        if (__hip_atomic_compare_exchange_weak(ctr, &old, next, __ATOMIC_RELAXED,
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-            return c;
-    }
-}
-
-// Count an arrival at *ctr, a word that an earlier kernel on the stream set
-// to zero: one atomic round trip.
+// Count an arrival at *ctr, a word that was zero when the launch began
+// (cleared by an earlier kernel on the stream, or left at zero by the
+// previous call's last arrival): one atomic round trip.
 __device__ inline uint32_t arrive_add(uint64_t *ctr) {
     return (uint32_t)__hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT) + 1u;
@@ -776,7 +759,6 @@ __device__ void load_q_f32(const AttnArgs &a, int pair, F32Lds<NW> &fl) {
     }
 }
 
-// Kernel arguments from a validated geometry and plan (host side).
 // Bytes of the split partials (o, then m and l) of one attention call.
 inline size_t ws_for(const Geo &g, int ns) {
     return ns == 1 ? 0 : (size_t)g.batch * g.hq * ns * (kHeadDim + 2) * sizeof(float);
@@ -784,6 +766,7 @@ inline size_t ws_for(const Geo &g, int ns) {
 
 inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
+// Kernel arguments from a validated geometry and plan (host side).
 inline void fill_args(AttnArgs &a, const Geo &g, const AttnPlan &p, const void *q, const void *K,
                       const void *V, const int32_t *idx, int k, void *out, void *ws) {
     a.q = q;
@@ -791,7 +774,8 @@ inline void fill_args(AttnArgs &a, const Geo &g, const AttnPlan &p, const void *
     a.V = V;
     a.idx = idx;
     a.out = out;
-    a.ws_o = static_cast<float *>(ws);
+    // the partials follow the workspace's arrival words
+    a.ws_o = reinterpret_cast<float *>(ws_body(ws));
     a.ws_ml = p.nsplit > 1 ? a.ws_o + (size_t)g.batch * g.hq * p.nsplit * kHeadDim : nullptr;
     a.hkv = g.hkv;
     a.gqa = g.gqa;

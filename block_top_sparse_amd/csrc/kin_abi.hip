@@ -7,7 +7,6 @@
 #include <string.h>
 
 #include <atomic>
-#include <chrono>
 
 #include "kin_internal.h"
 
@@ -116,24 +115,6 @@ static kin_status check_ws_size(size_t need, const void *ws, size_t ws_bytes) {
 
 static kin_status check_ws(const kin::AttnPlan &p, const void *ws, size_t ws_bytes) {
     return check_ws_size(p.ws_bytes, ws, ws_bytes);
-}
-
-// Round tag of one split select + attend launch: the arrival words in the
-// workspace count only when they carry the current call's tag, so the
-// workspace needs no clearing.  Starts at a per-process value so that a
-// workspace left by another process is unlikely to match.
-static uint32_t next_epoch() {
-    static std::atomic<uint32_t> epoch{
-        (uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() | 1u};
-    uint32_t e = epoch.fetch_add(2u);
-    return e ? e : epoch.fetch_add(2u);
-}
-
-// Workspace of the two-kernel decode step when the caller passes no scores
-// buffer: the attention plan's bytes, then the pair-major fp64 scores.
-static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
-static size_t step_scores_bytes(const kin::Geo &g) {
-    return (size_t)g.pairs * (size_t)g.nb_cap * sizeof(double);
 }
 
 extern "C" {
@@ -247,7 +228,7 @@ kin_status kin_decode_select_attend(const kin_desc *desc, const void *q, const v
     st = check_ws(p, ws, ws_bytes);
     if (st != KIN_OK) return st;
     return launched(kin::launch_select_attend(g, p, q, K, V, scores, k, idx, out, ws,
-                                              next_epoch(), (hipStream_t)stream),
+                                              (hipStream_t)stream),
                     "kin_decode_select_attend");
 }
 
@@ -273,28 +254,22 @@ static kin_status decode_step(const kin::Geo &g, const void *q, const void *K, c
     const kin::AttnPlan p = kin::plan_step(g, k, cu);
     // two kernels hand the scores over in memory: the caller's buffer, or
     // the workspace after the attention's part
-    const size_t need = scores ? p.ws_bytes : align256(p.ws_bytes) + step_scores_bytes(g);
+    const size_t need = scores ? p.ws_bytes : kin::step_ws_with_scores(g, p);
     st = check_ws_size(need, ws, ws_bytes);
     if (st != KIN_OK) return st;
-    double *sc = scores ? scores
-                        : reinterpret_cast<double *>(static_cast<char *>(ws) +
-                                                     align256(p.ws_bytes));
+    double *sc = scores ? scores : kin::step_scores_in_ws(g, p, ws);
     // every block kept and no scores wanted: only the newest summary row is
     // rebuilt, by the fused second half itself (its split partials then count
-    // their arrivals with the call's round tag)
+    // their arrivals in words the previous call on this workspace left at
+    // zero)
     const bool newest_only = !scores && k >= g.nb && g.dtype == KIN_BF16;
     if (newest_only && p.fused)
-        return launched(kin::launch_select_attend(g, p, q, K, V, sc, k, idx, out, ws,
-                                                  next_epoch(), s, S),
+        return launched(kin::launch_select_attend(g, p, q, K, V, sc, k, idx, out, ws, s, S),
                         "kin_sparse_decode_step");
-    // the bf16 scoring kernel also clears the second kernel's arrival words;
-    // the fp32 one does not, so there the splits count with a round tag
-    const bool clears = g.dtype == KIN_BF16;
+    // the scoring kernel also clears the second kernel's arrival words
     hipError_t e = kin::launch_update_and_score(g, q, K, S, sc, cu, s, newest_only,
-                                                clears ? kin::step_ctrl(g, p, ws) : nullptr);
-    if (e == hipSuccess)
-        e = kin::launch_select_attend(g, p, q, K, V, sc, k, idx, out, ws,
-                                      clears ? 0u : next_epoch(), s);
+                                                kin::step_ctrl(p, ws));
+    if (e == hipSuccess) e = kin::launch_select_attend(g, p, q, K, V, sc, k, idx, out, ws, s);
     return launched(e, "kin_sparse_decode_step");
 }
 
@@ -444,13 +419,11 @@ kin_status kin_quest_decode_step(const kin_desc *desc, const void *q, const void
         return launched(kin::launch_decode_step(g, q, K, V, Sq, scores, k, idx, out, cu, s, true),
                         "kin_quest_decode_step");
     const kin::AttnPlan p = kin::plan_step(g, k, cu);
-    st = check_ws_size(align256(p.ws_bytes) + (scores ? 0 : step_scores_bytes(g)), ws, ws_bytes);
+    st = check_ws_size(scores ? p.ws_bytes : kin::step_ws_with_scores(g, p), ws, ws_bytes);
     if (st != KIN_OK) return st;
-    double *sc = scores ? scores
-                        : reinterpret_cast<double *>(static_cast<char *>(ws) +
-                                                     align256(p.ws_bytes));
-    hipError_t e = kin::launch_quest_score(g, q, K, Sq, sc, cu, kin::step_ctrl(g, p, ws), true, s);
-    if (e == hipSuccess) e = kin::launch_select_attend(g, p, q, K, V, sc, k, idx, out, ws, 0u, s);
+    double *sc = scores ? scores : kin::step_scores_in_ws(g, p, ws);
+    hipError_t e = kin::launch_quest_score(g, q, K, Sq, sc, cu, kin::step_ctrl(p, ws), true, s);
+    if (e == hipSuccess) e = kin::launch_select_attend(g, p, q, K, V, sc, k, idx, out, ws, s);
     return launched(e, "kin_quest_decode_step");
 }
 
@@ -461,7 +434,7 @@ size_t kin_quest_ws_bytes(const kin_desc *desc, int32_t k) {
         fail(KIN_ERR_SHAPE, "k = %d: need 1 <= k <= %d", k, kin::kStepIdxCap);
         return (size_t)-1;
     }
-    return align256(kin::plan_step(g, k, num_cu()).ws_bytes) + step_scores_bytes(g);
+    return kin::step_ws_with_scores(g, kin::plan_step(g, k, num_cu()));
 }
 
 // Token-level step: the descriptor with block 1 (every token its own block).
@@ -522,9 +495,8 @@ size_t kin_sparse_ws_bytes(const kin_desc *desc, int32_t k) {
     const int cu = num_cu();
     const size_t a = kin::plan_attention(g, k, false, cu).ws_bytes;
     // the step's two-kernel form, with room for the scores (scores == NULL)
-    const size_t b = kin::step_single_kernel(g, k, cu)
-                         ? 0
-                         : align256(kin::plan_step(g, k, cu).ws_bytes) + step_scores_bytes(g);
+    const size_t b =
+        kin::step_single_kernel(g, k, cu) ? 0 : kin::step_ws_with_scores(g, kin::plan_step(g, k, cu));
     return a > b ? a : b;
 }
 

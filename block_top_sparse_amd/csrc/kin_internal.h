@@ -18,6 +18,18 @@ constexpr int kStepIdxCap = 2048;  // kept blocks the select+attend kernels hold
 constexpr int kTokIdxCap = 8192;   // kept tokens of the token-level step (LDS)
 constexpr int kTokMaxLen = 262144;  // tokens of one pair the two-kernel token step takes
 
+// Every workspace starts with kCtrlWords 64-bit arrival words (one per pair
+// of a split launch, which runs only with fewer pairs than compute units):
+// the caller zeroes a workspace once, and every call leaves these words at
+// zero when it completes.  The rest of the workspace (partials, handed-over
+// scores) follows them.
+constexpr int kCtrlWords = 1024;
+constexpr size_t kCtrlBytes = (size_t)kCtrlWords * sizeof(uint64_t);
+// bytes of a workspace whose part after the arrival words is `body` bytes
+inline size_t ws_total(size_t body) { return body ? kCtrlBytes + body : 0; }
+// the part of a workspace after its arrival words
+inline char *ws_body(void *ws) { return ws ? static_cast<char *>(ws) + kCtrlBytes : nullptr; }
+
 // Geometry shared by the launchers (all derived from a validated desc).
 struct Geo {
     int batch, hkv, gqa, hq, t_cap, ctx_len, block, dtype;
@@ -65,19 +77,24 @@ hipError_t launch_attention(const Geo &g, const AttnPlan &p, const void *q, cons
 // decode step, second half: top-k selection + sparse attention, fused per
 // pair when the plan allows it (plan_step); otherwise separate launches
 AttnPlan plan_step(const Geo &g, int k, int num_cu);
-// (epoch: the call's round tag for the in-kernel combine of split partials;
-// 0: the arrival words at step_ctrl() were cleared by an earlier kernel;
-// S_newest: with a fused plan that keeps every block, bf16, the summaries
-// whose newest row the kernel rebuilds, so that no first half is needed)
+// (the splits of a pair count their arrivals in the pair's word at
+// step_ctrl(), which is zero on entry: cleared by an earlier kernel of the
+// step or left at zero by the previous call; S_newest: with a fused plan
+// that keeps every block, bf16, the summaries whose newest row the kernel
+// rebuilds, so that no first half is needed)
 hipError_t launch_select_attend(const Geo &g, const AttnPlan &p, const void *q, const void *K,
                                 const void *V, const double *scores, int k, int32_t *idx,
-                                void *out, void *ws, uint32_t epoch, hipStream_t s,
-                                void *S_newest = nullptr);
+                                void *out, void *ws, hipStream_t s, void *S_newest = nullptr);
 // the whole decode step in one kernel (one workgroup per pair); usable when
 // step_single_kernel() says so (bf16, enough pairs to cover the chip)
 bool step_single_kernel(const Geo &g, int k, int num_cu);
-// the arrival words of a plan's in-kernel combine inside ws (nullptr: none)
-uint64_t *step_ctrl(const Geo &g, const AttnPlan &p, void *ws);
+// the arrival words of a plan's in-kernel combine (the start of ws;
+// nullptr: the plan has none)
+uint64_t *step_ctrl(const AttnPlan &p, void *ws);
+// where a two-kernel step keeps its fp64 scores in ws when the caller
+// passes no scores buffer, and the workspace bytes that form needs
+double *step_scores_in_ws(const Geo &g, const AttnPlan &p, void *ws);
+size_t step_ws_with_scores(const Geo &g, const AttnPlan &p);
 // Quest-style summaries ([pair][nb_cap][2][head_dim]: minimum, maximum) of
 // blocks [j0, j1), and the decode step's first kernel with the Quest bound
 // (update: the newest block's rows rebuilt first); bf16

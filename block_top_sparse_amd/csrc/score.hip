@@ -118,7 +118,8 @@ __global__ __launch_bounds__(256) void k_block_score(const void *__restrict__ qv
                                                      const void *__restrict__ Kv, void *Sv,
                                                      double *__restrict__ scores, int hkv,
                                                      int gqa, int t_cap, int nb_cap, int nb,
-                                                     int ctx_len, int block) {
+                                                     int ctx_len, int block,
+                                                     uint64_t *ctrl_zero) {
     constexpr int kBlocksPerWave = 16 * TPW;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int sub = lane & 15;  // channel slice: channels 8*sub .. 8*sub+7
@@ -127,6 +128,9 @@ __global__ __launch_bounds__(256) void k_block_score(const void *__restrict__ qv
     const int b = pair / hkv, g = pair % hkv;
     const size_t row0 = (size_t)pair * nb_cap;
     const int newest = nb - 1;
+    // the pair's arrival word for the next kernel's in-kernel combine starts
+    // at zero (kernels on one stream run in order)
+    if (ctrl_zero && blockIdx.x == 0 && threadIdx.x == 0) ctrl_zero[pair] = 0ull;
 
     if (UPDATE && blockIdx.x == 0) {
         __shared__ uint32_t row_lds[kHeadDim];
@@ -185,7 +189,7 @@ __global__ __launch_bounds__(256) void k_block_score(const void *__restrict__ qv
 
 template <int DT, bool UPDATE>
 static hipError_t launch_dt(const Geo &g, const void *q, const void *K, void *S, double *scores,
-                            hipStream_t s) {
+                            hipStream_t s, uint64_t *ctrl_zero) {
     // blocks per workgroup = 4 waves x 16 x TPW; smaller workgroups when the
     // problem is small so the grid still covers the chip
     const long long total = (long long)g.pairs * g.nb;
@@ -193,7 +197,7 @@ static hipError_t launch_dt(const Geo &g, const void *q, const void *K, void *S,
 #define KIN_SCORE_LAUNCH(TPW)                                                                    \
     k_block_score<DT, TPW, UPDATE><<<dim3((g.nb + 64 * TPW - 1) / (64 * TPW) + extra, g.pairs), \
                                      256, 0, s>>>(q, K, S, scores, g.hkv, g.gqa, g.t_cap,         \
-                                                  g.nb_cap, g.nb, g.ctx_len, g.block)
+                                                  g.nb_cap, g.nb, g.ctx_len, g.block, ctrl_zero)
     if (total >= 2048LL * 256)
         KIN_SCORE_LAUNCH(4);
     else if (total >= 2048LL * 128)
@@ -209,7 +213,7 @@ hipError_t launch_block_score(const Geo &g, const void *q, const void *S, double
     void *Sm = const_cast<void *>(S);  // not written without UPDATE
     return g.dtype == KIN_BF16
                ? launch_tiles(g, false, q, nullptr, Sm, scores, num_cu, s, false, nullptr)
-                               : launch_dt<KIN_F32, false>(g, q, nullptr, Sm, scores, s);
+                               : launch_dt<KIN_F32, false>(g, q, nullptr, Sm, scores, s, nullptr);
 }
 
 hipError_t launch_update_and_score(const Geo &g, const void *q, const void *K, void *S,
@@ -217,7 +221,7 @@ hipError_t launch_update_and_score(const Geo &g, const void *q, const void *K, v
                                    uint64_t *ctrl_zero) {
     return g.dtype == KIN_BF16 ? launch_tiles(g, true, q, K, S, scores, num_cu, s, newest_only,
                                               ctrl_zero)
-                               : launch_dt<KIN_F32, true>(g, q, K, S, scores, s);
+                               : launch_dt<KIN_F32, true>(g, q, K, S, scores, s, ctrl_zero);
 }
 
 }  // namespace kin

@@ -130,8 +130,12 @@ __global__ __launch_bounds__(kStepThreads) void k_tok_select_attend(AttnArgs a,
     stores_complete();
     __shared__ uint32_t last;
     __syncthreads();
-    // the arrival words were cleared by kernel 1
-    if (threadIdx.x == 0) last = arrive_add(ctrl + pair) == (uint32_t)a.nsplit;
+    // the arrival words were cleared by kernel 1; the last arrival leaves its
+    // word at zero again, as every call on a workspace does
+    if (threadIdx.x == 0) {
+        last = arrive_add(ctrl + pair) == (uint32_t)a.nsplit;
+        if (last) st_agent(ctrl + pair, (uint64_t)0);
+    }
     __syncthreads();
     if (last) combine_pair<KIN_BF16, kStepThreads>(a, pair);
 }
@@ -212,15 +216,15 @@ static void tok_tiles(const Geo &g, int num_cu, int &tiles, int &rows) {
     tiles = (g.ctx_len + rows - 1) / rows;
 }
 
-// Workspace of the two-kernel token step: split partials, arrival words,
-// the keys' top words, count tables (in that order, each 256-byte aligned).
+// Workspace of the two-kernel token step after its arrival words: split
+// partials, the keys' top words, count tables (in that order, each 256-byte
+// aligned; offsets from ws_body).
 struct TokWs {
-    size_t ctrl, keys, tables, total;
+    size_t keys, tables, total;
 };
 static TokWs tok_ws(const Geo &g, int nsplit, int tiles) {
     TokWs w;
-    w.ctrl = align256(ws_for(g, nsplit));
-    w.keys = align256(w.ctrl + (nsplit > 1 ? (size_t)g.pairs * sizeof(uint64_t) : 0));
+    w.keys = align256(ws_for(g, nsplit));
     w.tables = align256(w.keys + (size_t)g.pairs * g.t_cap * sizeof(uint32_t));
     w.total = w.tables + (size_t)g.pairs * tiles * kExpBins * sizeof(uint32_t);
     return w;
@@ -236,12 +240,13 @@ AttnPlan plan_tok(const Geo &g, int k, int num_cu) {
     const int max_ns = p.n_chunks / 8;
     if (ns > max_ns) ns = max_ns;
     if (ns > 64) ns = 64;
-    if (ns < 1) ns = 1;
+    // one arrival word per pair for the in-kernel combine
+    if (ns < 1 || g.pairs > kCtrlWords) ns = 1;
     p.nsplit = ns;
     p.fused = 1;
     int tiles, rows;
     tok_tiles(g, num_cu, tiles, rows);
-    p.ws_bytes = tok_ws(g, ns, tiles).total;
+    p.ws_bytes = ws_total(tok_ws(g, ns, tiles).total);
     return p;
 }
 
@@ -264,8 +269,9 @@ hipError_t launch_tok_step(const Geo &g0, const void *q, const void *K, const vo
     int tiles, rows;
     tok_tiles(g, num_cu, tiles, rows);
     const TokWs wl = tok_ws(g, p.nsplit, tiles);
-    char *w = static_cast<char *>(ws);
-    uint64_t *ctrl = p.nsplit > 1 ? reinterpret_cast<uint64_t *>(w + wl.ctrl) : nullptr;
+    char *w = ws_body(ws);
+    // the arrival words: the start of the workspace (cleared by kernel 1)
+    uint64_t *ctrl = p.nsplit > 1 ? static_cast<uint64_t *>(ws) : nullptr;
     uint32_t *keys = reinterpret_cast<uint32_t *>(w + wl.keys);
     uint32_t *tables = reinterpret_cast<uint32_t *>(w + wl.tables);
     AttnArgs a;

@@ -55,9 +55,16 @@
  *   - Pointers must be 16-byte aligned.  The values read must be finite.
  *   - No C++ exception crosses this interface.
  *   - The calls launch kernels only (no memset, copy or allocation), so they
- *     can be captured into a HIP graph and replayed; a workspace carries no
- *     state from one call or replay to the next that it needs cleared.  Calls
- *     that overlap in time must not share a workspace.
+ *     can be captured into a HIP graph and replayed.
+ *   - Workspaces (`ws`): a workspace must be ZERO-FILLED ONCE before its
+ *     first use (hipMemset, or a zero-initialised allocation).  Its first
+ *     8 KiB hold one 64-bit arrival word per (sequence, KV head) pair, in
+ *     which the workgroups that split a pair's kept blocks count themselves
+ *     so that the last one combines their partial results; every call
+ *     leaves those words at zero when it completes, so a workspace zeroed
+ *     once stays valid for every later call and graph replay, of any shape,
+ *     through any entry point.  The rest of a workspace needs no clearing.
+ *     Calls that overlap in time must not share a workspace.
  */
 #ifndef KIN_H
 #define KIN_H
@@ -107,6 +114,13 @@ typedef struct kin_desc {
 } kin_desc;
 
 /* Block summaries (the block representative: mean key).
+ * Defining passages: the skill summary page "Kinetics: Memory-Aware
+ * Test-Time Scaling", section "Implementation" (BlockTopKAttention divides
+ * the sequence into blocks and ranks each block by the mean of its
+ * attention scores; for one query that mean equals q . (mean key of the
+ * block), so the mean key is the block's representative), and the rebuttal
+ * page "Kinetics: Rethinking Test-Time Scaling Law", answer "Q4: KV block
+ * size and grouping strategy" (blocks of 16, 32 or 64 KV tokens).
  * Recomputes from scratch every block that intersects [t_begin, t_end) and
  * [0, ctx_len): S[b][g][j][c] = round(sum_{t in block j, t < ctx_len}
  * K[b][g][t][c] / n_j), n_j = min(block, ctx_len - j*block), the sum taken
@@ -118,33 +132,57 @@ typedef struct kin_desc {
 KIN_API kin_status kin_block_summary_update(const kin_desc *desc, const void *K, void *S,
                                     int32_t t_begin, int32_t t_end, kin_stream stream);
 
-/* Block scores.  scores[b][g][j] = sum over the group's query heads h
+/* Block scores.  Defining passages: the skill summary page "Kinetics:
+ * Memory-Aware Test-Time Scaling", section "Implementation" (the mean score
+ * per block of BlockTopKAttention, which ranks the blocks), and the
+ * rebuttal page "Kinetics: Rethinking Test-Time Scaling Law", answer "Q4:
+ * KV block size and grouping strategy" (Block-TopK groups the KV cache into
+ * fixed-size blocks and scores each block as a whole).  The pages do not
+ * say how a GQA group's heads combine; the reading taken is the sum of the
+ * heads' scores, one selection per KV head.
+ * scores[b][g][j] = sum over the group's query heads h
  * (h / gqa == g) of q[b][h] . S[b][g][j], in fp64, for j < nb; -0.0 is
  * written as +0.0.  Entries j >= nb are not written.
  * Errors: NULL pointers, shape. */
 KIN_API kin_status kin_block_score(const kin_desc *desc, const void *q, const void *S, double *scores,
                            kin_stream stream);
 
-/* Top-k block selection.  idx[b][g][0..k) = the min(k, nb) block indices
+/* Top-k block selection.  Defining passages: the skill summary page
+ * "Kinetics: Memory-Aware Test-Time Scaling", section "Implementation"
+ * (BlockTopKAttention keeps the top-k blocks by their block scores), and the
+ * rebuttal page "Kinetics: Rethinking Test-Time Scaling Law", answer "Q4: KV
+ * block size and grouping strategy" (the KV budget is block size x number of
+ * kept blocks, e.g. (16, 64), (32, 32), (64, 16) for 1024 tokens).
+ * idx[b][g][0..k) = the min(k, nb) block indices
  * with the largest scores, ties to the lower index, in ascending order,
  * followed by -1 when k > nb.  Only scores[b][g][0..nb) are read.
  * Errors: NULL pointers; k < 1; nb > 16384 (unsupported). */
 KIN_API kin_status kin_block_topk(const kin_desc *desc, const double *scores, int32_t k, int32_t *idx,
                           kin_stream stream);
 
-/* Sparse decode attention.  For each query head h of KV head g:
+/* Sparse decode attention.  Defining passage: the skill summary page
+ * "Kinetics: Memory-Aware Test-Time Scaling", section "Implementation"
+ * (BlockTopKAttention masks every token outside the kept blocks, then takes
+ * the softmax of q.k / sqrt(d) and multiplies by V; the masked tokens have
+ * weight zero, so the result is the softmax over the kept tokens alone).
+ * For each query head h of KV head g:
  * out[b][h] = sum_t softmax_t(q[b][h] . K[b][g][t] / sqrt(head_dim)) V[b][g][t]
  * over the tokens t < ctx_len of the blocks listed in idx[b][g][0..k)
  * (entries < 0 or >= nb are skipped).  Accumulation is fp32.
  * `ws` is scratch of at least kin_sparse_ws_bytes(desc, k) bytes (may be
- * NULL when that is 0); its contents on entry do not matter.
+ * NULL when that is 0), zero-filled once before its first use (see the
+ * conventions above).
  * Errors: NULL pointers, shape, workspace. */
 KIN_API kin_status kin_sparse_decode_attn(const kin_desc *desc, const void *q, const void *K,
                                   const void *V, const int32_t *idx, int32_t k, void *out,
                                   void *ws, size_t ws_bytes, kin_stream stream);
 
-/* Dense decode attention over every token in [0, ctx_len): the comparison
- * the pages measure Block-TopK against.  Same conventions as above. */
+/* Dense decode attention over every token in [0, ctx_len).  Defining
+ * passage: the rebuttal page "Kinetics: Rethinking Test-Time Scaling Law",
+ * answer "W2 & Q2: Real-world latency benchmarks" (decode latency per step
+ * of dense attention against Block-TopK at a 32K-token KV cache): this is
+ * that dense comparison, the same softmax(q.k / sqrt(d)) . v over every
+ * token.  Same conventions as kin_sparse_decode_attn. */
 KIN_API kin_status kin_dense_decode_attn(const kin_desc *desc, const void *q, const void *K,
                                  const void *V, void *out, void *ws, size_t ws_bytes,
                                  kin_stream stream);

@@ -1,7 +1,8 @@
 """The decode steps captured in a HIP graph (torch.cuda.CUDAGraph) and
 replayed: the library allocates nothing, never synchronises and records no
-memset, so a captured step replays; a replay repeats the round tag chosen at
-capture, so the split forms must leave their arrival words ready for it.
+memset, so a captured step replays; the split forms count their
+workgroups' arrivals in workspace words that each call (and each replay)
+must leave at zero for the next one.
 Each form is replayed four times back to back, with new query values
 written eagerly before each replay, and every replay must equal an eager
 call on the same inputs bit for bit."""
@@ -31,8 +32,8 @@ def _need_gpu():
 
 def _check_replays(call, q, outs, seed):
     """Replays back to back (new queries written eagerly before each, no
-    eager step in between, so each replay finds the words the previous
-    replay left with the same round tag), then the eager references."""
+    eager step in between, so each replay finds the arrival words exactly
+    as the previous replay left them), then the eager references."""
     call()  # eager warm-up (the library caches the device's CU count)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -61,8 +62,8 @@ BLOCK = [
     # name, batch, hq, hkv, ctx, block, k, dtype, t_cap, scores
     ("graph-one-kernel", 64, 16, 4, 2000, 16, 20, "bf16", 2048, False),   # 256 pairs
     ("graph-two-kernel", 3, 16, 2, 5000, 16, 100, "bf16", 5120, True),
-    ("graph-keepall", 2, 16, 4, 2000, 16, 125, "bf16", 2048, False),       # round-tagged splits
-    ("graph-f32-split", 3, 2, 2, 4730, 16, 292, "f32", 4793, True),        # round-tagged splits
+    ("graph-keepall", 2, 16, 4, 2000, 16, 125, "bf16", 2048, False),       # one launch, splits
+    ("graph-f32-split", 3, 2, 2, 4730, 16, 292, "f32", 4793, True),        # fp32 split step
 ]
 
 
@@ -91,7 +92,7 @@ def test_token_step_replayed_from_a_graph():
     desc = kb.make_desc(w.batch, w.hkv, w.gqa, w.cap, w.ctx_len, 1, torch.bfloat16)
     idx = torch.empty((w.batch, w.hkv, 500), dtype=torch.int32, device="cuda")
     out = torch.empty((w.batch, w.hq, 128), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(kb.kin_token_ws_bytes(desc, 500), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(kb.kin_token_ws_bytes(desc, 500), dtype=torch.uint8, device="cuda")
     _check_replays(lambda: kb.kin_token_decode_step(desc, inp["q"], inp["K"], inp["V"], None,
                                                     500, idx, out, ws),
                    inp["q"], lambda: (idx, out), 915)
@@ -106,7 +107,7 @@ def test_quest_step_replayed_from_a_graph():
     kb.kin_quest_summary_update(desc, inp["K"], Sq, 0, w.ctx_len)
     idx = torch.empty((w.batch, w.hkv, 60), dtype=torch.int32, device="cuda")
     out = torch.empty((w.batch, w.hq, 128), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(kb.kin_quest_ws_bytes(desc, 60), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(kb.kin_quest_ws_bytes(desc, 60), dtype=torch.uint8, device="cuda")
     _check_replays(lambda: kb.kin_quest_decode_step(desc, inp["q"], inp["K"], inp["V"], Sq, None,
                                                     60, idx, out, ws),
                    inp["q"], lambda: (idx, out), 916)
@@ -114,7 +115,7 @@ def test_quest_step_replayed_from_a_graph():
 
 def test_paged_keepall_step_replayed_from_a_graph():
     """Variable lengths in a paged pool, few pairs, every block kept and no
-    scores: the one-launch form with round-tagged splits."""
+    scores: the one-launch form whose splits count in words left at zero."""
     from test_paged_gpu import Case
 
     c = Case("graph-paged-keepall", 3, 2, 4, 16, 64, 600, 40, "rand")
@@ -137,7 +138,7 @@ def test_shared_prompt_step_replayed_from_a_graph():
     kb.kin_block_summary_update(c["desc"], c["K"], S, P, w.ctx_len)
     idx = torch.empty((w.batch, w.hkv, k), dtype=torch.int32, device="cuda")
     out = torch.empty((w.batch, w.hq, 128), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(max(kb.kin_sparse_ws_bytes(c["desc"], k), 16), dtype=torch.uint8,
+    ws = torch.zeros(max(kb.kin_sparse_ws_bytes(c["desc"], k), 16), dtype=torch.uint8,
                      device="cuda")
     share = kb.make_share(c["n_share"], P, c["Kp"], c["Vp"], c["Sp"])
 

@@ -100,7 +100,7 @@ class Case:
         self.idx = torch.empty((batch, hkv, k), dtype=torch.int32, device="cuda")
         self.out = torch.empty((batch, hkv * gqa, 128), dtype=torch.bfloat16, device="cuda")
         n = kb.kin_sparse_ws_bytes(self.desc, k)
-        self.ws = torch.empty(max(n, 16), dtype=torch.uint8, device="cuda")
+        self.ws = torch.zeros(max(n, 16), dtype=torch.uint8, device="cuda")
 
     def pages(self, paged=True, varlen=True):
         return kb.make_pages(self.lens_t if varlen else None, self.table if paged else None,

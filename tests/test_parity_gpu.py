@@ -240,9 +240,9 @@ F32_SPLIT = [
 @pytest.mark.parametrize("case", F32_SPLIT, ids=[c[0] for c in F32_SPLIT])
 def test_f32_two_kernel_step_splits_on_a_stale_workspace(case):
     """The fp32 two-kernel step with its attention split over several
-    workgroups per pair: the splits' arrivals are counted with a round tag,
-    so a workspace holding bytes of earlier calls (here all ones, then the
-    first call's own) gives the same result."""
+    workgroups per pair: its scoring kernel clears the arrival words the
+    splits count in, so even a workspace holding other bytes (here all ones,
+    then the first call's own) gives the same result."""
     name, b, hq, hkv, L, B, k, dt, cap = case
     w = Workload(name, batch=b, hq=hq, hkv=hkv, ctx_len=L, block=B, topk=k, dtype=dt,
                  seed=zlib.crc32(name.encode()) % 10000, t_cap=cap)
@@ -437,3 +437,86 @@ def test_topk_crafted_scores_bit_exact(kind, nb):
         torch.cuda.synchronize()
         ref, _ = oracle.block_topk(sc, nb, k)
         assert torch.equal(idx.cpu(), ref), (kind, nb, k)
+
+
+def _tied_cache(b, hkv, gqa, L, B, scales, seed):
+    """A cache whose blocks are copies of a few block patterns per pair: one
+    pattern of all zeros (its score is +0 or -0 before canonicalisation) and
+    one random N(0,1) pattern per entry of `scales`, multiplied by that power
+    of two (exact in bf16).  Every block copies one pattern (drawn at
+    random), so blocks of one pattern have identical summaries and their
+    scores tie exactly; selection among them is decided by index alone."""
+    g = torch.Generator().manual_seed(seed)
+    d = 128
+    nb = (L + B - 1) // B
+    gd = torch.Generator(device="cuda").manual_seed(seed)
+    q = torch.randn((b, hkv * gqa, d), generator=gd, device="cuda").to(torch.bfloat16)
+    K = torch.empty((b, hkv, L, d), dtype=torch.bfloat16, device="cuda")
+    V = torch.randn((b, hkv, L, d), generator=gd, device="cuda").to(torch.bfloat16)
+    for p in range(b * hkv):
+        pats = torch.randn((len(scales), B, d), generator=g) * torch.tensor(scales)[:, None, None]
+        pats = torch.cat([torch.zeros((1, B, d)), pats]).to(torch.bfloat16).cuda()
+        cls = torch.randint(0, len(scales) + 1, (nb,), generator=g).cuda()
+        K[p // hkv, p % hkv] = pats[cls].reshape(nb * B, d)[:L]
+    return {"q": q, "K": K, "V": V}
+
+
+TIES = [
+    # name, batch, hkv, gqa, ctx, block, k, scales, check outputs
+    ("ties-one-kernel-8w", 32, 8, 4, 4096, 16, 40, [1.0] * 5, True),
+    ("ties-one-kernel-4w", 64, 8, 5, 2048, 32, 20, [1.0] * 4, True),
+    ("ties-one-kernel-nb2048", 32, 8, 4, 32768, 16, 64, [1.0] * 6, True),
+    ("ties-few-pairs", 2, 4, 8, 8192, 16, 100, [1.0] * 5, True),
+    ("ties-few-pairs-nb8192", 1, 2, 4, 131072, 16, 300, [1.0] * 5, True),
+    # exponents far apart (scores spread over ~400 binades of both signs)
+    ("wide-one-kernel-8w", 32, 8, 4, 4096, 16, 40, [2.0**-100, 2.0**-40, 1.0, 2.0**40, 2.0**100],
+     False),
+    ("wide-one-kernel-4w", 64, 8, 5, 2048, 32, 20, [2.0**-90, 1.0, 2.0**90], False),
+    ("wide-few-pairs", 2, 4, 8, 8192, 16, 100, [2.0**-100, 2.0**-40, 1.0, 2.0**40, 2.0**100],
+     False),
+]
+
+
+@pytest.mark.parametrize("case", TIES, ids=[c[0] for c in TIES])
+def test_step_kernels_exact_ties_signed_zeros_and_wide_exponents(case):
+    """kin_sparse_decode_step (with and without a scores buffer: one kernel
+    when the pairs cover the chip, in both workgroup shapes, else the
+    two-kernel form) on caches full of exactly tied blocks: the selection of
+    every pair equals the oracle's selection on its own scores bit for bit
+    (no margin certificate: the ties are the point), and tied blocks get
+    bitwise equal scores."""
+    name, b, hkv, gqa, L, B, k, scales, check_out = case
+    say(f"case {name}")
+    inp = _tied_cache(b, hkv, gqa, L, B, scales, zlib.crc32(name.encode()) % 10000)
+    w = Workload(name, batch=b, hq=hkv * gqa, hkv=hkv, ctx_len=L, block=B, topk=k,
+                 dtype="bf16", seed=0)
+    nb = w.nb
+    for no_scores in (False, True):
+        bufs = run_gpu(w, inp, step=True, no_scores=no_scores)
+        qc, Kc = inp["q"].cpu(), inp["K"].cpu()
+        S_or, _ = oracle.block_summary(Kc, B, L)
+        assert torch.equal(bits(bufs.S[:, :, :nb].cpu()), bits(S_or[:, :, :nb]))
+        sc = oracle.block_score(qc, S_or, gqa, nb)
+        idx_or, _ = oracle.block_topk(sc, nb, k)
+        assert torch.equal(bufs.idx.cpu(), idx_or), f"{name}: selection differs"
+        if not no_scores:
+            sg = bufs.scores[:, :, :nb].cpu()
+            # equal summaries -> bitwise equal scores (and -0 written as +0)
+            assert not torch.any((sg == 0) & torch.signbit(sg))
+            Sb = bits(S_or[:, :, :nb]).view(b * hkv, nb, 128)
+            sgp = sg.view(b * hkv, nb)
+            for p in range(0, b * hkv, max(1, b * hkv // 16)):
+                _, inv = torch.unique(Sb[p], dim=0, return_inverse=True)
+                for c in inv.unique().tolist():
+                    vals = sgp[p][inv == c]
+                    assert torch.equal(vals, vals[:1].expand_as(vals)), f"{name}: tied scores"
+            scale = sc[:, :, :nb].abs().amax(dim=2, keepdim=True).clamp_min(1e-300)
+            assert ((sg - sc[:, :, :nb]).abs() / scale).max() < 1e-13
+        if check_out:
+            for s_ in sorted({0, b - 1}):
+                o = oracle.decode_attention(qc[s_:s_ + 1], Kc[s_:s_ + 1],
+                                            inp["V"][s_:s_ + 1].cpu(), gqa, L, B,
+                                            idx=idx_or[s_:s_ + 1].contiguous())
+                err = (bufs.out[s_:s_ + 1].cpu().double() - o).abs().max().item()
+                assert err <= TOL["bf16"], f"{name}: output error {err} at seq {s_}"
+    say(f"  ok")

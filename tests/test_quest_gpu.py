@@ -57,7 +57,7 @@ def run(w, inp, k, scores=True):
                     device="cuda") if scores else None
     idx = torch.full((w.batch, w.hkv, k), -7, dtype=torch.int32, device="cuda")
     out = torch.full((w.batch, w.hq, 128), NAN, dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(kb.kin_quest_ws_bytes(desc, k), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(kb.kin_quest_ws_bytes(desc, k), dtype=torch.uint8, device="cuda")
     kb.kin_quest_decode_step(desc, inp["q"], inp["K"], inp["V"], Sq, sc, k, idx, out, ws)
     torch.cuda.synchronize()
     return Sq, sc, idx, out

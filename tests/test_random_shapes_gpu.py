@@ -103,7 +103,7 @@ def _run_token(w, inp, k, scores):
     out = torch.full((w.batch, w.hq, 128), NAN, dtype=torch.bfloat16, device="cuda")
     sc = torch.full((w.batch, w.hkv, w.cap), NAN, dtype=torch.float64,
                     device="cuda") if scores else None
-    ws = torch.empty(max(kb.kin_token_ws_bytes(desc, k), 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(kb.kin_token_ws_bytes(desc, k), 16), dtype=torch.uint8, device="cuda")
     kb.kin_token_decode_step(desc, inp["q"], inp["K"], inp["V"], sc, k, idx, out, ws)
     torch.cuda.synchronize()
     return idx, out, sc
@@ -167,7 +167,7 @@ def test_random_quest_step(case):
     say(f"case {name}: pairs {w.pairs}, nb {w.nb}")
     inp = synth.make_inputs(w, device="cuda", tail_fill=NAN)
     desc = kb.make_desc(b, hkv, w.gqa, w.cap, L, B, torch.bfloat16)
-    ws = torch.empty(kb.kin_quest_ws_bytes(desc, k), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(kb.kin_quest_ws_bytes(desc, k), dtype=torch.uint8, device="cuda")
 
     def run(scores):
         Sq = torch.full((b, hkv, w.nb_cap, 2, 128), NAN, dtype=torch.bfloat16, device="cuda")

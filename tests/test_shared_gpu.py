@@ -79,7 +79,7 @@ def run(c, shared=True, with_scores=True):
     scores = torch.full((w.batch, w.hkv, nb_cap), NAN, dtype=torch.float64, device="cuda")
     idx = torch.full((w.batch, w.hkv, k), -7, dtype=torch.int32, device="cuda")
     out = torch.full((w.batch, w.hq, 128), NAN, dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(max(kb.kin_sparse_ws_bytes(c["desc"], k), 16), dtype=torch.uint8,
+    ws = torch.zeros(max(kb.kin_sparse_ws_bytes(c["desc"], k), 16), dtype=torch.uint8,
                      device="cuda")
     if shared:
         share = kb.make_share(c["n_share"], c["P"], c["Kp"], c["Vp"], c["Sp"])

@@ -36,7 +36,7 @@ def run_token(w, inp, k, scores=True):
     out = torch.full((w.batch, w.hq, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
     sc = torch.full((w.batch, w.hkv, w.cap), float("nan"), dtype=torch.float64,
                     device="cuda") if scores else None
-    ws = torch.empty(kb.kin_token_ws_bytes(desc, k), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(kb.kin_token_ws_bytes(desc, k), dtype=torch.uint8, device="cuda")
     kb.kin_token_decode_step(desc, inp["q"], inp["K"], inp["V"], sc, k, idx, out, ws)
     torch.cuda.synchronize()
     return idx, out, sc
