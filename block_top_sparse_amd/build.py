@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkin.so")
-SOURCES = ["kin_abi.hip", "summary.hip", "score.hip", "topk.hip", "attn.hip", "step.hip", "tok.hip", "quest.hip", "probe.hip"]
+SOURCES = ["kin_abi.hip", "summary.hip", "score.hip", "topk.hip", "attn.hip", "step.hip", "step_f32.hip", "tok.hip", "quest.hip", "probe.hip"]
 ARCH = os.environ.get("KIN_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -631,18 +631,23 @@ struct F32Lds {
     int row[NW][kChunkF32];
 };
 
-// One wave's share of the chunks (64 tokens each) of a pair, fp32.
-template <bool DENSE, int NW>
+// One wave's share of the chunks (64 tokens each) of a pair, fp32.  KB:
+// 16-byte key loads of a lane in flight at once (32: the whole key row);
+// VB: value rows in flight at once (at most 64, the chunk); MG: a bound on
+// the group's query heads (the per-head state lives in registers).
+template <bool DENSE, int NW, int KB = 8, int VB = 16, int MG = kMaxGqa>
 __device__ void attend_f32(const AttnArgs &a, const int32_t *sel, int pair, int c_beg, int c_end,
                            int first, int step, int slot, F32Lds<NW> &fl, MergeLds<NW> &sm) {
+    static_assert(kHeadDim / 4 % KB == 0 && kChunkF32 % VB == 0, "whole batches");
+    static_assert(MG <= kMaxGqa, "at most kMaxGqa heads");
     const int lane = threadIdx.x & 63;
     const int G = a.gqa;
     const float *Kp = static_cast<const float *>(a.K) + (size_t)pair * a.t_cap * kHeadDim;
     const float *Vp = static_cast<const float *>(a.V) + (size_t)pair * a.t_cap * kHeadDim;
 
-    float m_run[kMaxGqa], l_run[kMaxGqa], o0[kMaxGqa], o1[kMaxGqa];
+    float m_run[MG], l_run[MG], o0[MG], o1[MG];
 #pragma unroll
-    for (int h = 0; h < kMaxGqa; ++h) {
+    for (int h = 0; h < MG; ++h) {
         m_run[h] = -INFINITY;
         l_run[h] = 0.f;
         o0[h] = 0.f;
@@ -665,12 +670,12 @@ __device__ void attend_f32(const AttnArgs &a, const int32_t *sel, int pair, int 
         const int row = ok ? tok : 0;
         fl.row[slot][lane] = row;
 
-        float s[kMaxGqa];
+        float s[MG];
 #pragma unroll
-        for (int h = 0; h < kMaxGqa; ++h) s[h] = 0.f;
-        // the key row in batches of kKBatch 16-byte loads, all in flight
-        // before their FMAs (channel order unchanged)
-        constexpr int kKBatch = 8;
+        for (int h = 0; h < MG; ++h) s[h] = 0.f;
+        // the key row in batches of KB 16-byte loads, all in flight before
+        // their FMAs (channel order unchanged)
+        constexpr int kKBatch = KB;
         const f32x4 *kr = reinterpret_cast<const f32x4 *>(Kp + (size_t)row * kHeadDim);
         for (int c0 = 0; c0 < kHeadDim / 4; c0 += kKBatch) {
             f32x4 kv[kKBatch];
@@ -680,7 +685,7 @@ __device__ void attend_f32(const AttnArgs &a, const int32_t *sel, int pair, int 
             for (int u = 0; u < kKBatch; ++u) {
                 const int c4 = c0 + u;
 #pragma unroll
-                for (int h = 0; h < kMaxGqa; ++h) {
+                for (int h = 0; h < MG; ++h) {
                     if (h < G) {
                         s[h] = fmaf(fl.q[h][4 * c4 + 0], kv[u][0], s[h]);
                         s[h] = fmaf(fl.q[h][4 * c4 + 1], kv[u][1], s[h]);
@@ -691,7 +696,7 @@ __device__ void attend_f32(const AttnArgs &a, const int32_t *sel, int pair, int 
             }
         }
 #pragma unroll
-        for (int h = 0; h < kMaxGqa; ++h) {
+        for (int h = 0; h < MG; ++h) {
             if (h >= G) continue;
             const float z = ok ? s[h] * a.scale_log2 : -INFINITY;
             float mx = z;
@@ -709,9 +714,9 @@ __device__ void attend_f32(const AttnArgs &a, const int32_t *sel, int pair, int 
         }
         wave_lds_sync();  // p / row entries of this wave are complete
         // p . v: lane owns channels 2*lane, 2*lane+1; the value rows in
-        // batches of kVBatch tokens, all loads in flight before their FMAs
-        // (token order unchanged)
-        constexpr int kVBatch = 16;
+        // batches of VB tokens, all loads in flight before their FMAs (token
+        // order unchanged)
+        constexpr int kVBatch = VB;
         for (int t0 = 0; t0 < kChunkF32; t0 += kVBatch) {
             float2 v[kVBatch];
 #pragma unroll
@@ -721,7 +726,7 @@ __device__ void attend_f32(const AttnArgs &a, const int32_t *sel, int pair, int 
 #pragma unroll
             for (int u = 0; u < kVBatch; ++u) {
 #pragma unroll
-                for (int h = 0; h < kMaxGqa; ++h) {
+                for (int h = 0; h < MG; ++h) {
                     if (h < G) {
                         const float pt = fl.p[slot][h][t0 + u];
                         o0[h] = fmaf(pt, v[u].x, o0[h]);
@@ -733,7 +738,7 @@ __device__ void attend_f32(const AttnArgs &a, const int32_t *sel, int pair, int 
         wave_lds_sync();  // every lane is done reading before the next chunk writes
     }
 #pragma unroll
-    for (int h = 0; h < kMaxGqa; ++h) {
+    for (int h = 0; h < MG; ++h) {
         if (h >= G) continue;
         float l = l_run[h];
 #pragma unroll

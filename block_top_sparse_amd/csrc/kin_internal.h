@@ -88,6 +88,12 @@ hipError_t launch_select_attend(const Geo &g, const AttnPlan &p, const void *q, 
 // the whole decode step in one kernel (one workgroup per pair); usable when
 // step_single_kernel() says so (bf16, enough pairs to cover the chip)
 bool step_single_kernel(const Geo &g, int k, int num_cu);
+// the whole fp32 decode step in one kernel (one workgroup per pair) for
+// steps of small per-pair bytes (contiguous caches)
+bool step_f32_single_kernel(const Geo &g, int k);
+hipError_t launch_decode_step_f32(const Geo &g, const void *q, const void *K, const void *V,
+                                  void *S, double *scores, int k, int32_t *idx, void *out,
+                                  hipStream_t s);
 // the arrival words of a plan's in-kernel combine (the start of ws;
 // nullptr: the plan has none)
 uint64_t *step_ctrl(const AttnPlan &p, void *ws);

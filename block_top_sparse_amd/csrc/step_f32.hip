@@ -1,0 +1,185 @@
+// step_f32.hip -- a whole fp32 block top-k sparse decode step in ONE
+// kernel, one workgroup (8 waves) per (sequence, KV head) pair, for steps
+// whose per-pair bytes are small (a short context and a small budget: the
+// tiny fp32 layer):
+//
+//   1. wave 0 rebuilds the newest block's summary (fp64 mean in token
+//      order, rounded to fp32), writes it to S and keeps it in LDS, while
+//      every wave scores its share of the other blocks against the group's
+//      query sum (fp64, the per-lane math and butterfly of k_block_score,
+//      so the scores are bit for bit those of the two-kernel step); wave 0
+//      then scores the newest block from its LDS row.  The scores stay in
+//      LDS and are counted into the select's exponent tables;
+//   2. the workgroup selects the top k blocks (select.h);
+//   3. the waves attend over the kept tokens (fp32 VALU, 64 tokens per
+//      chunk, a whole key row and 32 value rows per lane in flight) and
+//      merge into the output.
+//
+// The steps are those of BlockTopKAttention (skill summary "Kinetics:
+// Memory-Aware Test-Time Scaling", Implementation) with KV blocks and a
+// budget of k blocks (rebuttal "Kinetics: Rethinking Test-Time Scaling
+// Law", Q4 "KV block size and grouping strategy").
+//
+// Why one kernel here: such a step moves about a megabyte, so its time is
+// a chain of latencies (launches, memory round trips, barriers), not
+// bandwidth.  The two-kernel form paid a second launch and ran its
+// attention on one workgroup per pair anyway (too few chunks to split), so
+// one workgroup per pair doing the whole step removes a launch and the
+// scores' trip through memory.
+#include "attn_impl.h"
+#include "score_impl.h"
+
+namespace kin {
+
+constexpr int kStepF32MaxBlocks = 8192;
+// per-pair bytes (summary rows + kept K and V rows) up to which the fp32
+// step runs as this one kernel
+constexpr size_t kStepF32MaxPairBytes = (size_t)1 << 20;
+
+struct StepF32Extra {
+    void *S;
+    double *scores;  // may be null: the scores are then not written out
+    int32_t *idx;
+    int nb_cap;
+};
+
+// MG: a bound on the group's query heads (8 or 16); with at most 8 the
+// attention keeps a whole key row per lane in flight, else half of it.
+template <int KPT, int MG>
+__global__ __launch_bounds__(kStepThreads) void k_decode_step_f32(AttnArgs a, StepF32Extra x) {
+    constexpr int NT = kStepThreads, NW = NT / 64;
+    __shared__ int32_t sel[kStepIdxCap];
+    __shared__ SelectLds<KPT, NT> sl;
+    __shared__ union {
+        double sc[kStepF32MaxBlocks];
+        MergeLds<NW> m;
+    } u;
+    __shared__ F32Lds<NW> fl;
+    __shared__ uint32_t row_lds[kHeadDim];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pair = blockIdx.x;
+    const int b = pair / a.hkv, g = pair % a.hkv;
+    const int nb = a.nb;
+    const size_t row0 = (size_t)pair * x.nb_cap;
+    double *sc_out = x.scores ? x.scores + row0 : nullptr;
+    auto emit = [&](int j, double v) {
+        if (v == 0.0) v = 0.0;  // one zero: -0.0 becomes +0.0
+        u.sc[j] = v;
+        if (sc_out) sc_out[j] = v;  // scores are an optional output
+        select_count(sl, v);
+    };
+
+    select_clear(sl);
+    load_q_f32<NW>(a, pair, fl);
+    __syncthreads();
+
+    // 1. scores.  Rows of blocks below the newest one, 16 per wave and
+    // round (4 rows per 16-lane group load), the next round's loads issued
+    // before this round's math; past the range a load re-reads the last
+    // scored row and its score is dropped.  The newest row is never loaded
+    // here: wave 0 rewrites it during this phase.
+    const int sub = lane & 15, grp = lane >> 4;
+    double qs[8];
+    group_query_sum<KIN_F32>(a.q, b, g, a.hkv, a.gqa, sub, qs);
+    if (wave == 0)
+        newest_summary<KIN_F32>(a.K, x.S, pair, a.t_cap, x.nb_cap, a.ctx_len, a.block, row_lds,
+                                lane);
+    wave_lds_sync();  // wave 0's row_lds entries, read across its lanes below
+    const int n_rows = nb - 1;
+    constexpr int kRound = NW * 16;
+    const int n_it = wave * 16 < n_rows ? (n_rows - wave * 16 + kRound - 1) / kRound : 0;
+    if (n_it > 0) {
+        auto load_round = [&](int it, u32x4 (&ra)[4], u32x4 (&rb)[4]) {
+            const int j0 = wave * 16 + it * kRound;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                load_row_slice<KIN_F32>(x.S, row0 + min(j0 + 4 * v + grp, n_rows - 1), sub, ra[v],
+                                        rb[v]);
+        };
+        u32x4 wa[2][4], wb[2][4];
+        load_round(0, wa[0], wb[0]);
+        for (int it = 0; it < n_it; ++it) {
+            const int cur = it & 1;
+            // the next round (or a harmless repeat of the last one)
+            load_round(min(it + 1, n_it - 1), wa[cur ^ 1], wb[cur ^ 1]);
+            double part[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) part[v] = slice_dot<KIN_F32>(qs, wa[cur][v], wb[cur][v]);
+            const double xv = fold4(part, lane);
+            const int slot = ((lane & 8) ? 2 : 0) + ((lane & 4) ? 1 : 0);
+            const int j = wave * 16 + it * kRound + 4 * slot + grp;
+            if ((lane & 3) == 0 && j < n_rows) emit(j, xv);
+        }
+    }
+    if (wave == 0) {
+        // the newest row (written to row_lds by this wave) in slot 0 of row
+        // group 0, zero rows elsewhere: the butterfly every block goes through
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        u32x4 ra = zero, rb = zero;
+        if (grp == 0) {
+            const uint32_t *r = row_lds + 8 * sub;
+            ra = u32x4{r[0], r[1], r[2], r[3]};
+            rb = u32x4{r[4], r[5], r[6], r[7]};
+        }
+        double part[4];
+        part[0] = slice_dot<KIN_F32>(qs, ra, rb);
+        part[1] = part[2] = part[3] = slice_dot<KIN_F32>(qs, zero, zero);
+        const double xv = fold4(part, lane);
+        if (lane == 0) emit(nb - 1, xv);
+    }
+    __syncthreads();
+
+    // 2. selection (the scores are dead afterwards: the merge reuses them)
+    select_topk<KPT, NT, true>(u.sc, nb, a.k, sel, sl);
+    __syncthreads();
+    for (int i = tid; i < a.k; i += NT) x.idx[(size_t)pair * a.k + i] = sel[i];
+
+    // 3. attention over the kept tokens, then the merge of the 8 waves
+    constexpr int KB = MG <= 8 ? 32 : 16;
+    attend_f32<false, NW, KB, 32, MG>(a, sel, pair, 0, a.n_chunks, wave, NW, wave, fl, u.m);
+    __syncthreads();
+    merge_waves_and_store<KIN_F32, NW>(a, u.m, pair, 0);
+}
+
+bool step_f32_single_kernel(const Geo &g, int k) {
+    if (g.dtype != KIN_F32 || g.nb > kStepF32MaxBlocks || k > kStepIdxCap) return false;
+    const size_t keff = (size_t)(k < g.nb ? k : g.nb);
+    const size_t row = (size_t)kHeadDim * sizeof(float);
+    return (size_t)g.nb * row + keff * g.block * row * 2 <= kStepF32MaxPairBytes;
+}
+
+hipError_t launch_decode_step_f32(const Geo &g, const void *q, const void *K, const void *V,
+                                  void *S, double *scores, int k, int32_t *idx, void *out,
+                                  hipStream_t s) {
+    AttnPlan p;
+    const int keff = k < g.nb ? k : g.nb;
+    p.n_tokens = keff * g.block;
+    p.n_chunks = (p.n_tokens + kChunkF32 - 1) / kChunkF32;
+    p.nsplit = 1;
+    p.fused = 1;
+    p.ws_bytes = 0;
+    AttnArgs a;
+    fill_args(a, g, p, q, K, V, nullptr, k, out, nullptr);
+    const StepF32Extra x{S, scores, idx, g.nb_cap};
+    const dim3 grid(g.pairs);
+#define KIN_F32_STEP(KPT)                                                            \
+    do {                                                                             \
+        if (g.gqa <= 8)                                                              \
+            k_decode_step_f32<KPT, 8><<<grid, kStepThreads, 0, s>>>(a, x);           \
+        else                                                                         \
+            k_decode_step_f32<KPT, kMaxGqa><<<grid, kStepThreads, 0, s>>>(a, x);     \
+    } while (0)
+    switch (select_kpt(g.nb, kStepThreads)) {
+    case 1: KIN_F32_STEP(1); break;
+    case 2: KIN_F32_STEP(2); break;
+    case 4: KIN_F32_STEP(4); break;
+    case 8: KIN_F32_STEP(8); break;
+    default: KIN_F32_STEP(16); break;
+    }
+#undef KIN_F32_STEP
+    return hipGetLastError();
+}
+
+}  // namespace kin

@@ -520,3 +520,40 @@ def test_step_kernels_exact_ties_signed_zeros_and_wide_exponents(case):
                 err = (bufs.out[s_:s_ + 1].cpu().double() - o).abs().max().item()
                 assert err <= TOL["bf16"], f"{name}: output error {err} at seq {s_}"
     say(f"  ok")
+
+
+F32_STEP = [
+    # name, batch, hq, hkv, ctx, block, k, dtype, t_cap  (small per-pair bytes: one kernel)
+    ("f32step-tiny-shape", 1, 8, 2, 4096, 16, 32, "f32", 4096),
+    ("f32step-g1-b32-ragged", 3, 2, 2, 1000, 32, 5, "f32", 1024),
+    ("f32step-g16-b64-k1", 2, 32, 2, 700, 64, 1, "f32", 704),
+    ("f32step-g5-b16-kpast", 2, 10, 2, 100, 16, 9, "f32", 112),      # k > nb
+    ("f32step-g8-b128-keepall", 1, 16, 2, 300, 128, 3, "f32", 384),  # k = nb, partial block
+    ("f32step-g3-b16-one-block", 2, 6, 2, 7, 16, 2, "f32", 16),      # nb = 1
+    ("f32step-g4-b16-nb1024", 1, 8, 2, 16384, 16, 8, "f32", 16384),  # KPT 2
+]
+
+
+@pytest.mark.parametrize("case", F32_STEP, ids=[c[0] for c in F32_STEP])
+def test_f32_one_kernel_step_against_oracle(case):
+    """kin_sparse_decode_step in fp32 with small per-pair bytes: one kernel
+    per step (newest-row rebuild, scores, selection, attention); with and
+    without a scores buffer, against the oracle on every sequence, and equal
+    (selection, summaries, scores) to the separate calls."""
+    name, b, hq, hkv, L, B, k, dt, cap = case
+    w = Workload(name, batch=b, hq=hq, hkv=hkv, ctx_len=L, block=B, topk=k, dtype=dt,
+                 seed=zlib.crc32(name.encode()) % 10000, t_cap=cap)
+    say(f"case {name}: {w.describe()}")
+    inp = gpu_inputs(w)
+    bufs = run_gpu(w, inp, step=True)
+    assert bufs.ws is None or kb.kin_sparse_ws_bytes(bufs.desc, k) >= 0
+    r = check_sequences(w, inp, bufs, range(b))
+    sep = run_gpu(w, inp)
+    assert torch.equal(sep.idx, bufs.idx)
+    assert torch.equal(bits(sep.S[:, :, :w.nb]), bits(bufs.S[:, :, :w.nb]))
+    assert torch.equal(sep.scores[:, :, :w.nb], bufs.scores[:, :, :w.nb])
+    quiet = run_gpu(w, inp, step=True, no_scores=True)
+    assert torch.equal(quiet.idx, bufs.idx)
+    assert torch.equal(bits(quiet.out), bits(bufs.out))
+    assert torch.isnan(quiet.scores).all()
+    say(f"  ok {r}")
