@@ -104,6 +104,7 @@ def lib():
             "kin_quest_decode_step": (I, [D, P, P, P, P, P, I, P, P, P, Z, P]),
             "kin_quest_ws_bytes": (Z, [D, I]),
             "kin_token_ws_bytes": (Z, [D, I]),
+            "kin_sparse_decode_step_noalloc": (I, [D, P, P, P, P, P, I, P, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -120,7 +121,7 @@ def exported_names():
             "kin_version", "kin_paged_summary_update", "kin_paged_decode_step",
             "kin_token_decode_step", "kin_token_ws_bytes", "kin_shared_decode_step",
             "kin_quest_summary_update", "kin_quest_decode_step", "kin_quest_ws_bytes",
-            "kin_hbm_read_probe"]
+            "kin_hbm_read_probe", "kin_sparse_decode_step_noalloc"]
 
 
 def _p(t):
@@ -175,6 +176,11 @@ def kin_sparse_decode_step(desc, q, K, V, S, scores, k, idx, out, ws=None, strea
     _check(lib().kin_sparse_decode_step(ctypes.byref(desc), _p(q), _p(K), _p(V), _p(S),
                                         _p(scores), k, _p(idx), _p(out), _p(ws), _nbytes(ws),
                                         _s(stream)))
+
+
+def kin_sparse_decode_step_noalloc(desc, q, K, V, S, scores, k, idx, out, stream=None):
+    _check(lib().kin_sparse_decode_step_noalloc(ctypes.byref(desc), _p(q), _p(K), _p(V), _p(S),
+                                                _p(scores), k, _p(idx), _p(out), _s(stream)))
 
 
 def kin_paged_summary_update(desc, pages, K, S, t_begin, t_end, stream=None):

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "kin_internal.h"
 
@@ -116,6 +117,55 @@ static kin_status check_ws_size(size_t need, const void *ws, size_t ws_bytes) {
 static kin_status check_ws(const kin::AttnPlan &p, const void *ws, size_t ws_bytes) {
     return check_ws_size(p.ws_bytes, ws, ws_bytes);
 }
+
+// ---- the step without allocation --------------------------------------
+// Callers that cannot allocate device memory (code under HIP graph capture,
+// tight serving loops, harnesses that forbid hipMalloc) take
+// kin_sparse_decode_step's workspace from this file-scope device array:
+// KIN_NOALLOC_SCRATCH_BYTES on every device the library runs on, held until
+// the process ends.  In host code `scratch` only names the symbol; its
+// device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[KIN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];  // device address of `scratch`, per device
+
+// zero n 64-bit words (the arrival words of a fresh scratch array)
+__global__ void k_zero_words(uint64_t *p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0ull;
+}
+
+// This device's scratch address; on the first call for a device it is
+// looked up and the arrival words at its start are cleared on `stream`
+// (the array starts zeroed anyway; every call leaves those words at zero).
+kin_status scratch_on_device(hipStream_t stream, void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(KIN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(KIN_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(KIN_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        constexpr int n = kin::kCtrlWords;
+        k_zero_words<<<(n + 255) / 256, 256, 0, stream>>>(static_cast<uint64_t *>(p), n);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return fail(KIN_ERR_HIP, "clearing the scratch words: %s", hipGetErrorString(e));
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return KIN_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -232,6 +282,16 @@ kin_status kin_decode_select_attend(const kin_desc *desc, const void *q, const v
                     "kin_decode_select_attend");
 }
 
+// Workspace bytes the decode step takes for this geometry (scores: whether
+// the caller passes a scores buffer; without one the two-kernel form keeps
+// the scores in the workspace).
+static size_t step_ws_need(const kin::Geo &g, int32_t k, int cu, bool scores) {
+    if (kin::step_single_kernel(g, k, cu)) return 0;
+    if (!g.pages && !g.share_n && kin::step_f32_single_kernel(g, k)) return 0;
+    const kin::AttnPlan p = kin::plan_step(g, k, cu);
+    return scores ? p.ws_bytes : kin::step_ws_with_scores(g, p);
+}
+
 // The decode step for a checked geometry (contiguous or paged).
 static kin_status decode_step(const kin::Geo &g, const void *q, const void *K, const void *V,
                               void *S, double *scores, int32_t k, int32_t *idx, void *out,
@@ -257,8 +317,7 @@ static kin_status decode_step(const kin::Geo &g, const void *q, const void *K, c
     const kin::AttnPlan p = kin::plan_step(g, k, cu);
     // two kernels hand the scores over in memory: the caller's buffer, or
     // the workspace after the attention's part
-    const size_t need = scores ? p.ws_bytes : kin::step_ws_with_scores(g, p);
-    st = check_ws_size(need, ws, ws_bytes);
+    st = check_ws_size(step_ws_need(g, k, cu, scores != nullptr), ws, ws_bytes);
     if (st != KIN_OK) return st;
     double *sc = scores ? scores : kin::step_scores_in_ws(g, p, ws);
     // every block kept and no scores wanted: only the newest summary row is
@@ -285,6 +344,35 @@ kin_status kin_sparse_decode_step(const kin_desc *desc, const void *q, const voi
     kin_status st = check_step(desc, &g);
     if (st != KIN_OK) return st;
     return decode_step(g, q, K, V, S, scores, k, idx, out, ws, ws_bytes, stream);
+}
+
+kin_status kin_sparse_decode_step_noalloc(const kin_desc *desc, const void *q, const void *K,
+                                          const void *V, void *S, double *scores, int32_t k,
+                                          int32_t *idx, void *out, kin_stream stream) {
+    kin::Geo g;
+    kin_status st = check_step(desc, &g);
+    if (st != KIN_OK) return st;
+    KIN_REQUIRE_PTR(q);
+    KIN_REQUIRE_PTR(K);
+    KIN_REQUIRE_PTR(V);
+    KIN_REQUIRE_PTR(S);
+    if (scores && !aligned16(scores)) return fail(KIN_ERR_ALIGN, "scores is not 16-byte aligned");
+    KIN_REQUIRE_PTR(idx);
+    KIN_REQUIRE_PTR(out);
+    if (k < 1) return fail(KIN_ERR_SHAPE, "k = %d: need k >= 1", k);
+    const size_t need = step_ws_need(g, k, num_cu(), scores != nullptr);
+    if (need > KIN_NOALLOC_SCRATCH_BYTES)
+        return fail(KIN_ERR_WORKSPACE,
+                    "this step needs %zu bytes of scratch; the no-allocation step holds %zu "
+                    "(use kin_sparse_decode_step with a workspace)",
+                    need, (size_t)KIN_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if (need) {
+        st = scratch_on_device((hipStream_t)stream, &ws);
+        if (st != KIN_OK) return st;
+    }
+    return decode_step(g, q, K, V, S, scores, k, idx, out, ws, need ? KIN_NOALLOC_SCRATCH_BYTES : 0,
+                       stream);
 }
 
 // Variable lengths and paged caches: the descriptor plus the kin_pages

@@ -220,6 +220,26 @@ KIN_API kin_status kin_sparse_decode_step(const kin_desc *desc, const void *q, c
                                   int32_t *idx, void *out, void *ws, size_t ws_bytes,
                                   kin_stream stream);
 
+/* The same step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It takes no workspace argument: the workspace kin_sparse_decode_step
+ * would need comes from a scratch array that the library holds on every
+ * device it runs on, KIN_NOALLOC_SCRATCH_BYTES bytes, kept until the
+ * process ends.  The call itself allocates nothing (no hipMalloc, no
+ * allocating library routine).  Results equal kin_sparse_decode_step's on
+ * the same arguments.  A step that needs more scratch than the array holds
+ * (few (sequence, KV head) pairs with very many blocks and no scores
+ * buffer, e.g. 200 pairs of 16384 blocks) returns KIN_ERR_WORKSPACE before
+ * anything is enqueued.  Every call on a device shares that device's array:
+ * calls that overlap in time on one device (other streams, other host
+ * threads) race and must be serialised by the caller.  Errors: as
+ * kin_sparse_decode_step. */
+#define KIN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+KIN_API kin_status kin_sparse_decode_step_noalloc(const kin_desc *desc, const void *q,
+                                                  const void *K, const void *V, void *S,
+                                                  double *scores, int32_t k, int32_t *idx,
+                                                  void *out, kin_stream stream);
+
 /* ---- Variable lengths and paged caches ---------------------------------
  * The serving layout of the latency runs on the rebuttal page "Kinetics:
  * Rethinking Test-Time Scaling Law" (W2 & Q2: Real-world latency

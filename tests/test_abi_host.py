@@ -29,7 +29,7 @@ def header_entry_points():
 
 def test_every_declared_entry_point_is_exported():
     declared = header_entry_points()
-    assert len(declared) == 22, declared
+    assert len(declared) == 23, declared
     lib = ctypes.CDLL(kb.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
@@ -204,3 +204,22 @@ def test_read_probe_argument_checks():
     assert f(MISALIGNED, 64, FAKE, None) == align
     assert f(FAKE, 0, FAKE, None) == shape
     assert f(FAKE, 40, FAKE, None) == shape
+
+
+def test_noalloc_step_rejects_a_step_beyond_its_scratch():
+    """kin_sparse_decode_step_noalloc checks, on the host and before any
+    launch, that the step fits its scratch array: 192 pairs of 16384 blocks
+    with no scores buffer keep 24 MiB of scores in the workspace, more than
+    KIN_NOALLOC_SCRATCH_BYTES (16 MiB), so the call returns KIN_ERR_WORKSPACE."""
+    d = kb.make_desc(64, 3, 4, 262144, 262144, 16, kb.KIN_BF16)
+    rc = _raw("kin_sparse_decode_step_noalloc", ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 64,
+              FAKE, FAKE, None)
+    assert rc == -6
+    assert "scratch" in kb.kin_last_error()
+    # the argument checks of kin_sparse_decode_step come first
+    rc = _raw("kin_sparse_decode_step_noalloc", ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 0,
+              FAKE, FAKE, None)
+    assert rc == -2
+    rc = _raw("kin_sparse_decode_step_noalloc", ctypes.byref(d), None, FAKE, FAKE, FAKE, None, 64,
+              FAKE, FAKE, None)
+    assert rc == -1
