@@ -35,8 +35,10 @@
 // wave loads chunk c + stride while it computes chunk c (two register
 // buffers), so a wave always has one chunk (16 KiB) of loads in flight.
 //
-// fp32 path (VALU), 64 tokens per chunk: lane = token for q.k (each lane
-// reads its key row), LDS holds the weights, lane = 2 channels for p.v.
+// fp32 path (MFMA, v_mfma_f32_16x16x4_f32), 16 tokens per chunk: the same
+// two products with 4-channel k-steps, laid out so that every load reads
+// contiguous row pieces and the weights again stay in the lanes that
+// computed them (attn_impl.h); fp32 weights and accumulation.
 #include "attn_impl.h"
 
 namespace kin {
@@ -61,16 +63,18 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(AttnArgs a) {
 template <bool DENSE>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_f32(AttnArgs a) {
     __shared__ MergeLds<4> sm;
-    __shared__ F32Lds<4> fl;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int split = blockIdx.x, pair = blockIdx.y;
-    load_q_f32<4>(a, pair, fl);
-    __syncthreads();
     const int cps = (a.n_chunks + a.nsplit - 1) / a.nsplit;
     const int c_beg = split * cps;
     const int c_end = min(a.n_chunks, c_beg + cps);
-    const int32_t *sel = DENSE ? nullptr : a.idx + (size_t)pair * a.k;
-    attend_f32<DENSE, 4>(a, sel, pair, c_beg, c_end, wave, 4, wave, fl, sm);
+    f32x4 qf[8];
+    load_q_f32(a, pair, qf);
+    if (DENSE)
+        attend_f32<DenseRuns, 4>(a, dense_runs(a, pair), qf, c_beg, c_end, wave, 4, wave, sm);
+    else
+        attend_f32<ListRuns, 4>(a, list_runs(a, pair, a.idx + (size_t)pair * a.k), qf, c_beg,
+                                c_end, wave, 4, wave, sm);
     __syncthreads();
     merge_waves_and_store<KIN_F32, 4>(a, sm, pair, split);
 }
@@ -96,6 +100,9 @@ __global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a0,
     int pair, split;
     split_slot(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, gridDim.y, pair, split);
     const AttnArgs a = for_pair(a0, pair);  // this sequence's own length
+    // fp32: the attention's query operand, loaded before the selection
+    f32x4 qf32[8];
+    if constexpr (DT == KIN_F32) load_q_f32(a, pair, qf32);
     select_clear(u.s);
     __syncthreads();
     select_topk<KPT, kStepThreads, false>(scores + (size_t)pair * nb_cap, a.nb, a.k, sel, u.s);
@@ -130,10 +137,8 @@ __global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a0,
         attend_bf16<ListRuns, NW>(a, list_runs(a, pair, sel), pair, c_beg, c_end, wave, NW, wave,
                                   u.m);
     } else {
-        __shared__ F32Lds<NW> fl;
-        load_q_f32<NW>(a, pair, fl);
-        __syncthreads();
-        attend_f32<false, NW>(a, sel, pair, c_beg, c_end, wave, NW, wave, fl, u.m);
+        attend_f32<ListRuns, NW>(a, list_runs(a, pair, sel), qf32, c_beg, c_end, wave, NW, wave,
+                                 u.m);
     }
     __syncthreads();
     if (a.nsplit == 1) {

@@ -611,10 +611,6 @@ __device__ __forceinline__ ListRuns list_runs(const AttnArgs &a, int pair, const
     return ListRuns{(int64_t)pair * a.t_cap, sel, a.k, a.nb, a.block, a.block_shift};
 }
 
-// ---------------------------------------------------------------------------
-// fp32, VALU
-// ---------------------------------------------------------------------------
-
 // Order LDS writes of one wave before its following LDS reads (the lanes of
 // a wave run in lockstep and the LDS queue of a wave is in order; this only
 // keeps the compiler from moving accesses across the point).
@@ -624,144 +620,169 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int NW>
-struct F32Lds {
-    float q[kMaxGqa][kHeadDim];
-    float p[NW][kMaxGqa][kChunkF32];
-    int row[NW][kChunkF32];
+// ---------------------------------------------------------------------------
+// fp32, MFMA (v_mfma_f32_16x16x4_f32), 16 tokens per chunk
+// ---------------------------------------------------------------------------
+//
+// S^T[token][head] = K_tile . Q^T   32 MFMAs of 4 channels: k-step 4n + e
+//                                   takes channel 16n + 4g + e, so lane (j, g)
+//                                   (j = lane % 16, g = lane / 16) holds K row
+//                                   j's channels 16n + 4g .. +3 as one 16 B
+//                                   load per n (each instruction reads 64
+//                                   contiguous bytes of 16 rows), and the
+//                                   query the same channels of head j
+// O[head][chan]   += P . V_tile     4 token k-steps x 8 column tiles: k-step
+//                                   s, lane (j, g) supplies token 4g + s,
+//                                   whose score (head j) it already holds in
+//                                   row s of its S^T block, and the value
+//                                   channels 8j .. 8j+7 of that token (column
+//                                   j of tile n is channel 8j + n; 512
+//                                   contiguous bytes per row)
+// The weights stay fp32 (no rounding), the products are fp32 MFMAs with
+// fp32 accumulation; every chunk's loads are issued while the previous
+// chunk computes (two register buffers).
+
+struct ChunkRegsF32 {
+    f32x4 k[8];     // K row j of the tile, channels 16n + 4g .. +3
+    f32x4 v[4][2];  // V row 4g + s, channels 8j .. 8j+3 and 8j+4 .. 8j+7
+    uint32_t ok;    // bit s: the token of V row 4g + s is kept and inside the context
 };
 
-// One wave's share of the chunks (64 tokens each) of a pair, fp32.  KB:
-// 16-byte key loads of a lane in flight at once (32: the whole key row);
-// VB: value rows in flight at once (at most 64, the chunk); MG: a bound on
-// the group's query heads (the per-head state lives in registers).
-template <bool DENSE, int NW, int KB = 8, int VB = 16, int MG = kMaxGqa>
-__device__ void attend_f32(const AttnArgs &a, const int32_t *sel, int pair, int c_beg, int c_end,
-                           int first, int step, int slot, F32Lds<NW> &fl, MergeLds<NW> &sm) {
-    static_assert(kHeadDim / 4 % KB == 0 && kChunkF32 % VB == 0, "whole batches");
-    static_assert(MG <= kMaxGqa, "at most kMaxGqa heads");
-    const int lane = threadIdx.x & 63;
-    const int G = a.gqa;
-    const float *Kp = static_cast<const float *>(a.K) + (size_t)pair * a.t_cap * kHeadDim;
-    const float *Vp = static_cast<const float *>(a.V) + (size_t)pair * a.t_cap * kHeadDim;
+__device__ __forceinline__ f32x4 as_f32x4(u32x4 v) { return __builtin_bit_cast(f32x4, v); }
 
-    float m_run[MG], l_run[MG], o0[MG], o1[MG];
+template <class Runs>
+__device__ __forceinline__ void load_chunk_f32(const AttnArgs &a, const Runs &runs, const float *K,
+                                               const float *V, int c, int j, int g,
+                                               ChunkRegsF32 &cr) {
+    static_assert(!Runs::kPerToken && !Runs::kTwoBases, "fp32: contiguous block lists");
+    bool valid;
+    int t0;
+    const int64_t row0 = runs.run(c * kChunkF32, valid, t0);
+    const int64_t rowk = (valid && t0 + j < a.ctx_len) ? row0 + j : runs.safe();
+    const float *kr = K + rowk * kHeadDim + 4 * g;
 #pragma unroll
-    for (int h = 0; h < MG; ++h) {
-        m_run[h] = -INFINITY;
-        l_run[h] = 0.f;
-        o0[h] = 0.f;
-        o1[h] = 0.f;
-    }
-    for (int c = c_beg + first; c < c_end; c += step) {
-        // this lane's token: list position c*64 + lane
-        const int p = c * kChunkF32 + lane;
-        bool ok;
-        int tok;
-        if (DENSE) {
-            tok = p;
-            ok = p < a.ctx_len;
-        } else {
-            const int slotp = p >> a.block_shift;
-            const int id = slotp < a.k ? sel[slotp] : -1;
-            tok = id * a.block + (p & (a.block - 1));
-            ok = id >= 0 && id < a.nb && tok < a.ctx_len;
-        }
-        const int row = ok ? tok : 0;
-        fl.row[slot][lane] = row;
-
-        float s[MG];
+    for (int n = 0; n < 8; ++n) cr.k[n] = as_f32x4(ld_nt16(kr + 16 * n));
+    cr.ok = 0;
 #pragma unroll
-        for (int h = 0; h < MG; ++h) s[h] = 0.f;
-        // the key row in batches of KB 16-byte loads, all in flight before
-        // their FMAs (channel order unchanged)
-        constexpr int kKBatch = KB;
-        const f32x4 *kr = reinterpret_cast<const f32x4 *>(Kp + (size_t)row * kHeadDim);
-        for (int c0 = 0; c0 < kHeadDim / 4; c0 += kKBatch) {
-            f32x4 kv[kKBatch];
-#pragma unroll
-            for (int u = 0; u < kKBatch; ++u) kv[u] = kr[c0 + u];
-#pragma unroll
-            for (int u = 0; u < kKBatch; ++u) {
-                const int c4 = c0 + u;
-#pragma unroll
-                for (int h = 0; h < MG; ++h) {
-                    if (h < G) {
-                        s[h] = fmaf(fl.q[h][4 * c4 + 0], kv[u][0], s[h]);
-                        s[h] = fmaf(fl.q[h][4 * c4 + 1], kv[u][1], s[h]);
-                        s[h] = fmaf(fl.q[h][4 * c4 + 2], kv[u][2], s[h]);
-                        s[h] = fmaf(fl.q[h][4 * c4 + 3], kv[u][3], s[h]);
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < MG; ++h) {
-            if (h >= G) continue;
-            const float z = ok ? s[h] * a.scale_log2 : -INFINITY;
-            float mx = z;
-#pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
-            const float m_new = fmaxf(m_run[h], mx);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = exp2f(m_run[h] - m_use);
-            const float pz = exp2f(z - m_use);
-            l_run[h] = l_run[h] * alpha + pz;
-            o0[h] *= alpha;
-            o1[h] *= alpha;
-            m_run[h] = m_new;
-            fl.p[slot][h][lane] = pz;
-        }
-        wave_lds_sync();  // p / row entries of this wave are complete
-        // p . v: lane owns channels 2*lane, 2*lane+1; the value rows in
-        // batches of VB tokens, all loads in flight before their FMAs (token
-        // order unchanged)
-        constexpr int kVBatch = VB;
-        for (int t0 = 0; t0 < kChunkF32; t0 += kVBatch) {
-            float2 v[kVBatch];
-#pragma unroll
-            for (int u = 0; u < kVBatch; ++u)
-                v[u] = reinterpret_cast<const float2 *>(Vp + (size_t)fl.row[slot][t0 + u] *
-                                                                 kHeadDim)[lane];
-#pragma unroll
-            for (int u = 0; u < kVBatch; ++u) {
-#pragma unroll
-                for (int h = 0; h < MG; ++h) {
-                    if (h < G) {
-                        const float pt = fl.p[slot][h][t0 + u];
-                        o0[h] = fmaf(pt, v[u].x, o0[h]);
-                        o1[h] = fmaf(pt, v[u].y, o1[h]);
-                    }
-                }
-            }
-        }
-        wave_lds_sync();  // every lane is done reading before the next chunk writes
-    }
-#pragma unroll
-    for (int h = 0; h < MG; ++h) {
-        if (h >= G) continue;
-        float l = l_run[h];
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) l += __shfl_xor(l, d);
-        if (lane == 0) {
-            sm.m[slot][h] = m_run[h];
-            sm.l[slot][h] = l;
-        }
-        sm.o[slot][h][2 * lane] = o0[h];
-        sm.o[slot][h][2 * lane + 1] = o1[h];
+    for (int s = 0; s < 4; ++s) {
+        const int dv = 4 * g + s;
+        const bool ok = valid && t0 + dv < a.ctx_len;
+        cr.ok |= (ok ? 1u : 0u) << s;
+        const float *vr = V + (ok ? row0 + dv : runs.safe()) * kHeadDim + 8 * j;
+        cr.v[s][0] = as_f32x4(ld_nt16(vr));
+        cr.v[s][1] = as_f32x4(ld_nt16(vr + 4));
     }
 }
 
-template <int NW>
-__device__ void load_q_f32(const AttnArgs &a, int pair, F32Lds<NW> &fl) {
+__device__ __forceinline__ void compute_chunk_f32(const ChunkRegsF32 &cr, const f32x4 (&qf)[8],
+                                                  float scale_log2, int g, WaveState &st) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cr.k[n][e], qf[n][e], acc, 0, 0, 0);
+    float s[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = ((cr.ok >> r) & 1u) ? acc[r] * scale_log2 : -INFINITY;
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(st.m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(st.m_run - m_use);  // 0 while nothing was seen
+    float p[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        p[r] = exp2f(s[r] - m_use);
+        psum += p[r];
+    }
+    st.l_run = st.l_run * alpha + psum;
+    st.m_run = m_new;
+    // rescale O rows (heads 4g + r) by their heads' alpha
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(alpha, 4 * g + r);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) st.o[n][r] *= ar;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+            st.o[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[t], cr.v[t][n >> 2][n & 3], st.o[n],
+                                                          0, 0, 0);
+}
+
+// The B operand of the fp32 S^T = K . Q^T for this lane: head j = lane % 16
+// (zero past the group), channels 16n + 4g .. +3, g = lane / 16.  Loaded by
+// the kernels ahead of time, so its round trip overlaps earlier work.
+__device__ __forceinline__ void load_q_f32(const AttnArgs &a, int pair, f32x4 (&qf)[8]) {
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 15, g = lane >> 4;
     const int b = pair / a.hkv, gk = pair % a.hkv;
     const int hq = a.hkv * a.gqa;
-    for (int i = threadIdx.x; i < kMaxGqa * kHeadDim; i += NW * 64) {
-        const int h = i / kHeadDim, c = i % kHeadDim;
-        fl.q[h][c] = h < a.gqa ? static_cast<const float *>(a.q)[((size_t)b * hq + gk * a.gqa + h) *
-                                                                 kHeadDim + c]
-                               : 0.f;
+    const bool live = j < a.gqa;
+    const float *qp = static_cast<const float *>(a.q) +
+                      ((size_t)b * hq + (size_t)gk * a.gqa + (live ? j : 0)) * kHeadDim + 4 * g;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+        f32x4 v = *reinterpret_cast<const f32x4 *>(qp + 16 * n);
+        qf[n] = live ? v : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+}
+
+// One wave's share of a pair's chunks [c_beg, c_end), every `step`-th chunk
+// starting at c_beg + first, then its (m, l, o) into merge slot `slot`
+// (fp32; `runs` maps list positions to cache rows: DenseRuns, ListRuns;
+// qf from load_q_f32).
+template <class Runs, int NW>
+__device__ void attend_f32(const AttnArgs &a, const Runs &runs, const f32x4 (&qf)[8], int c_beg,
+                           int c_end, int first, int step, int slot, MergeLds<NW> &sm) {
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 15, g = lane >> 4;
+    const float *Kp = static_cast<const float *>(a.K);
+    const float *Vp = static_cast<const float *>(a.V);
+    WaveState st;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) st.o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
+
+    // two register buffers: chunk i computes while chunk i + 1 loads (the
+    // tail is peeled, so the loads inside the loop are unconditional)
+    const int c0 = c_beg + first;
+    const int n = c0 < c_end ? (c_end - c0 + step - 1) / step : 0;
+    ChunkRegsF32 ra, rb;
+    if (n > 0) {
+        load_chunk_f32(a, runs, Kp, Vp, c0, j, g, ra);
+        int i = 0;
+        for (; i + 2 < n; i += 2) {
+            load_chunk_f32(a, runs, Kp, Vp, c0 + (i + 1) * step, j, g, rb);
+            compute_chunk_f32(ra, qf, a.scale_log2, g, st);
+            load_chunk_f32(a, runs, Kp, Vp, c0 + (i + 2) * step, j, g, ra);
+            compute_chunk_f32(rb, qf, a.scale_log2, g, st);
+        }
+        if (n - i == 2) {
+            load_chunk_f32(a, runs, Kp, Vp, c0 + (i + 1) * step, j, g, rb);
+            compute_chunk_f32(ra, qf, a.scale_log2, g, st);
+            compute_chunk_f32(rb, qf, a.scale_log2, g, st);
+        } else {
+            compute_chunk_f32(ra, qf, a.scale_log2, g, st);
+        }
+    }
+
+    float l_tot = st.l_run + __shfl_xor(st.l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (lane < 16) {
+        sm.m[slot][lane] = st.m_run;
+        sm.l[slot][lane] = l_tot;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int n2 = 0; n2 < 8; ++n2) sm.o[slot][4 * g + r][8 * j + n2] = st.o[n2][r];
 }
 
 // Bytes of the split partials (o, then m and l) of one attention call.

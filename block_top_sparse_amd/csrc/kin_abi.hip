@@ -287,7 +287,8 @@ kin_status kin_decode_select_attend(const kin_desc *desc, const void *q, const v
 // the scores in the workspace).
 static size_t step_ws_need(const kin::Geo &g, int32_t k, int cu, bool scores) {
     if (kin::step_single_kernel(g, k, cu)) return 0;
-    if (!g.pages && !g.share_n && kin::step_f32_single_kernel(g, k)) return 0;
+    if (!g.pages && !g.share_n && kin::step_f32_single_kernel(g, k))
+        return kin::step_f32_ws_bytes(g, k);
     const kin::AttnPlan p = kin::plan_step(g, k, cu);
     return scores ? p.ws_bytes : kin::step_ws_with_scores(g, p);
 }
@@ -311,9 +312,12 @@ static kin_status decode_step(const kin::Geo &g, const void *q, const void *K, c
     if (kin::step_single_kernel(g, k, cu))
         return launched(kin::launch_decode_step(g, q, K, V, S, scores, k, idx, out, cu, s),
                         "kin_sparse_decode_step");
-    if (!g.pages && !g.share_n && kin::step_f32_single_kernel(g, k))
-        return launched(kin::launch_decode_step_f32(g, q, K, V, S, scores, k, idx, out, s),
+    if (!g.pages && !g.share_n && kin::step_f32_single_kernel(g, k)) {
+        st = check_ws_size(kin::step_f32_ws_bytes(g, k), ws, ws_bytes);
+        if (st != KIN_OK) return st;
+        return launched(kin::launch_decode_step_f32(g, q, K, V, S, scores, k, idx, out, ws, s),
                         "kin_sparse_decode_step");
+    }
     const kin::AttnPlan p = kin::plan_step(g, k, cu);
     // two kernels hand the scores over in memory: the caller's buffer, or
     // the workspace after the attention's part
@@ -586,9 +590,9 @@ size_t kin_sparse_ws_bytes(const kin_desc *desc, int32_t k) {
     const int cu = num_cu();
     const size_t a = kin::plan_attention(g, k, false, cu).ws_bytes;
     // the step's two-kernel form, with room for the scores (scores == NULL)
-    const size_t b = kin::step_single_kernel(g, k, cu) || kin::step_f32_single_kernel(g, k)
-                         ? 0
-                         : kin::step_ws_with_scores(g, kin::plan_step(g, k, cu));
+    const size_t b = kin::step_single_kernel(g, k, cu)      ? 0
+                     : kin::step_f32_single_kernel(g, k) ? kin::step_f32_ws_bytes(g, k)
+                                                         : kin::step_ws_with_scores(g, kin::plan_step(g, k, cu));
     return a > b ? a : b;
 }
 

@@ -13,7 +13,7 @@ constexpr int kHeadDim = 128;  // the only head_dim built
 constexpr int kMaxGqa = 16;    // query heads of one group fit one 16-row MFMA tile
 constexpr int kMaxBlocks = 16384;
 constexpr int kChunkBf16 = 32;  // tokens per wave iteration, bf16 attention
-constexpr int kChunkF32 = 64;   // tokens per wave iteration, fp32 attention
+constexpr int kChunkF32 = 16;   // tokens per wave iteration, fp32 attention
 constexpr int kStepIdxCap = 2048;  // kept blocks the select+attend kernels hold in LDS
 constexpr int kTokIdxCap = 8192;   // kept tokens of the token-level step (LDS)
 constexpr int kTokMaxLen = 262144;  // tokens of one pair the two-kernel token step takes
@@ -88,12 +88,13 @@ hipError_t launch_select_attend(const Geo &g, const AttnPlan &p, const void *q, 
 // the whole decode step in one kernel (one workgroup per pair); usable when
 // step_single_kernel() says so (bf16, enough pairs to cover the chip)
 bool step_single_kernel(const Geo &g, int k, int num_cu);
-// the whole fp32 decode step in one kernel (one workgroup per pair) for
-// steps of small per-pair bytes (contiguous caches)
+// the whole fp32 decode step in one kernel (a few workgroups per pair) for
+// steps of small per-pair bytes (contiguous caches); its workspace
 bool step_f32_single_kernel(const Geo &g, int k);
+size_t step_f32_ws_bytes(const Geo &g, int k);
 hipError_t launch_decode_step_f32(const Geo &g, const void *q, const void *K, const void *V,
                                   void *S, double *scores, int k, int32_t *idx, void *out,
-                                  hipStream_t s);
+                                  void *ws, hipStream_t s);
 // the arrival words of a plan's in-kernel combine (the start of ws;
 // nullptr: the plan has none)
 uint64_t *step_ctrl(const AttnPlan &p, void *ws);

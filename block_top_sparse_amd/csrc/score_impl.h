@@ -113,8 +113,8 @@ __device__ __forceinline__ void store_score(double *scores, size_t at, double x)
 
 // Newest-block summary (one wave, lane = channels 2l, 2l+1): fp64 sum in
 // ascending token order, fp64 division, fp64 -> fp32 -> (bf16) rounding.
-// Writes the row to S and, if row_lds is not null, to row_lds (the same
-// 256 / 512 B row layout).
+// Writes the row to S (unless S is null) and, if row_lds is not null, to
+// row_lds (the same 256 / 512 B row layout).
 template <int DT>
 __device__ void newest_summary(const void *K, void *S, size_t pair, int t_cap, int nb_cap,
                                int ctx_len, int block, uint32_t *row_lds, int lane) {
@@ -146,10 +146,10 @@ __device__ void newest_summary(const void *K, void *S, size_t pair, int t_cap, i
     const size_t o = (pair * (size_t)nb_cap + (size_t)j) * (kHeadDim / 2) + lane;
     if (DT == KIN_BF16) {
         const uint32_t w = f32_to_bf16_bits(m0) | (f32_to_bf16_bits(m1) << 16);
-        static_cast<uint32_t *>(S)[o] = w;
+        if (S) static_cast<uint32_t *>(S)[o] = w;
         if (row_lds) row_lds[lane] = w;
     } else {
-        static_cast<float2 *>(S)[o] = make_float2(m0, m1);
+        if (S) static_cast<float2 *>(S)[o] = make_float2(m0, m1);
         if (row_lds) {
             row_lds[2 * lane] = __float_as_uint(m0);
             row_lds[2 * lane + 1] = __float_as_uint(m1);

@@ -1,31 +1,35 @@
 // step_f32.hip -- a whole fp32 block top-k sparse decode step in ONE
-// kernel, one workgroup (8 waves) per (sequence, KV head) pair, for steps
-// whose per-pair bytes are small (a short context and a small budget: the
-// tiny fp32 layer):
+// kernel for steps whose per-pair bytes are small (a short context and a
+// small budget: the tiny fp32 layer).  Each (sequence, KV head) pair runs
+// on `nsplit` workgroups of 8 waves; every one of them
 //
-//   1. wave 0 rebuilds the newest block's summary (fp64 mean in token
-//      order, rounded to fp32), writes it to S and keeps it in LDS, while
-//      every wave scores its share of the other blocks against the group's
+//   1. rebuilds the newest block's summary in LDS (fp64 mean in token
+//      order, rounded to fp32; split 0 also writes it to S) with wave 0,
+//      while all waves score the pair's other blocks against the group's
 //      query sum (fp64, the per-lane math and butterfly of k_block_score,
 //      so the scores are bit for bit those of the two-kernel step); wave 0
 //      then scores the newest block from its LDS row.  The scores stay in
 //      LDS and are counted into the select's exponent tables;
-//   2. the workgroup selects the top k blocks (select.h);
-//   3. the waves attend over the kept tokens (fp32 VALU, 64 tokens per
-//      chunk, a whole key row and 32 value rows per lane in flight) and
-//      merge into the output.
+//   2. selects the top k blocks (select.h; split 0 writes idx and, if
+//      asked, the scores);
+//   3. attends over its share of the kept tokens (fp32 MFMA, 16 tokens per
+//      chunk); with one split it merges its waves into the output, else it
+//      writes a partial (o, m, l) and the pair's last split to arrive
+//      combines the partials (the workspace's arrival word of the pair).
 //
 // The steps are those of BlockTopKAttention (skill summary "Kinetics:
 // Memory-Aware Test-Time Scaling", Implementation) with KV blocks and a
 // budget of k blocks (rebuttal "Kinetics: Rethinking Test-Time Scaling
 // Law", Q4 "KV block size and grouping strategy").
 //
-// Why one kernel here: such a step moves about a megabyte, so its time is
-// a chain of latencies (launches, memory round trips, barriers), not
-// bandwidth.  The two-kernel form paid a second launch and ran its
-// attention on one workgroup per pair anyway (too few chunks to split), so
-// one workgroup per pair doing the whole step removes a launch and the
-// scores' trip through memory.
+// Why this shape: such a step moves about a megabyte, so its time is a
+// chain of latencies, and one compute unit pulls only ~50 GB/s (its
+// outstanding misses are bounded): one workgroup per pair spent 12-14 us
+// reading 512 KiB of kept K/V.  Splitting the kept tokens over several
+// workgroups spreads those bytes over as many compute units; repeating the
+// pair's small scan and selection in every split costs less than handing
+// scores between workgroups (no wait anywhere: the arrival count is the
+// only exchange, and nobody waits on it).
 #include "attn_impl.h"
 #include "score_impl.h"
 
@@ -35,6 +39,9 @@ constexpr int kStepF32MaxBlocks = 8192;
 // per-pair bytes (summary rows + kept K and V rows) up to which the fp32
 // step runs as this one kernel
 constexpr size_t kStepF32MaxPairBytes = (size_t)1 << 20;
+// kept-token chunks (16 tokens) each split attends: 4 (64 tokens, 64 KiB of
+// K and V)
+constexpr int kStepF32ChunksPerSplit = 4;
 
 struct StepF32Extra {
     void *S;
@@ -43,10 +50,9 @@ struct StepF32Extra {
     int nb_cap;
 };
 
-// MG: a bound on the group's query heads (8 or 16); with at most 8 the
-// attention keeps a whole key row per lane in flight, else half of it.
-template <int KPT, int MG>
-__global__ __launch_bounds__(kStepThreads) void k_decode_step_f32(AttnArgs a, StepF32Extra x) {
+template <int KPT>
+__global__ __launch_bounds__(kStepThreads) void k_decode_step_f32(AttnArgs a, StepF32Extra x,
+                                                                  uint64_t *ctrl) {
     constexpr int NT = kStepThreads, NW = NT / 64;
     __shared__ int32_t sel[kStepIdxCap];
     __shared__ SelectLds<KPT, NT> sl;
@@ -54,16 +60,15 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step_f32(AttnArgs a, St
         double sc[kStepF32MaxBlocks];
         MergeLds<NW> m;
     } u;
-    __shared__ F32Lds<NW> fl;
     __shared__ uint32_t row_lds[kHeadDim];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int pair = blockIdx.x;
+    const int split = blockIdx.x, pair = blockIdx.y;
     const int b = pair / a.hkv, g = pair % a.hkv;
     const int nb = a.nb;
     const size_t row0 = (size_t)pair * x.nb_cap;
-    double *sc_out = x.scores ? x.scores + row0 : nullptr;
+    double *sc_out = x.scores && split == 0 ? x.scores + row0 : nullptr;
     auto emit = [&](int j, double v) {
         if (v == 0.0) v = 0.0;  // one zero: -0.0 becomes +0.0
         u.sc[j] = v;
@@ -71,8 +76,11 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step_f32(AttnArgs a, St
         select_count(sl, v);
     };
 
+    // the attention's query operand, loaded now so its round trip overlaps
+    // the scoring
+    f32x4 qf[8];
+    load_q_f32(a, pair, qf);
     select_clear(sl);
-    load_q_f32<NW>(a, pair, fl);
     __syncthreads();
 
     // 1. scores.  Rows of blocks below the newest one, 16 per wave and
@@ -84,8 +92,8 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step_f32(AttnArgs a, St
     double qs[8];
     group_query_sum<KIN_F32>(a.q, b, g, a.hkv, a.gqa, sub, qs);
     if (wave == 0)
-        newest_summary<KIN_F32>(a.K, x.S, pair, a.t_cap, x.nb_cap, a.ctx_len, a.block, row_lds,
-                                lane);
+        newest_summary<KIN_F32>(a.K, split == 0 ? x.S : nullptr, pair, a.t_cap, x.nb_cap,
+                                a.ctx_len, a.block, row_lds, lane);
     wave_lds_sync();  // wave 0's row_lds entries, read across its lanes below
     const int n_rows = nb - 1;
     constexpr int kRound = NW * 16;
@@ -134,14 +142,45 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step_f32(AttnArgs a, St
     // 2. selection (the scores are dead afterwards: the merge reuses them)
     select_topk<KPT, NT, true>(u.sc, nb, a.k, sel, sl);
     __syncthreads();
-    for (int i = tid; i < a.k; i += NT) x.idx[(size_t)pair * a.k + i] = sel[i];
+    if (split == 0)
+        for (int i = tid; i < a.k; i += NT) x.idx[(size_t)pair * a.k + i] = sel[i];
 
-    // 3. attention over the kept tokens, then the merge of the 8 waves
-    constexpr int KB = MG <= 8 ? 32 : 16;
-    attend_f32<false, NW, KB, 32, MG>(a, sel, pair, 0, a.n_chunks, wave, NW, wave, fl, u.m);
+    // 3. attention over this split's kept tokens, then the merge of the 8
+    // waves; with several splits, the pair's last one combines
+    const int cps = (a.n_chunks + a.nsplit - 1) / a.nsplit;
+    const int c_beg = split * cps;
+    const int c_end = min(a.n_chunks, c_beg + cps);
+    attend_f32<ListRuns, NW>(a, list_runs(a, pair, sel), qf, c_beg, c_end, wave, NW, wave, u.m);
     __syncthreads();
-    merge_waves_and_store<KIN_F32, NW>(a, u.m, pair, 0);
+    if (a.nsplit == 1) {
+        merge_waves_and_store<KIN_F32, NW>(a, u.m, pair, 0);
+        return;
+    }
+    merge_waves_and_store<KIN_F32, NW, true>(a, u.m, pair, split);
+    stores_complete();
+    __shared__ uint32_t last;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        // the word was zero on entry (left so by the previous call on this
+        // workspace); the last arrival leaves it at zero again
+        last = arrive_add(ctrl + pair) == (uint32_t)a.nsplit;
+        if (last) st_agent(ctrl + pair, (uint64_t)0);
+    }
+    __syncthreads();
+    if (last) combine_pair<KIN_F32, NT>(a, pair);
 }
+
+// splits per pair of the one-kernel fp32 step
+static int step_f32_splits(const Geo &g, int k) {
+    const int keff = k < g.nb ? k : g.nb;
+    const int n_chunks = (keff * g.block + kChunkF32 - 1) / kChunkF32;
+    int ns = (n_chunks + kStepF32ChunksPerSplit - 1) / kStepF32ChunksPerSplit;
+    if (ns > 64) ns = 64;
+    if (ns < 1 || g.pairs > kCtrlWords) ns = 1;
+    return ns;
+}
+
+size_t step_f32_ws_bytes(const Geo &g, int k) { return ws_total(ws_for(g, step_f32_splits(g, k))); }
 
 bool step_f32_single_kernel(const Geo &g, int k) {
     if (g.dtype != KIN_F32 || g.nb > kStepF32MaxBlocks || k > kStepIdxCap) return false;
@@ -152,25 +191,21 @@ bool step_f32_single_kernel(const Geo &g, int k) {
 
 hipError_t launch_decode_step_f32(const Geo &g, const void *q, const void *K, const void *V,
                                   void *S, double *scores, int k, int32_t *idx, void *out,
-                                  hipStream_t s) {
+                                  void *ws, hipStream_t s) {
     AttnPlan p;
     const int keff = k < g.nb ? k : g.nb;
     p.n_tokens = keff * g.block;
     p.n_chunks = (p.n_tokens + kChunkF32 - 1) / kChunkF32;
-    p.nsplit = 1;
+    p.nsplit = step_f32_splits(g, k);
     p.fused = 1;
-    p.ws_bytes = 0;
+    p.ws_bytes = step_f32_ws_bytes(g, k);
     AttnArgs a;
-    fill_args(a, g, p, q, K, V, nullptr, k, out, nullptr);
+    fill_args(a, g, p, q, K, V, nullptr, k, out, ws);
     const StepF32Extra x{S, scores, idx, g.nb_cap};
-    const dim3 grid(g.pairs);
-#define KIN_F32_STEP(KPT)                                                            \
-    do {                                                                             \
-        if (g.gqa <= 8)                                                              \
-            k_decode_step_f32<KPT, 8><<<grid, kStepThreads, 0, s>>>(a, x);           \
-        else                                                                         \
-            k_decode_step_f32<KPT, kMaxGqa><<<grid, kStepThreads, 0, s>>>(a, x);     \
-    } while (0)
+    // the pair's arrival word: the start of the workspace
+    uint64_t *ctrl = p.nsplit > 1 ? static_cast<uint64_t *>(ws) : nullptr;
+    const dim3 grid(p.nsplit, g.pairs);
+#define KIN_F32_STEP(KPT) k_decode_step_f32<KPT><<<grid, kStepThreads, 0, s>>>(a, x, ctrl)
     switch (select_kpt(g.nb, kStepThreads)) {
     case 1: KIN_F32_STEP(1); break;
     case 2: KIN_F32_STEP(2); break;

@@ -64,6 +64,7 @@ BLOCK = [
     ("graph-two-kernel", 3, 16, 2, 5000, 16, 100, "bf16", 5120, True),
     ("graph-keepall", 2, 16, 4, 2000, 16, 125, "bf16", 2048, False),       # one launch, splits
     ("graph-f32-split", 3, 2, 2, 4730, 16, 292, "f32", 4793, True),        # fp32 split step
+    ("graph-f32-one", 1, 8, 2, 4096, 16, 32, "f32", 4096, False),          # fp32 one kernel
 ]
 
 

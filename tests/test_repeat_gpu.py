@@ -50,6 +50,7 @@ BLOCK = [
     ("rep-two-kernel-nosc", 3, 16, 2, 5000, 16, 100, "bf16", 5120, False),
     ("rep-keepall", 2, 16, 4, 2000, 16, 125, "bf16", 2048, False),       # one launch
     ("rep-f32-split", 3, 2, 2, 4730, 16, 292, "f32", 4793, True),        # fp32 kernel 1 clears
+    ("rep-f32-one", 1, 8, 2, 4096, 16, 32, "f32", 4096, False),          # fp32 one kernel, splits
 ]
 
 
@@ -181,6 +182,7 @@ def test_one_workspace_zeroed_once_serves_every_split_form():
     block_case("ws-half", 3, 16, 2, 5000, 16, 100, "bf16", 5120, "half")
     block_case("ws-f32", 3, 2, 2, 4730, 16, 292, "f32", 4793, "step")
     block_case("ws-attn", 2, 8, 2, 6000, 32, 150, "bf16", 6016, "attn")
+    block_case("ws-f32-one", 1, 8, 2, 4096, 16, 32, "f32", 4096, "step")
 
     wt = Workload("ws-token", batch=2, hq=8, hkv=2, ctx_len=20000, block=1, topk=500,
                   dtype="bf16", seed=915, t_cap=20000)

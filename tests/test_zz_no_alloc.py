@@ -58,6 +58,8 @@ PAIRS = [
      ("na-c", 3, 32, 4, 4000, 32, 125, "bf16", 4096), ("na-d", 2, 16, 4, 2000, 16, 125, "bf16", 2048)),
     ("fp32-split",
      ("na-e", 3, 4, 2, 9000, 16, 500, "f32", 9024), ("na-f", 3, 2, 2, 4730, 16, 292, "f32", 4793)),
+    ("fp32-one-kernel",
+     ("na-i", 1, 8, 2, 4096, 16, 32, "f32", 4096), ("na-j", 1, 4, 2, 2048, 16, 16, "f32", 2048)),
     ("four-launch-bf16",
      ("na-g", 1, 8, 2, 40000, 16, 2100, "bf16", 40000), ("na-h", 1, 8, 2, 36000, 16, 2050, "bf16", 36000)),
 ]
