@@ -132,6 +132,7 @@ FEW_PAIRS = [
     # name, batch, hq, hkv, ctx, block, k, dtype, t_cap  (bf16, fewer pairs than CUs: the
     # two-kernel step)
     ("few-g4-b16-ragged", 3, 16, 4, 5000, 16, 40, "bf16", 5120),
+    ("few-255-pairs", 51, 20, 5, 3000, 16, 30, "bf16", 3008),       # one CU short of one per pair
     ("few-g8-b64-k1", 2, 64, 8, 3000, 64, 1, "bf16", 3072),         # one split
     ("few-g5-b32-kpast", 4, 20, 4, 700, 32, 40, "bf16", 704),       # k > nb
     ("few-g1-b16-nb8192", 1, 2, 2, 131072, 16, 512, "bf16", 131072),

@@ -48,6 +48,7 @@ BLOCK = [
     # name, batch, hq, hkv, ctx, block, k, dtype, t_cap, scores
     ("rep-two-kernel", 3, 16, 2, 5000, 16, 100, "bf16", 5120, True),     # kernel 1 clears words
     ("rep-two-kernel-nosc", 3, 16, 2, 5000, 16, 100, "bf16", 5120, False),
+    ("rep-two-kernel-one-split", 2, 64, 8, 3000, 64, 1, "bf16", 3072, False),  # one split per pair
     ("rep-keepall", 2, 16, 4, 2000, 16, 125, "bf16", 2048, False),       # one launch
     ("rep-f32-split", 3, 2, 2, 4730, 16, 292, "f32", 4793, True),        # fp32 kernel 1 clears
     ("rep-f32-one", 1, 8, 2, 4096, 16, 32, "f32", 4096, False),          # fp32 one kernel, splits
@@ -142,7 +143,8 @@ def test_two_streams_at_once_match_one_after_the_other():
 
 def test_one_workspace_zeroed_once_serves_every_split_form():
     """One workspace, zeroed once, used in turn by split forms of different
-    shapes and entry points: the keep-all one-launch step, the standalone
+    shapes and entry points: the keep-all one-launch step, the bf16 two-kernel
+    step (its first kernel clears the second's words), the standalone
     second half (kin_decode_select_attend), the fp32 two-kernel step, the
     standalone split attention, the token-level and Quest two-kernel steps.
     After every call the first 8 KiB (the arrival words) are zero again, and
@@ -179,6 +181,7 @@ def test_one_workspace_zeroed_once_serves_every_split_form():
         calls.append((name, call, need, outs))
 
     block_case("ws-keepall", 2, 16, 4, 2000, 16, 125, "bf16", 2048, "step")
+    block_case("ws-two-kernel", 1, 8, 2, 40000, 32, 64, "bf16", 40000, "step")
     block_case("ws-half", 3, 16, 2, 5000, 16, 100, "bf16", 5120, "half")
     block_case("ws-f32", 3, 2, 2, 4730, 16, 292, "f32", 4793, "step")
     block_case("ws-attn", 2, 8, 2, 6000, 32, 150, "bf16", 6016, "attn")
