@@ -209,15 +209,21 @@ def single_kernel(w, num_cu):
 
 def step_kernels(w, num_cu):
     """The launches of one kin_sparse_decode_step without a scores output, as
-    the library plans them: "one" (the whole step per pair), "one-split" (a
-    step that keeps every block, few pairs: select + split attention alone),
-    "two" (score tiles, then select + split attention), "four" (more than
-    2048 kept blocks: scores or the newest row, top-k, attention, combine)."""
+    the library plans them: "one" (the whole step per pair), "one-f32" (the
+    fp32 step of at most 1 MiB per pair in one kernel, split over several
+    workgroups per pair), "one-split" (a step that keeps every block, few
+    pairs: select + split attention alone), "two" (score tiles, then select
+    + split attention), "four" (more than 2048 kept blocks: scores or the
+    newest row, top-k, attention, combine)."""
     if single_kernel(w, num_cu):
         return "one"
     if w.topk > 2048:
         return "four"
-    return "one-split" if w.topk >= w.nb and w.dtype == "bf16" else "two"
+    if w.dtype == "f32":
+        keff = min(w.topk, w.nb)
+        small = w.nb <= 8192 and w.nb * 512 + keff * w.block * 1024 <= 1 << 20
+        return "one-f32" if small else "two"
+    return "one-split" if w.topk >= w.nb else "two"
 
 
 def run_sweep(args):
@@ -513,6 +519,7 @@ def cpu_baseline(w, layer, max_seqs, min_seconds=10.0, single_seqs=2, single_sec
 
 
 KERNEL_NAMES = {"one": "k_decode_step",
+                "one-f32": "k_decode_step_f32 (one launch, splits per pair)",
                 "one-split": "k_select_attend (one launch)",
                 "two": "k_score_tiles + k_select_attend (two launches)",
                 "two-f32": "k_block_score + k_select_attend (two launches)",

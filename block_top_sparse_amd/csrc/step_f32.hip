@@ -87,27 +87,29 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step_f32(AttnArgs a, St
     // round (4 rows per 16-lane group load), the next round's loads issued
     // before this round's math; past the range a load re-reads the last
     // scored row and its score is dropped.  The newest row is never loaded
-    // here: wave 0 rewrites it during this phase.
+    // here: wave 0 rewrites it during this phase.  The first round's loads
+    // go out before the query rows are summed (they do not need the sum),
+    // so their round trip overlaps the query's and the newest row's.
     const int sub = lane & 15, grp = lane >> 4;
+    const int n_rows = nb - 1;
+    constexpr int kRound = NW * 16;
+    const int n_it = wave * 16 < n_rows ? (n_rows - wave * 16 + kRound - 1) / kRound : 0;
+    auto load_round = [&](int it, u32x4 (&ra)[4], u32x4 (&rb)[4]) {
+        const int j0 = wave * 16 + it * kRound;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            load_row_slice<KIN_F32>(x.S, row0 + min(j0 + 4 * v + grp, n_rows - 1), sub, ra[v],
+                                    rb[v]);
+    };
+    u32x4 wa[2][4], wb[2][4];
+    if (n_it > 0) load_round(0, wa[0], wb[0]);
     double qs[8];
     group_query_sum<KIN_F32>(a.q, b, g, a.hkv, a.gqa, sub, qs);
     if (wave == 0)
         newest_summary<KIN_F32>(a.K, split == 0 ? x.S : nullptr, pair, a.t_cap, x.nb_cap,
                                 a.ctx_len, a.block, row_lds, lane);
     wave_lds_sync();  // wave 0's row_lds entries, read across its lanes below
-    const int n_rows = nb - 1;
-    constexpr int kRound = NW * 16;
-    const int n_it = wave * 16 < n_rows ? (n_rows - wave * 16 + kRound - 1) / kRound : 0;
     if (n_it > 0) {
-        auto load_round = [&](int it, u32x4 (&ra)[4], u32x4 (&rb)[4]) {
-            const int j0 = wave * 16 + it * kRound;
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                load_row_slice<KIN_F32>(x.S, row0 + min(j0 + 4 * v + grp, n_rows - 1), sub, ra[v],
-                                        rb[v]);
-        };
-        u32x4 wa[2][4], wb[2][4];
-        load_round(0, wa[0], wb[0]);
         for (int it = 0; it < n_it; ++it) {
             const int cur = it & 1;
             // the next round (or a harmless repeat of the last one)

@@ -33,7 +33,8 @@ def test_launch_form_labels_follow_the_dispatch_rules():
     scores output): one kernel when the pairs cover the chip (at most 8192
     blocks and 2048 kept), the split select + attend alone when few pairs
     keep every block, score tiles + select/attend for few pairs otherwise,
-    and four launches past 2048 kept blocks."""
+    and four launches past 2048 kept blocks; the tiny fp32 layer is one
+    fp32 kernel."""
     sys.path.insert(0, ROOT)
     import bench
     from block_top_sparse_amd import workloads
@@ -41,6 +42,7 @@ def test_launch_form_labels_follow_the_dispatch_rules():
     cu = 256
     form = {w.name: bench.step_kernels(w, cu) for w in workloads.sweep()}
     assert bench.step_kernels(workloads.QWEN3_8B, cu) == "one"
+    assert bench.step_kernels(workloads.TINY, cu) == "one-f32"                # 640 KiB per pair
     assert form["sweep-b32-ctx32768-blk16-budget1024"] == "one"        # 256 pairs
     assert form["sweep-b8-ctx32768-blk16-budget8192"] == "two"         # 64 pairs, 512 of 2048
     assert form["sweep-b8-ctx8192-blk16-allblocks"] == "one-split"     # 64 pairs, all 512 kept
