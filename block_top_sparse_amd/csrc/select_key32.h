@@ -21,6 +21,18 @@
 // more 8-bit passes; keys equal in all 64 bits keep the lower indices.  The
 // ordered compaction takes two sweeps (per (round, wave) counts of the keys
 // kept for sure and of the exact ties, a workgroup scan, then the writes).
+//
+// Shared form (Key32Share, the few-pair two-kernel step): the nsplit
+// workgroups of one pair, which all need the whole kept list, each sweep
+// only their own contiguous range of the keys.  Every pass's 256 counts are
+// summed over the splits through the workspace (agent-scope stores and
+// loads, one arrival count per exchange), so every split takes the same
+// decisions; the compaction exchanges the splits' totals the same way (the
+// keys of the lower splits come first in index order), each split writes its kept
+// indices into a list in the workspace, and every split reads the whole
+// list back.  A split waits only for the other splits of its pair, which
+// have all started by then (the splits of a pair take consecutive places in
+// the launch's start order).
 #pragma once
 
 #include "attn_impl.h"
@@ -74,10 +86,12 @@ __device__ __noinline__ double exact_score_row(const uint16_t *row, const double
 }
 
 // Exclusive prefix sums, in place, of a[0..n) and b[0..n) over the whole
-// workgroup (each thread scans a contiguous segment).  Ends with a barrier.
+// workgroup (each thread scans a contiguous segment); ta, tb: the totals.
+// Ends with a barrier.
 template <int NT>
 __device__ void block_exclusive_scan2(uint32_t *a, uint32_t *b, int n,
-                                      uint32_t (&wsum)[2][NT / 64]) {
+                                      uint32_t (&wsum)[2][NT / 64], uint32_t &ta,
+                                      uint32_t &tb) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m = (n + NT - 1) / NT;
@@ -94,9 +108,14 @@ __device__ void block_exclusive_scan2(uint32_t *a, uint32_t *b, int n,
     }
     __syncthreads();
     uint32_t oa = ia - sa, ob = ib - sb;
-    for (int w = 0; w < wave; ++w) {
-        oa += wsum[0][w];
-        ob += wsum[1][w];
+    ta = tb = 0;
+    for (int w = 0; w < NT / 64; ++w) {
+        if (w < wave) {
+            oa += wsum[0][w];
+            ob += wsum[1][w];
+        }
+        ta += wsum[0][w];
+        tb += wsum[1][w];
     }
     for (int i = s0; i < s1; ++i) {
         const uint32_t va = a[i], vb = b[i];
@@ -141,35 +160,123 @@ __device__ __forceinline__ void coarse_from_fine(const uint32_t *fine, uint32_t 
     }
 }
 
-// f(j0, x) for every batch of keys j0 + u * NT + threadIdx.x (u < B), in
-// order.
+// f(j0, x) for every batch of keys j0 + u * NT + threadIdx.x (u < B) with
+// j0 in [lo, hi), in order (lo and hi multiples of B * NT, or hi = n).
 template <int NT, int B, class F>
-__device__ __forceinline__ void key32_sweep(const uint32_t *key, int n, F f) {
-    for (int j0 = 0; j0 < n; j0 += B * NT) {
+__device__ __forceinline__ void key32_sweep(const uint32_t *key, int n, int lo, int hi, F f) {
+    for (int j0 = lo; j0 < hi; j0 += B * NT) {
         uint32_t x[B];
         key32_batch<NT, B>(key, n, j0, x);
         f(j0, x);
     }
 }
 
+// The splits of one pair that share its selection (ns == 1: none).
+struct Key32Share {
+    int ns, split;
+    int lo, hi;       // this split's keys [lo, hi)
+    uint32_t *hist;   // [2][ns][256] pass counts, by exchange parity
+    int32_t *list;    // [k] the kept indices
+    uint64_t *word;   // the pair's exchange count (zero on entry)
+};
+
+__device__ __forceinline__ Key32Share key32_alone(int n) {
+    return Key32Share{1, 0, 0, n, nullptr, nullptr, nullptr};
+}
+
+// polls of one exchange before it gives up (about a second; a correct count
+// is reached in microseconds)
+constexpr uint32_t kSharePollLimit = 1u << 20;
+
+// Agent-scope accesses to the exchange areas, through global-memory pointers
+// (those areas are always in the workspace, never in LDS).
+template <class T>
+__device__ __forceinline__ void st_ws(T *p, T v) {
+    typedef __attribute__((address_space(1))) T gT;
+    __hip_atomic_store((gT *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T ld_ws(const T *p) {
+    typedef __attribute__((address_space(1))) T gT;
+    return __hip_atomic_load((gT *)const_cast<T *>(p), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// This split's stores done, its arrival counted, then the wait until every
+// split of the pair has made `round` arrivals.  Every thread calls this.
+__device__ __forceinline__ void share_arrive_wait(const Key32Share &x, uint32_t round) {
+    stores_complete();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        typedef __attribute__((address_space(1))) uint64_t gu64;
+        __hip_atomic_fetch_add((gu64 *)x.word, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t want = (uint64_t)round * (uint64_t)x.ns;
+        uint32_t polls = 0;
+        while (ld_ws(x.word) < want && ++polls < kSharePollLimit) __builtin_amdgcn_s_sleep(1);
+    }
+    __syncthreads();
+}
+
+// h[0..256) (LDS, this split's counts) becomes the sum over the pair's
+// splits, added in split order.  Ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void share_hist(uint32_t *h, const Key32Share &x, uint32_t &round) {
+    if (x.ns == 1) return;
+    uint32_t *slot = x.hist + (size_t)(round & 1u) * x.ns * 256;
+    for (int i = threadIdx.x; i < 256; i += NT) st_ws(slot + x.split * 256 + i, h[i]);
+    share_arrive_wait(x, ++round);
+    for (int i = threadIdx.x; i < 256; i += NT) {
+        uint32_t sum = 0;
+        for (int sp = 0; sp < x.ns; ++sp) sum += ld_ws(slot + sp * 256 + i);
+        h[i] = sum;
+    }
+    __syncthreads();
+}
+
+// The kept and tie counts of the splits before this one (its keys' ranks
+// start there): every split's (gt, tie) in slots 2 split, 2 split + 1 of
+// the zeroed LDS vector tv, summed over the splits.  Ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void share_totals(uint32_t *tv, uint32_t gt, uint32_t tie,
+                                             const Key32Share &x, uint32_t &round,
+                                             uint32_t &gt_before, uint32_t &tie_before) {
+    if (threadIdx.x == 0) {
+        tv[2 * x.split] = gt;
+        tv[2 * x.split + 1] = tie;
+    }
+    __syncthreads();
+    share_hist<NT>(tv, x, round);
+    gt_before = tie_before = 0;
+    for (int sp = 0; sp < x.split; ++sp) {
+        gt_before += tv[2 * sp];
+        tie_before += tv[2 * sp + 1];
+    }
+}
+
 // Write out[0..k): the min(k, n) largest keys of the pair, their indices
 // ascending, then -1.  key[0..n): top words of the order keys (LDS or global
-// memory); fine: the kExpBins-bin count of their top 12 bits (LDS, may share
-// memory with sc); row0: the pair's first K row (bf16 rows of kHeadDim) and
-// qp: its first query head, for the low words.  Every thread of the
-// NT-thread workgroup calls this; it ends with a barrier after the last
-// write of `out`.  Requires 1 <= k and n <= MAXN.  B: keys per thread read
-// together (kKey32BatchLds or kKey32BatchMem); coarse: kExpBins / 16 words
-// of LDS apart from fine and sc.
+// memory); fine: the kExpBins-bin count of their top 12 bits over all n
+// keys (LDS, may share memory with sc); row0: the pair's first K row (bf16
+// rows of kHeadDim) and qp: its first query head, for the low words; sh:
+// the splits sharing the selection (key32_alone(n): none; this workgroup
+// then sweeps every key).  Every thread of the NT-thread workgroup calls
+// this; it ends with a barrier after the last write of `out`.  Requires
+// 1 <= k and n <= MAXN.  B: keys per thread read together (kKey32BatchLds
+// or kKey32BatchMem); coarse: kExpBins / 16 words of LDS apart from fine
+// and sc.
 template <int NT, int MAXN, int B>
 __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
                              const uint32_t *fine, uint32_t *coarse, Key32Scratch<NT, MAXN> &sc,
-                             const uint16_t *row0, const uint16_t *qp, int gqa) {
+                             const uint16_t *row0, const uint16_t *qp, int gqa,
+                             const Key32Share &sh) {
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int keff = min(k, n);
-    const int R = (n + NT - 1) / NT;
+    // this workgroup's keys and rounds (a round: NT consecutive keys)
+    const int lo = sh.lo, hi = sh.hi;
+    const int r_lo = lo / NT, R = (hi + NT - 1) / NT;
+    uint32_t round = 0;  // exchanges made with the other splits
 
     for (int i = keff + tid; i < k; i += NT) out[i] = -1;
     if (keff == n) {  // every key is kept
@@ -199,36 +306,37 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
     __syncthreads();
 
     // digits of the top word: bits 19..12, 11..4, then 3..0
-    int buf = 0, lo = 12, width = 8;
+    int buf = 0, lo_bit = 12, width = 8;
     while (!resolved) {
         uint32_t *h = sc.hist[buf];
         const int nbuf = buf == 2 ? 0 : buf + 1;
         const uint32_t dmask = (1u << width) - 1u;
-        key32_sweep<NT, B>(key, n, [&](int j0, const uint32_t (&x)[B]) {
+        key32_sweep<NT, B>(key, n, lo, hi, [&](int j0, const uint32_t (&x)[B]) {
 #pragma unroll
             for (int u = 0; u < B; ++u)
                 if (j0 + u * NT + tid < n && (x[u] & pmask) == prefix)
-                    atomicAdd(&h[(x[u] >> lo) & dmask], 1u);
+                    atomicAdd(&h[(x[u] >> lo_bit) & dmask], 1u);
         });
         for (int i = tid; i < 256; i += NT) sc.hist[nbuf][i] = 0u;
         __syncthreads();
+        share_hist<NT>(h, sh, round);
 #pragma unroll
         for (int r = 0; r < 4; ++r) c[r] = h[255 - 4 * lane - r];
         const BinHit hb = find_bin(c, krem, 255u, lane);
         buf = nbuf;
         krem -= hb.above;
-        prefix |= hb.digit << lo;
-        pmask |= dmask << lo;
+        prefix |= hb.digit << lo_bit;
+        pmask |= dmask << lo_bit;
         if (hb.in_bin == krem) {
             resolved = true;
             break;
         }
-        if (lo == 0) break;  // all 32 top bits used
-        if (lo >= 8) {
-            lo -= 8;
+        if (lo_bit == 0) break;  // all 32 top bits used
+        if (lo_bit >= 8) {
+            lo_bit -= 8;
         } else {
-            width = lo;
-            lo = 0;
+            width = lo_bit;
+            lo_bit = 0;
         }
     }
 
@@ -247,7 +355,7 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
         for (int llo = 24;; llo -= 8) {
             uint32_t *h = sc.hist[buf];
             const int nbuf = buf == 2 ? 0 : buf + 1;
-            key32_sweep<NT, B>(key, n, [&](int j0, const uint32_t (&x)[B]) {
+            key32_sweep<NT, B>(key, n, lo, hi, [&](int j0, const uint32_t (&x)[B]) {
 #pragma unroll
                 for (int u = 0; u < B; ++u) {
                     const int j = j0 + u * NT + tid;
@@ -260,6 +368,7 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
             });
             for (int i = tid; i < 256; i += NT) sc.hist[nbuf][i] = 0u;
             __syncthreads();
+            share_hist<NT>(h, sh, round);
 #pragma unroll
             for (int r = 0; r < 4; ++r) c[r] = h[255 - 4 * lane - r];
             const BinHit hb = find_bin(c, krem, 255u, lane);
@@ -275,13 +384,24 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
         }
     }
 
+    // Shared: this split has written its kept indices, out[p0, p0 + cnt)
+    // (its keys are consecutive in index order, so are their places); they
+    // go to the workspace list, and every split reads the whole list back.
+    auto gather = [&](uint32_t p0, uint32_t cnt) {
+        if (sh.ns == 1) return;
+        for (uint32_t i = p0 + tid; i < p0 + cnt; i += NT) st_ws(sh.list + i, out[i]);
+        share_arrive_wait(sh, ++round);
+        for (int i = tid; i < keff; i += NT) out[i] = ld_ws(sh.list + i);
+        __syncthreads();
+    };
+
     if (resolved) {
         // settled by the top words: kept = top word >= prefix (zeros below
         // its mask); no ties, no low words.  Lane u of a wave carries the
         // count (then the offset) of round j0 / NT + u of the batch, so a
         // round costs a compare, a ballot and a bit count.
         static_assert(B <= 64, "one lane per round of a batch");
-        key32_sweep<NT, B>(key, n, [&](int j0, const uint32_t (&x)[B]) {
+        key32_sweep<NT, B>(key, n, lo, hi, [&](int j0, const uint32_t (&x)[B]) {
             const int r0 = j0 / NT;
             const bool full = j0 + B * NT <= n;  // uniform: no bound checks
             uint32_t mine = 0;
@@ -297,8 +417,11 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
             }
         });
         __syncthreads();
-        block_exclusive_scan2<NT>(sc.cnt, sc.cnt_tie, R * NW, sc.wsum);
-        key32_sweep<NT, B>(key, n, [&](int j0, const uint32_t (&x)[B]) {
+        uint32_t tot, tot_tie, before, before_tie;
+        block_exclusive_scan2<NT>(sc.cnt + r_lo * NW, sc.cnt_tie + r_lo * NW, (R - r_lo) * NW,
+                                  sc.wsum, tot, tot_tie);
+        share_totals<NT>(sc.hist[buf], tot, 0u, sh, round, before, before_tie);
+        key32_sweep<NT, B>(key, n, lo, hi, [&](int j0, const uint32_t (&x)[B]) {
             const int r0 = j0 / NT;
             const bool full = j0 + B * NT <= n;
             const uint32_t base = lane < B && r0 + lane < R ? sc.cnt[(r0 + lane) * NW + wave] : 0u;
@@ -306,11 +429,12 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
             for (int u = 0; u < B; ++u) {
                 const int j = j0 + u * NT + tid;
                 const bool keep = (full || j < n) && x[u] >= prefix;
-                const uint32_t pos = lane_value(base, u) + rank_below(__ballot(keep));
+                const uint32_t pos = before + lane_value(base, u) + rank_below(__ballot(keep));
                 if (keep) out[pos] = j;
             }
         });
         __syncthreads();
+        gather(before, tot);
         return;
     }
 
@@ -325,7 +449,7 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
     };
 
     // ordered compaction: counts per (round, wave), a scan, then the writes
-    key32_sweep<NT, B>(key, n, [&](int j0, const uint32_t (&x)[B]) {
+    key32_sweep<NT, B>(key, n, lo, hi, [&](int j0, const uint32_t (&x)[B]) {
 #pragma unroll
         for (int u = 0; u < B; ++u) {
             const int r = j0 / NT + u;
@@ -340,8 +464,11 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
         }
     });
     __syncthreads();
-    block_exclusive_scan2<NT>(sc.cnt, sc.cnt_tie, R * NW, sc.wsum);
-    key32_sweep<NT, B>(key, n, [&](int j0, const uint32_t (&x)[B]) {
+    uint32_t tot, tot_tie, before, before_tie;
+    block_exclusive_scan2<NT>(sc.cnt + r_lo * NW, sc.cnt_tie + r_lo * NW, (R - r_lo) * NW, sc.wsum,
+                              tot, tot_tie);
+    share_totals<NT>(sc.hist[buf], tot, tot_tie, sh, round, before, before_tie);
+    key32_sweep<NT, B>(key, n, lo, hi, [&](int j0, const uint32_t (&x)[B]) {
 #pragma unroll
         for (int u = 0; u < B; ++u) {
             const int r = j0 / NT + u;
@@ -349,12 +476,15 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
             const int j = r * NT + tid;
             const int cl = j < n ? cls(j, x[u]) : 0;
             const uint64_t ma = __ballot(cl == 2), mt = __ballot(cl == 1);
-            const uint32_t gt_before = sc.cnt[r * NW + wave] + rank_below(ma);
-            const uint32_t tie_before = sc.cnt_tie[r * NW + wave] + rank_below(mt);
+            const uint32_t gt_before = before + sc.cnt[r * NW + wave] + rank_below(ma);
+            const uint32_t tie_before = before_tie + sc.cnt_tie[r * NW + wave] + rank_below(mt);
             if (cl == 2 || (cl == 1 && tie_before < krem)) out[gt_before + min(tie_before, krem)] = j;
         }
     });
     __syncthreads();
+    // this split's kept keys: its sure ones and its ties that are still kept
+    const uint32_t ties_kept = min(before_tie + tot_tie, krem) - min(before_tie, krem);
+    gather(before + min(before_tie, krem), tot + ties_kept);
 }
 
 }  // namespace kin

@@ -10,7 +10,10 @@
 //            those words, read from memory, low words recomputed from K
 //            only where they decide), then attention over those tokens' K/V
 //            (MFMA, online softmax), split over several workgroups when
-//            there are fewer pairs than CUs, the splits combined in-kernel.
+//            there are fewer pairs than CUs, the splits combined in-kernel;
+//            the splits of a pair share the selection's sweeps (each sweeps
+//            its own range of the keys, the counts summed through the
+//            workspace).
 //
 // With at least as many pairs as CUs, a context of at most 32768 tokens and
 // at most 2048 kept, the whole step runs in one kernel (k_tok_step), one
@@ -29,12 +32,20 @@
 namespace kin {
 
 constexpr int kTokScoreThreads = 512;
+// workspace words of the split form besides the pairs' combine words
+// [0, pairs): the pairs' selection exchange counts, and the start-order
+// ticket of kernel 2's workgroups
+constexpr int kTokShareWords = kCtrlWords / 2;
+constexpr int kTokTicketWord = kCtrlWords - 1;
+// keys one split of a shared selection sweeps: whole batches
+constexpr int kTokShareSeg = kKey32BatchMem * kStepThreads;
 
 // Kernel 1: the group score of every key of one tile of a pair's tokens;
 // the top word of its order key written to `keys` ([pair][t_cap]), the
 // score itself to `scores` when asked for, and the tile's sign/exponent
 // counts written to `tables` ([pair][tile][kExpBins]).  Also clears the
-// pair's arrival word for kernel 2's combine.
+// pair's words for kernel 2 (its combine and selection-exchange counts, and
+// the ticket word).
 __global__ __launch_bounds__(kTokScoreThreads) void k_tok_score(AttnArgs a, uint32_t *keys,
                                                                double *scores, int tile_rows,
                                                                uint32_t *tables,
@@ -43,7 +54,11 @@ __global__ __launch_bounds__(kTokScoreThreads) void k_tok_score(AttnArgs a, uint
     __shared__ NewestLds<NW> nl;  // not used: no summary to rebuild
     __shared__ uint32_t fine[4096];
     const int pair = blockIdx.y, tile = blockIdx.x;
-    if (ctrl_zero && tile == 0 && threadIdx.x == 0) ctrl_zero[pair] = 0ull;
+    if (ctrl_zero && tile == 0 && threadIdx.x == 0) {
+        ctrl_zero[pair] = 0ull;
+        ctrl_zero[kTokShareWords + pair] = 0ull;
+        if (pair == 0) ctrl_zero[kTokTicketWord] = 0ull;
+    }
     for (int i = threadIdx.x; i < 4096; i += kTokScoreThreads) fine[i] = 0u;
     __syncthreads();
     const int j_beg = tile * tile_rows;
@@ -76,17 +91,43 @@ struct TokLds {
     } u;
 };
 
+// The workspace areas of the shared selection (null with one split per
+// pair): per pair [2][nsplit][256] exchanged counts and [k] kept indices.
+struct TokShare {
+    uint32_t *hist;
+    int32_t *list;
+};
+
 __global__ __launch_bounds__(kStepThreads) void k_tok_select_attend(AttnArgs a,
                                                                    const uint32_t *__restrict__ keys,
                                                                    int32_t *idx_out,
                                                                    uint64_t *ctrl,
                                                                    const uint32_t *tables,
-                                                                   int ntables) {
+                                                                   int ntables, TokShare ts) {
     constexpr int NW = kStepThreads / 64;
     __shared__ TokLds<kStepThreads> lds;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int pair, split;
-    split_slot(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, gridDim.y, pair, split);
+    if (a.nsplit > 1) {
+        // the splits of a pair wait for one another during the selection,
+        // so they are numbered in start order (a ticket drawn as each
+        // workgroup starts): when a split waits, its pair's other splits
+        // hold tickets just below or above its own and have started, or
+        // start as soon as the workgroups ahead of them (which wait for
+        // nothing unstarted) end
+        __shared__ uint32_t ticket;
+        if (threadIdx.x == 0) {
+            const uint32_t t = (uint32_t)__hip_atomic_fetch_add(
+                ctrl + kTokTicketWord, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (t == gridDim.x * gridDim.y - 1) st_agent(ctrl + kTokTicketWord, (uint64_t)0);
+            ticket = t;
+        }
+        __syncthreads();
+        pair = (int)ticket / a.nsplit;
+        split = (int)ticket % a.nsplit;
+    } else {
+        split_slot(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, gridDim.y, pair, split);
+    }
 
     // the pair's counts: its tiles' tables summed (one table's bins of this
     // thread loaded together)
@@ -108,9 +149,23 @@ __global__ __launch_bounds__(kStepThreads) void k_tok_select_attend(AttnArgs a,
     const uint16_t *row0 = static_cast<const uint16_t *>(a.K) + (size_t)pair * a.t_cap * kHeadDim;
     const uint16_t *qp = static_cast<const uint16_t *>(a.q) +
                          ((size_t)b * a.hkv * a.gqa + (size_t)g * a.gqa) * kHeadDim;
+    Key32Share sh = key32_alone(a.ctx_len);
+    if (a.nsplit > 1) {
+        // split s sweeps keys [s q, (s + 1) q), q whole batches
+        const int q = ((a.ctx_len + a.nsplit - 1) / a.nsplit + kTokShareSeg - 1) / kTokShareSeg *
+                      kTokShareSeg;
+        sh.ns = a.nsplit;
+        sh.split = split;
+        sh.lo = min(split * q, a.ctx_len);
+        sh.hi = min(sh.lo + q, a.ctx_len);
+        sh.hist = ts.hist + (size_t)pair * 2 * a.nsplit * 256;
+        sh.list = ts.list + (size_t)pair * a.k;
+        sh.word = ctrl + kTokShareWords + pair;
+    }
     select_key32<kStepThreads, kTokMaxLen, kKey32BatchMem>(keys + (size_t)pair * a.t_cap,
                                                            a.ctx_len, a.k, lds.sel, lds.u.fine,
-                                                           lds.coarse, lds.u.s, row0, qp, a.gqa);
+                                                           lds.coarse, lds.u.s, row0, qp, a.gqa,
+                                                           sh);
     if (split == 0)
         for (int i = threadIdx.x; i < a.k; i += kStepThreads)
             idx_out[(size_t)pair * a.k + i] = lds.sel[i];
@@ -130,11 +185,15 @@ __global__ __launch_bounds__(kStepThreads) void k_tok_select_attend(AttnArgs a,
     stores_complete();
     __shared__ uint32_t last;
     __syncthreads();
-    // the arrival words were cleared by kernel 1; the last arrival leaves its
-    // word at zero again, as every call on a workspace does
+    // the arrival words were cleared by kernel 1; the last arrival (every
+    // split is past its selection's exchanges) leaves the pair's words at
+    // zero again, as every call on a workspace does
     if (threadIdx.x == 0) {
         last = arrive_add(ctrl + pair) == (uint32_t)a.nsplit;
-        if (last) st_agent(ctrl + pair, (uint64_t)0);
+        if (last) {
+            st_agent(ctrl + pair, (uint64_t)0);
+            st_agent(ctrl + kTokShareWords + pair, (uint64_t)0);
+        }
     }
     __syncthreads();
     if (last) combine_pair<KIN_BF16, kStepThreads>(a, pair);
@@ -182,7 +241,8 @@ __global__ __launch_bounds__(kStepThreads) void k_tok_step(AttnArgs a, double *s
     const uint16_t *qp = static_cast<const uint16_t *>(a.q) +
                          ((size_t)b * a.hkv * a.gqa + (size_t)g * a.gqa) * kHeadDim;
     select_key32<kStepThreads, kTokStepMaxLen, kKey32BatchLds>(u.key, L, a.k, sel, v.fine, coarse,
-                                                               v.s, row0, qp, a.gqa);
+                                                               v.s, row0, qp, a.gqa,
+                                                               key32_alone(L));
     for (int i = threadIdx.x; i < a.k; i += kStepThreads) idx_out[(size_t)pair * a.k + i] = sel[i];
     // the keys are dead: the merge area overlays them
     const TokenRuns runs{(int64_t)pair * a.t_cap, sel, a.k, L};
@@ -217,16 +277,20 @@ static void tok_tiles(const Geo &g, int num_cu, int &tiles, int &rows) {
 }
 
 // Workspace of the two-kernel token step after its arrival words: split
-// partials, the keys' top words, count tables (in that order, each 256-byte
-// aligned; offsets from ws_body).
+// partials, the keys' top words, count tables, and with several splits per
+// pair the shared selection's exchanged counts and kept list (in that
+// order, each 256-byte aligned; offsets from ws_body).
 struct TokWs {
-    size_t keys, tables, total;
+    size_t keys, tables, hist, list, total;
 };
-static TokWs tok_ws(const Geo &g, int nsplit, int tiles) {
+static TokWs tok_ws(const Geo &g, int nsplit, int tiles, int k) {
     TokWs w;
     w.keys = align256(ws_for(g, nsplit));
     w.tables = align256(w.keys + (size_t)g.pairs * g.t_cap * sizeof(uint32_t));
-    w.total = w.tables + (size_t)g.pairs * tiles * kExpBins * sizeof(uint32_t);
+    w.hist = align256(w.tables + (size_t)g.pairs * tiles * kExpBins * sizeof(uint32_t));
+    const size_t np = nsplit > 1 ? (size_t)g.pairs * 2 * nsplit : 0;
+    w.list = align256(w.hist + np * 256 * sizeof(uint32_t));
+    w.total = w.list + (nsplit > 1 ? (size_t)g.pairs * k * sizeof(int32_t) : 0);
     return w;
 }
 
@@ -240,13 +304,13 @@ AttnPlan plan_tok(const Geo &g, int k, int num_cu) {
     const int max_ns = p.n_chunks / 8;
     if (ns > max_ns) ns = max_ns;
     if (ns > 64) ns = 64;
-    // one arrival word per pair for the in-kernel combine
-    if (ns < 1 || g.pairs > kCtrlWords) ns = 1;
+    // an arrival word and a selection-exchange word per pair
+    if (ns < 1 || g.pairs >= kTokShareWords) ns = 1;
     p.nsplit = ns;
     p.fused = 1;
     int tiles, rows;
     tok_tiles(g, num_cu, tiles, rows);
-    p.ws_bytes = ws_total(tok_ws(g, ns, tiles).total);
+    p.ws_bytes = ws_total(tok_ws(g, ns, tiles, k).total);
     return p;
 }
 
@@ -268,7 +332,7 @@ hipError_t launch_tok_step(const Geo &g0, const void *q, const void *K, const vo
     const AttnPlan p = plan_tok(g, k, num_cu);
     int tiles, rows;
     tok_tiles(g, num_cu, tiles, rows);
-    const TokWs wl = tok_ws(g, p.nsplit, tiles);
+    const TokWs wl = tok_ws(g, p.nsplit, tiles, k);
     char *w = ws_body(ws);
     // the arrival words: the start of the workspace (cleared by kernel 1)
     uint64_t *ctrl = p.nsplit > 1 ? static_cast<uint64_t *>(ws) : nullptr;
@@ -281,8 +345,13 @@ hipError_t launch_tok_step(const Geo &g0, const void *q, const void *K, const vo
                                                                   ctrl);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    TokShare ts{nullptr, nullptr};
+    if (p.nsplit > 1) {
+        ts.hist = reinterpret_cast<uint32_t *>(w + wl.hist);
+        ts.list = reinterpret_cast<int32_t *>(w + wl.list);
+    }
     const dim3 grid(p.nsplit, g.pairs);
-    k_tok_select_attend<<<grid, kStepThreads, 0, s>>>(a, keys, idx, ctrl, tables, tiles);
+    k_tok_select_attend<<<grid, kStepThreads, 0, s>>>(a, keys, idx, ctrl, tables, tiles, ts);
     return hipGetLastError();
 }
 
