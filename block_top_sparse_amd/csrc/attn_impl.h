@@ -539,9 +539,12 @@ __device__ __forceinline__ void compute_chunk(const ChunkRegs &cr, const bf16x8 
 // One wave's share of a pair's chunks [c_beg, c_end), every `step`-th chunk
 // starting at c_beg + first, then its (m, l, o) into merge slot `slot`.
 // `runs` maps list positions to cache rows (DenseRuns, ListRuns, PagedRuns).
-template <class Runs, int NW>
+// PRE: when use_pre, the wave's first chunk is already loaded into pre (its
+// loads may still be in flight).
+template <class Runs, int NW, bool PRE = false>
 __device__ void attend_bf16(const AttnArgs &a, const Runs &runs, int pair, int c_beg,
-                            int c_end, int first, int step, int slot, MergeLds<NW> &sm) {
+                            int c_end, int first, int step, int slot, MergeLds<NW> &sm,
+                            const ChunkRegs *pre = nullptr, bool use_pre = false) {
     const int lane = threadIdx.x & 63;
     const int j = lane & 15, g4 = lane >> 4;
     const int b = pair / a.hkv, gk = pair % a.hkv;
@@ -575,7 +578,10 @@ __device__ void attend_bf16(const AttnArgs &a, const Runs &runs, int pair, int c
     const int n = c0 < c_end ? (c_end - c0 + step - 1) / step : 0;
     ChunkRegs ra, rb;
     if (n > 0) {
-        load_chunk(a, runs, Kp, Vp, c0, j, g4, ra);
+        if (PRE && use_pre)
+            ra = *pre;
+        else
+            load_chunk(a, runs, Kp, Vp, c0, j, g4, ra);
         int i = 0;
         for (; i + 2 < n; i += 2) {
             load_chunk(a, runs, Kp, Vp, c0 + (i + 1) * step, j, g4, rb);

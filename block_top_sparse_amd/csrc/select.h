@@ -185,15 +185,26 @@ __device__ __forceinline__ BinHit find_bin(const uint32_t (&c)[4], uint32_t krem
     return BinHit{lane_value(dsel, src), lane_value(above, src), lane_value(in_bin, src)};
 }
 
+// The selection's hook once the sign/exponent bin of the k-th key is known
+// from the count tables: early(key, bin), called by every thread with its
+// keys (block e * NT + threadIdx.x in key[e]; 0 past nb) and the bin (top
+// 12 bits of the k-th key); keys in higher bins are certainly kept.  This
+// one does nothing.
+struct NoEarly {
+    template <int KPT>
+    __device__ void operator()(const uint64_t (&)[KPT], uint32_t) const {}
+};
+
 // Write out[0..k): the min(k, nb) selected block indices ascending, then -1.
 // sc: the pair's scores (nb entries; global memory or LDS).  Every thread of
 // the workgroup calls this, after select_clear and a barrier; with COUNTED
 // the caller has also passed every score to select_count (and synchronised
-// since).  It ends without a barrier, so callers synchronise before other
-// waves read `out`.  Requires 1 <= k and nb <= KPT * NT.
-template <int KPT, int NT, bool COUNTED>
+// since), and early (see NoEarly) runs between the count tables and the
+// mantissa passes.  It ends without a barrier, so callers synchronise before
+// other waves read `out`.  Requires 1 <= k and nb <= KPT * NT.
+template <int KPT, int NT, bool COUNTED, class Early = NoEarly>
 __device__ void select_topk(const double *__restrict__ sc, int nb, int k, int32_t *out,
-                            SelectLds<KPT, NT> &lds) {
+                            SelectLds<KPT, NT> &lds, Early early = Early()) {
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -311,6 +322,7 @@ __device__ void select_topk(const double *__restrict__ sc, int nb, int k, int32_
         krem -= h2.above;
         prefix = (uint64_t)h2.digit << 52;
         in_bin = h2.in_bin;
+        if (COUNTED) early(key, h2.digit);
     }
     bool resolved = in_bin == krem;  // true: every key matching `prefix` is kept
 

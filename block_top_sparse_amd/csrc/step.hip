@@ -11,7 +11,13 @@
 //   3. the workgroup selects the top k blocks from LDS (select.h; the
 //      exponent count tables are filled while the scores are made);
 //   4. the waves attend over the kept blocks' K/V (MFMA, online softmax)
-//      and merge into the output.
+//      and merge into the output.  The 8-wave form walks a few blocks
+//      already certain to be kept first (their sign/exponent bin lies above
+//      the k-th key's, known from the count tables before the mantissa
+//      passes) and the rest of the kept list after them, and with a
+//      contiguous cache each wave loads its first chunk from those blocks
+//      while step 3 still runs (the idx output stays the ascending list; the
+//      order depends only on the scores, so every cache mode sums alike).
 //
 // The steps follow the method of BlockTopKAttention (skill summary
 // "Kinetics: Memory-Aware Test-Time Scaling", Implementation) with KV
@@ -76,6 +82,14 @@ __global__ __launch_bounds__(NW * 64, NW == kStepSmallWaves ? 2 : 1) void k_deco
         double sc[MAXNB];
         MergeLds<NW> m;
     } u;
+    // the 8-wave form's block order: the attention's list, the blocks put
+    // first (a bit per block), per-wave counts; kPre: their first chunks
+    // are loaded during the selection (contiguous caches)
+    constexpr bool kOrder = NW == 8;
+    constexpr bool kPre = kOrder && MODE == kContig;
+    __shared__ int32_t att[kOrder ? kStepIdxCap : 1];
+    __shared__ uint32_t picked[kOrder ? kStepMaxBlocks / 32 : 1];
+    __shared__ uint32_t pcnt[kOrder ? (kStepIdxCap / NT) * NW : 1];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -104,26 +118,105 @@ __global__ __launch_bounds__(NW * 64, NW == kStepSmallWaves ? 2 : 1) void k_deco
     __syncthreads();
 
     // 3. selection (reads the scores from LDS; they are dead afterwards, so
-    //    the merge area may reuse them)
-    select_topk<KPT, NT, true>(u.sc, nb, a.k, sel, sl);
+    //    the merge area may reuse them).  kOrder: once the k-th key's bin is
+    //    known, P blocks above it (P blocks hold the NW waves' first chunks)
+    //    go to att[0, P); kPre: every wave starts loading its first chunk.
+    const int lane = tid & 63;
+    ChunkRegs pre;
+    bool use_pre = false;  // att holds the order (uniform)
+    int n_pre = 0;
+    auto early = [&](const uint64_t (&key)[KPT], uint32_t bin) {
+        if constexpr (kOrder) {
+            bool cert[KPT];
+            uint32_t mine = 0;
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                cert[e] = (e * NT + tid < nb) && (uint32_t)(key[e] >> 52) > bin;
+                mine += (uint32_t)__popcll(__ballot(cert[e]));
+            }
+            if (lane == 0) pcnt[wave] = mine;
+            for (int i = tid; i < (nb + 31) / 32; i += NT) picked[i] = 0u;
+            __syncthreads();
+            uint32_t total = 0, run = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const uint32_t c = pcnt[w];
+                total += c;
+                run += w < wave ? c : 0u;
+            }
+            const int P = (NW * kChunkBf16 + a.block - 1) >> a.block_shift;
+            if (total >= (uint32_t)P) {  // uniform
+#pragma unroll
+                for (int e = 0; e < KPT; ++e) {
+                    const uint64_t m = __ballot(cert[e]);
+                    const uint32_t r = run + rank_below(m);
+                    const int j = e * NT + tid;
+                    if (cert[e] && r < (uint32_t)P) {
+                        att[r] = j;
+                        atomicOr(&picked[j >> 5], 1u << (j & 31));
+                    }
+                    run += (uint32_t)__popcll(m);
+                }
+                __syncthreads();
+                if constexpr (kPre) {
+                    const ListRuns head{(int64_t)pair * a.t_cap, att, P, nb, a.block,
+                                        a.block_shift};
+                    load_chunk(a, head, static_cast<const uint16_t *>(a.K),
+                               static_cast<const uint16_t *>(a.V), wave, lane & 15, lane >> 4,
+                               pre);
+                }
+                use_pre = true;
+                n_pre = P;
+            }
+        }
+    };
+    select_topk<KPT, NT, true>(u.sc, nb, a.k, sel, sl, early);
     __syncthreads();
     for (int i = tid; i < a.k; i += NT) x.idx[(size_t)pair * a.k + i] = sel[i];
+    if constexpr (kOrder) {
+        if (use_pre) {  // uniform
+            // att[P, keff): the kept blocks not loaded early, ascending (an
+            // ordered compaction of sel)
+            const int keff = min(a.k, nb);
+            for (int i0 = 0; i0 < keff; i0 += NT) {
+                const int id = i0 + tid < keff ? sel[i0 + tid] : -1;
+                const bool rest = id >= 0 && !((picked[id >> 5] >> (id & 31)) & 1u);
+                const uint64_t m = __ballot(rest);
+                if (lane == 0) pcnt[(i0 / NT) * NW + wave] = (uint32_t)__popcll(m);
+            }
+            __syncthreads();
+            for (int i0 = 0; i0 < keff; i0 += NT) {
+                const int r0 = i0 / NT;
+                uint32_t off = (uint32_t)n_pre;
+                for (int q = 0; q < r0 * NW + wave; ++q) off += pcnt[q];
+                const int id = i0 + tid < keff ? sel[i0 + tid] : -1;
+                const bool rest = id >= 0 && !((picked[id >> 5] >> (id & 31)) & 1u);
+                const uint64_t m = __ballot(rest);
+                if (rest) att[off + rank_below(m)] = id;
+            }
+            __syncthreads();
+        }
+    }
+    const int32_t *order = use_pre ? att : sel;  // the attention's block list
 
     // 4. attention over the kept blocks, then the merge of the 8 waves
     if constexpr (MODE == kPaged) {
         // first row of every kept block (a block lies inside one page); the
         // select's LDS is dead now
         for (int i = tid; i < a.k; i += NT) {
-            const int id = sel[i];
+            const int id = order[i];
             su.selrow[i] = id >= 0 && id < nb ? token_row(a, pair, id * a.block) : -1;
         }
         __syncthreads();
-        const PagedRuns runs{sel, su.selrow, token_row(a, pair, 0), a.k, nb, a.block,
+        const PagedRuns runs{order, su.selrow, token_row(a, pair, 0), a.k, nb, a.block,
                              a.block_shift};
         attend_bf16<PagedRuns, NW>(a, runs, pair, 0, a.n_chunks, wave, NW, wave, u.m);
     } else if constexpr (MODE == kShared) {
-        attend_bf16<SharedRuns, NW>(a, shared_runs(a, pair, sel), pair, 0, a.n_chunks, wave, NW,
-                                    wave, u.m);
+        attend_bf16<SharedRuns, NW>(a, shared_runs(a, pair, order), pair, 0, a.n_chunks, wave,
+                                    NW, wave, u.m);
+    } else if constexpr (kPre) {
+        attend_bf16<ListRuns, NW, true>(a, list_runs(a, pair, order), pair, 0, a.n_chunks, wave,
+                                        NW, wave, u.m, &pre, use_pre);
     } else {
         attend_bf16<ListRuns, NW>(a, list_runs(a, pair, sel), pair, 0, a.n_chunks, wave, NW,
                                   wave, u.m);
