@@ -11,7 +11,7 @@
 //   3. the workgroup selects the top k blocks from LDS (select.h; the
 //      exponent count tables are filled while the scores are made);
 //   4. the waves attend over the kept blocks' K/V (MFMA, online softmax)
-//      and merge into the output.  The 8-wave form walks a few blocks
+//      and merge into the output.  The attention walks a few blocks
 //      already certain to be kept first (their sign/exponent bin lies above
 //      the k-th key's, known from the count tables before the mantissa
 //      passes) and the rest of the kept list after them, and with a
@@ -82,14 +82,24 @@ __global__ __launch_bounds__(NW * 64, NW == kStepSmallWaves ? 2 : 1) void k_deco
         double sc[MAXNB];
         MergeLds<NW> m;
     } u;
-    // the 8-wave form's block order: the attention's list, the blocks put
-    // first (a bit per block), per-wave counts; kPre: their first chunks
-    // are loaded during the selection (contiguous caches)
-    constexpr bool kOrder = NW == 8;
-    constexpr bool kPre = kOrder && MODE == kContig;
-    __shared__ int32_t att[kOrder ? kStepIdxCap : 1];
-    __shared__ uint32_t picked[kOrder ? kStepMaxBlocks / 32 : 1];
-    __shared__ uint32_t pcnt[kOrder ? (kStepIdxCap / NT) * NW : 1];
+    // After the scoring, the newest-row rebuild's LDS holds the attention's
+    // block order: the list, the blocks put first (a bit per block) and
+    // per-wave counts.  kPre: their first chunks are loaded during the
+    // selection (contiguous caches).
+    constexpr bool kPre = MODE == kContig;
+    struct OrderLds {
+        int32_t att[kStepIdxCap];
+        uint32_t picked[MAXNB / 32];
+        uint32_t pcnt[(kStepIdxCap / NT) * NW];
+    };
+    __shared__ union {
+        NewestLds<NW> nl;
+        OrderLds o;
+    } nu;
+    NewestLds<NW> &nl = nu.nl;
+    int32_t *att = nu.o.att;
+    uint32_t *picked = nu.o.picked;
+    uint32_t *pcnt = nu.o.pcnt;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -100,7 +110,6 @@ __global__ __launch_bounds__(NW * 64, NW == kStepSmallWaves ? 2 : 1) void k_deco
 
     // 1+2. score every block (wave 0 rebuilds the newest block's summary
     // first); the scores go to LDS and into the select's exponent tables
-    __shared__ NewestLds<NW> nl;
     select_clear(sl);
     if (tid == 0) nl.ready = 0u;
     __syncthreads();
@@ -118,7 +127,7 @@ __global__ __launch_bounds__(NW * 64, NW == kStepSmallWaves ? 2 : 1) void k_deco
     __syncthreads();
 
     // 3. selection (reads the scores from LDS; they are dead afterwards, so
-    //    the merge area may reuse them).  kOrder: once the k-th key's bin is
+    //    the merge area may reuse them).  Once the k-th key's bin is
     //    known, P blocks above it (P blocks hold the NW waves' first chunks)
     //    go to att[0, P); kPre: every wave starts loading its first chunk.
     const int lane = tid & 63;
@@ -126,7 +135,7 @@ __global__ __launch_bounds__(NW * 64, NW == kStepSmallWaves ? 2 : 1) void k_deco
     bool use_pre = false;  // att holds the order (uniform)
     int n_pre = 0;
     auto early = [&](const uint64_t (&key)[KPT], uint32_t bin) {
-        if constexpr (kOrder) {
+        {
             bool cert[KPT];
             uint32_t mine = 0;
 #pragma unroll
@@ -173,7 +182,7 @@ __global__ __launch_bounds__(NW * 64, NW == kStepSmallWaves ? 2 : 1) void k_deco
     select_topk<KPT, NT, true>(u.sc, nb, a.k, sel, sl, early);
     __syncthreads();
     for (int i = tid; i < a.k; i += NT) x.idx[(size_t)pair * a.k + i] = sel[i];
-    if constexpr (kOrder) {
+    {
         if (use_pre) {  // uniform
             // att[P, keff): the kept blocks not loaded early, ascending (an
             // ordered compaction of sel)
