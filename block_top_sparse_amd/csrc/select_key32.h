@@ -85,6 +85,13 @@ __device__ __noinline__ double exact_score_row(const uint16_t *row, const double
     return v;
 }
 
+// exact_score_row of the pair's token map[j] (row0: the pair's first K row;
+// map: a candidate list in memory).
+__device__ __noinline__ double exact_score_mapped(const uint16_t *row0, const int32_t *map, int j,
+                                                  const double *qsum) {
+    return exact_score_row(row0 + (size_t)map[j] * kHeadDim, qsum);
+}
+
 // Exclusive prefix sums, in place, of a[0..n) and b[0..n) over the whole
 // workgroup (each thread scans a contiguous segment); ta, tb: the totals.
 // Ends with a barrier.
@@ -259,28 +266,43 @@ __device__ __forceinline__ void share_totals(uint32_t *tv, uint32_t gt, uint32_t
 // keys (LDS, may share memory with sc); row0: the pair's first K row (bf16
 // rows of kHeadDim) and qp: its first query head, for the low words; sh:
 // the splits sharing the selection (key32_alone(n): none; this workgroup
-// then sweeps every key).  Every thread of the NT-thread workgroup calls
-// this; it ends with a barrier after the last write of `out`.  Requires
-// 1 <= k and n <= MAXN.  B: keys per thread read together (kKey32BatchLds
-// or kKey32BatchMem); coarse: kExpBins / 16 words of LDS apart from fine
-// and sc.
+// then sweeps every key).  Key j is token tok0 + j of the pair, or, when
+// mapped, token map[j] (a candidate list; out then receives the kept keys'
+// places j, which the caller turns into token numbers); out_key, if given,
+// receives each kept key's top word (0 past keff).  Every thread
+// of the NT-thread workgroup calls this; it ends with a barrier after the
+// last write of `out`.  Requires 1 <= k and n <= MAXN.  B: keys per thread
+// read together (kKey32BatchLds or kKey32BatchMem); coarse: kExpBins / 16
+// words of LDS apart from fine and sc.
 template <int NT, int MAXN, int B>
 __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
                              const uint32_t *fine, uint32_t *coarse, Key32Scratch<NT, MAXN> &sc,
                              const uint16_t *row0, const uint16_t *qp, int gqa,
-                             const Key32Share &sh) {
+                             const Key32Share &sh, int tok0 = 0, bool mapped = false,
+                             const int32_t *map = nullptr, uint32_t *out_key = nullptr) {
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int keff = min(k, n);
+    // the exact fp64 score of key j (its K row, through the map if mapped)
+    auto exact = [&](int j) -> double {
+        return mapped ? exact_score_mapped(row0, map, j, sc.qsum)
+                      : exact_score_row(row0 + (size_t)(tok0 + j) * kHeadDim, sc.qsum);
+    };
     // this workgroup's keys and rounds (a round: NT consecutive keys)
     const int lo = sh.lo, hi = sh.hi;
     const int r_lo = lo / NT, R = (hi + NT - 1) / NT;
     uint32_t round = 0;  // exchanges made with the other splits
 
-    for (int i = keff + tid; i < k; i += NT) out[i] = -1;
+    for (int i = keff + tid; i < k; i += NT) {
+        out[i] = -1;
+        if (out_key) out_key[i] = 0u;
+    }
     if (keff == n) {  // every key is kept
-        for (int i = tid; i < n; i += NT) out[i] = i;
+        for (int i = tid; i < n; i += NT) {
+            out[i] = tok0 + i;
+            if (out_key) out_key[i] = key[i];
+        }
         __syncthreads();
         return;
     }
@@ -361,7 +383,7 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
                     const int j = j0 + u * NT + tid;
                     if (j < n && x[u] == prefix) {
                         const uint32_t w = (uint32_t)order_key(
-                            exact_score_row(row0 + (size_t)j * kHeadDim, sc.qsum));
+                            exact(j));
                         if ((w & lmask) == lprefix) atomicAdd(&h[(w >> llo) & 255u], 1u);
                     }
                 }
@@ -430,7 +452,10 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
                 const int j = j0 + u * NT + tid;
                 const bool keep = (full || j < n) && x[u] >= prefix;
                 const uint32_t pos = before + lane_value(base, u) + rank_below(__ballot(keep));
-                if (keep) out[pos] = j;
+                if (keep) {
+                    out[pos] = tok0 + j;
+                    if (out_key) out_key[pos] = x[u];
+                }
             }
         });
         __syncthreads();
@@ -443,7 +468,7 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
     auto cls = [&](int j, uint32_t x) -> int {
         if (x != prefix) return x > prefix ? 2 : 0;
         const uint32_t w =
-            (uint32_t)order_key(exact_score_row(row0 + (size_t)j * kHeadDim, sc.qsum));
+            (uint32_t)order_key(exact(j));
         if (lresolved) return w >= lprefix ? 2 : 0;
         return w > lprefix ? 2 : (w == lprefix ? 1 : 0);
     };
@@ -478,7 +503,11 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
             const uint64_t ma = __ballot(cl == 2), mt = __ballot(cl == 1);
             const uint32_t gt_before = before + sc.cnt[r * NW + wave] + rank_below(ma);
             const uint32_t tie_before = before_tie + sc.cnt_tie[r * NW + wave] + rank_below(mt);
-            if (cl == 2 || (cl == 1 && tie_before < krem)) out[gt_before + min(tie_before, krem)] = j;
+            if (cl == 2 || (cl == 1 && tie_before < krem)) {
+                const uint32_t pos = gt_before + min(tie_before, krem);
+                out[pos] = tok0 + j;
+                if (out_key) out_key[pos] = x[u];
+            }
         }
     });
     __syncthreads();

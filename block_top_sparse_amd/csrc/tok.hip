@@ -39,19 +39,35 @@ constexpr int kTokShareWords = kCtrlWords / 2;
 constexpr int kTokTicketWord = kCtrlWords - 1;
 // keys one split of a shared selection sweeps: whole batches
 constexpr int kTokShareSeg = kKey32BatchMem * kStepThreads;
+// rows of a score tile whose top words fit in LDS for its own selection
+constexpr int kTokLocalRows = 32768;
 
-// Kernel 1: the group score of every key of one tile of a pair's tokens;
-// the top word of its order key written to `keys` ([pair][t_cap]), the
-// score itself to `scores` when asked for, and the tile's sign/exponent
-// counts written to `tables` ([pair][tile][kExpBins]).  Also clears the
+// Kernel 1: the group score of every key of one tile of a pair's tokens,
+// the score itself written to `scores` when asked for.  The top word of
+// each score's order key is written to `keys` ([pair][t_cap]) and the
+// tile's sign/exponent counts to `tables` ([pair][tile][kExpBins]), or,
+// LOCAL, the top words stay in LDS and the tile selects its own top k
+// (ties to the lower index): every token of the pair's top k is among its
+// tile's top k, since fewer than k tokens of the pair, hence of the tile,
+// come before it.  The tile's candidates (token numbers ascending, -1 past
+// the tile's length) go to cand_idx ([pair][tile][k]), their top words to
+// `keys` (same places, 0 past), their counts to `tables`.  Also clears the
 // pair's words for kernel 2 (its combine and selection-exchange counts, and
 // the ticket word).
+template <bool LOCAL>
 __global__ __launch_bounds__(kTokScoreThreads) void k_tok_score(AttnArgs a, uint32_t *keys,
                                                                double *scores, int tile_rows,
                                                                uint32_t *tables,
-                                                               uint64_t *ctrl_zero) {
+                                                               uint64_t *ctrl_zero,
+                                                               int32_t *cand_idx) {
     constexpr int NW = kTokScoreThreads / 64;
-    __shared__ NewestLds<NW> nl;  // not used: no summary to rebuild
+    // no summary to rebuild: the rebuild's LDS (never used) holds the
+    // tile's top words when LOCAL
+    __shared__ union {
+        NewestLds<NW> nl;
+        uint32_t key[LOCAL ? kTokLocalRows : 1];
+    } u;
+    NewestLds<NW> &nl = u.nl;
     __shared__ uint32_t fine[4096];
     const int pair = blockIdx.y, tile = blockIdx.x;
     if (ctrl_zero && tile == 0 && threadIdx.x == 0) {
@@ -71,11 +87,39 @@ __global__ __launch_bounds__(kTokScoreThreads) void k_tok_score(AttnArgs a, uint
         score_blocks<NW, false>(a, const_cast<void *>(a.K), a.t_cap, pair, j_beg, j_end, nl,
                                 [&](int j, double v) {
             const uint32_t top = (uint32_t)(order_key(v) >> 32);
-            kp[j] = top;
+            if (LOCAL)
+                u.key[j - j_beg] = top;
+            else
+                kp[j] = top;
             count_wave_aggregated(fine, top >> 20, true);
             if (sp) sp[j] = v;  // scores are an optional output
         });
     __syncthreads();
+    if constexpr (LOCAL) {
+        __shared__ uint32_t coarse[kExpBins / 16];
+        __shared__ Key32Scratch<kTokScoreThreads, kTokLocalRows> sc;
+        const int n_t = max(0, j_end - j_beg);
+        const size_t c0 = ((size_t)pair * gridDim.x + tile) * a.k;
+        const int b = pair / a.hkv, g = pair % a.hkv;
+        const uint16_t *row0 =
+            static_cast<const uint16_t *>(a.K) + (size_t)pair * a.t_cap * kHeadDim;
+        const uint16_t *qp = static_cast<const uint16_t *>(a.q) +
+                             ((size_t)b * a.hkv * a.gqa + (size_t)g * a.gqa) * kHeadDim;
+        select_key32<kTokScoreThreads, kTokLocalRows, kKey32BatchLds>(
+            u.key, n_t, a.k, cand_idx + c0, fine, coarse, sc, row0, qp, a.gqa, key32_alone(n_t),
+            j_beg, false, nullptr, keys + c0);
+        // the candidates' sign/exponent counts (the block's own stores,
+        // visible to it after the selection's final barrier)
+        for (int i = threadIdx.x; i < kExpBins; i += kTokScoreThreads) fine[i] = 0u;
+        __syncthreads();
+        const int kt = min(a.k, n_t);
+        for (int i0 = 0; i0 < kt; i0 += kTokScoreThreads) {
+            const int i = i0 + (int)threadIdx.x;
+            const bool on = i < kt;
+            count_wave_aggregated(fine, (on ? keys[c0 + i] : 0u) >> 20, on);
+        }
+        __syncthreads();
+    }
     uint32_t *t = tables + ((size_t)pair * gridDim.x + tile) * kExpBins;
     for (int i = threadIdx.x; i < kExpBins; i += kTokScoreThreads) t[i] = fine[i];
 }
@@ -92,10 +136,13 @@ struct TokLds {
 };
 
 // The workspace areas of the shared selection (null with one split per
-// pair): per pair [2][nsplit][256] exchanged counts and [k] kept indices.
+// pair, or with the tiles' candidates): per pair [2][nsplit][256] exchanged
+// counts and [k] kept indices; cand: the tiles' candidates ([pair][tiles *
+// k] token numbers; null: keys holds every token's top word).
 struct TokShare {
     uint32_t *hist;
     int32_t *list;
+    const int32_t *cand;
 };
 
 __global__ __launch_bounds__(kStepThreads) void k_tok_select_attend(AttnArgs a,
@@ -108,7 +155,8 @@ __global__ __launch_bounds__(kStepThreads) void k_tok_select_attend(AttnArgs a,
     __shared__ TokLds<kStepThreads> lds;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int pair, split;
-    if (a.nsplit > 1) {
+    const bool shared = a.nsplit > 1 && !ts.cand;  // the splits share the selection
+    if (shared) {
         // the splits of a pair wait for one another during the selection,
         // so they are numbered in start order (a ticket drawn as each
         // workgroup starts): when a split waits, its pair's other splits
@@ -149,8 +197,14 @@ __global__ __launch_bounds__(kStepThreads) void k_tok_select_attend(AttnArgs a,
     const uint16_t *row0 = static_cast<const uint16_t *>(a.K) + (size_t)pair * a.t_cap * kHeadDim;
     const uint16_t *qp = static_cast<const uint16_t *>(a.q) +
                          ((size_t)b * a.hkv * a.gqa + (size_t)g * a.gqa) * kHeadDim;
-    Key32Share sh = key32_alone(a.ctx_len);
-    if (a.nsplit > 1) {
+    // the keys: every token's top word, or the tiles' candidates (a few per
+    // kept token, in token order; every split then selects on its own)
+    const int n = ts.cand ? ntables * a.k : a.ctx_len;
+    const uint32_t *kp = keys + (size_t)pair * (ts.cand ? (size_t)n : (size_t)a.t_cap);
+    const bool mapped = ts.cand != nullptr;
+    const int32_t *map = ts.cand + (mapped ? (size_t)pair * n : 0);
+    Key32Share sh = key32_alone(n);
+    if (shared) {
         // split s sweeps keys [s q, (s + 1) q), q whole batches
         const int q = ((a.ctx_len + a.nsplit - 1) / a.nsplit + kTokShareSeg - 1) / kTokShareSeg *
                       kTokShareSeg;
@@ -162,10 +216,14 @@ __global__ __launch_bounds__(kStepThreads) void k_tok_select_attend(AttnArgs a,
         sh.list = ts.list + (size_t)pair * a.k;
         sh.word = ctrl + kTokShareWords + pair;
     }
-    select_key32<kStepThreads, kTokMaxLen, kKey32BatchMem>(keys + (size_t)pair * a.t_cap,
-                                                           a.ctx_len, a.k, lds.sel, lds.u.fine,
+    select_key32<kStepThreads, kTokMaxLen, kKey32BatchMem>(kp, n, a.k, lds.sel, lds.u.fine,
                                                            lds.coarse, lds.u.s, row0, qp, a.gqa,
-                                                           sh);
+                                                           sh, 0, mapped, map);
+    if (mapped) {  // places in the candidate list -> token numbers
+        const int keff = min(a.k, n);
+        for (int i = threadIdx.x; i < keff; i += kStepThreads) lds.sel[i] = map[lds.sel[i]];
+        __syncthreads();
+    }
     if (split == 0)
         for (int i = threadIdx.x; i < a.k; i += kStepThreads)
             idx_out[(size_t)pair * a.k + i] = lds.sel[i];
@@ -192,7 +250,7 @@ __global__ __launch_bounds__(kStepThreads) void k_tok_select_attend(AttnArgs a,
         last = arrive_add(ctrl + pair) == (uint32_t)a.nsplit;
         if (last) {
             st_agent(ctrl + pair, (uint64_t)0);
-            st_agent(ctrl + kTokShareWords + pair, (uint64_t)0);
+            if (shared) st_agent(ctrl + kTokShareWords + pair, (uint64_t)0);
         }
     }
     __syncthreads();
@@ -276,21 +334,34 @@ static void tok_tiles(const Geo &g, int num_cu, int &tiles, int &rows) {
     tiles = (g.ctx_len + rows - 1) / rows;
 }
 
+// Whether the score tiles select their own candidates (kernel 1 LOCAL):
+// several tiles per pair, each small enough for LDS, and fewer candidates
+// than tokens.
+static bool tok_local(const Geo &g, int tiles, int rows, int k) {
+    return tiles > 1 && rows <= kTokLocalRows && k < g.ctx_len &&
+           (long long)tiles * k < (long long)g.ctx_len;
+}
+
 // Workspace of the two-kernel token step after its arrival words: split
-// partials, the keys' top words, count tables, and with several splits per
-// pair the shared selection's exchanged counts and kept list (in that
-// order, each 256-byte aligned; offsets from ws_body).
+// partials, the keys' top words (LOCAL: the tiles' candidates' top words,
+// then their token numbers), count tables, and with several splits per pair
+// sharing the selection its exchanged counts and kept list (in that order,
+// each 256-byte aligned; offsets from ws_body).
 struct TokWs {
-    size_t keys, tables, hist, list, total;
+    bool local;
+    size_t keys, cand, tables, hist, list, total;
 };
-static TokWs tok_ws(const Geo &g, int nsplit, int tiles, int k) {
+static TokWs tok_ws(const Geo &g, int nsplit, int tiles, int rows, int k) {
     TokWs w;
+    w.local = tok_local(g, tiles, rows, k);
+    const size_t per_pair = w.local ? (size_t)tiles * k : (size_t)g.t_cap;
     w.keys = align256(ws_for(g, nsplit));
-    w.tables = align256(w.keys + (size_t)g.pairs * g.t_cap * sizeof(uint32_t));
+    w.cand = align256(w.keys + (size_t)g.pairs * per_pair * sizeof(uint32_t));
+    w.tables = align256(w.cand + (w.local ? (size_t)g.pairs * per_pair * sizeof(int32_t) : 0));
     w.hist = align256(w.tables + (size_t)g.pairs * tiles * kExpBins * sizeof(uint32_t));
-    const size_t np = nsplit > 1 ? (size_t)g.pairs * 2 * nsplit : 0;
+    const size_t np = nsplit > 1 && !w.local ? (size_t)g.pairs * 2 * nsplit : 0;
     w.list = align256(w.hist + np * 256 * sizeof(uint32_t));
-    w.total = w.list + (nsplit > 1 ? (size_t)g.pairs * k * sizeof(int32_t) : 0);
+    w.total = w.list + (np ? (size_t)g.pairs * k * sizeof(int32_t) : 0);
     return w;
 }
 
@@ -310,7 +381,7 @@ AttnPlan plan_tok(const Geo &g, int k, int num_cu) {
     p.fused = 1;
     int tiles, rows;
     tok_tiles(g, num_cu, tiles, rows);
-    p.ws_bytes = ws_total(tok_ws(g, ns, tiles, k).total);
+    p.ws_bytes = ws_total(tok_ws(g, ns, tiles, rows, k).total);
     return p;
 }
 
@@ -332,7 +403,7 @@ hipError_t launch_tok_step(const Geo &g0, const void *q, const void *K, const vo
     const AttnPlan p = plan_tok(g, k, num_cu);
     int tiles, rows;
     tok_tiles(g, num_cu, tiles, rows);
-    const TokWs wl = tok_ws(g, p.nsplit, tiles, k);
+    const TokWs wl = tok_ws(g, p.nsplit, tiles, rows, k);
     char *w = ws_body(ws);
     // the arrival words: the start of the workspace (cleared by kernel 1)
     uint64_t *ctrl = p.nsplit > 1 ? static_cast<uint64_t *>(ws) : nullptr;
@@ -341,12 +412,17 @@ hipError_t launch_tok_step(const Geo &g0, const void *q, const void *K, const vo
     AttnArgs a;
     fill_args(a, g, p, q, K, V, nullptr, k, out, ws);
     // kernel 1: the scores straight from K (the keys are the summaries)
-    k_tok_score<<<dim3(tiles, g.pairs), kTokScoreThreads, 0, s>>>(a, keys, scores, rows, tables,
-                                                                  ctrl);
+    int32_t *cand = wl.local ? reinterpret_cast<int32_t *>(w + wl.cand) : nullptr;
+    if (wl.local)
+        k_tok_score<true><<<dim3(tiles, g.pairs), kTokScoreThreads, 0, s>>>(a, keys, scores, rows,
+                                                                            tables, ctrl, cand);
+    else
+        k_tok_score<false><<<dim3(tiles, g.pairs), kTokScoreThreads, 0, s>>>(a, keys, scores, rows,
+                                                                             tables, ctrl, cand);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    TokShare ts{nullptr, nullptr};
-    if (p.nsplit > 1) {
+    TokShare ts{nullptr, nullptr, cand};
+    if (p.nsplit > 1 && !wl.local) {
         ts.hist = reinterpret_cast<uint32_t *>(w + wl.hist);
         ts.list = reinterpret_cast<int32_t *>(w + wl.list);
     }

@@ -365,7 +365,9 @@ KIN_API size_t kin_quest_ws_bytes(const kin_desc *desc, int32_t k);
  *   ws        kin_token_ws_bytes(desc, k) bytes of device scratch (the
  *             two-kernel form keeps there the scores' top words, its count
  *             tables and, with several workgroups per pair, what they
- *             exchange during the selection).
+ *             exchange during the selection; when every score tile of a
+ *             pair first keeps its own k best tokens, only those
+ *             candidates' top words and token numbers).
  * bf16 only; 1 <= k <= 8192; ctx_len <= 262144.  Errors: KIN_ERR_SHAPE for
  * block != 1 or k < 1, KIN_ERR_UNSUPPORTED for fp32, k > 8192 or longer
  * contexts, plus the checks of the other calls.  One kernel on `stream` when

@@ -74,6 +74,7 @@ TOKEN = [
     ("tok-few-g2-kpast", 2, 8, 4, 300, 400, 320),          # k > ctx: all kept, -1 after
     ("tok-many-g4-k1024", 64, 16, 4, 20000, 1024, 20480),  # 256 pairs: one workgroup each
     ("tok-long-g2-k2048", 1, 4, 2, 131072, 2048, 131072),  # 256 rounds of the select
+    ("tok-tiles-g8-L131072", 2, 32, 4, 131072, 1000, 131072),  # each tile picks candidates
     ("tok-kmax-g4", 2, 4, 1, 40000, 8192, 40000),          # the largest k
     ("tok-g16-short", 2, 32, 2, 33, 32, 48),               # one round, ragged
     # at least as many pairs as CUs, at most 32768 tokens and 2048 kept: one kernel
@@ -109,6 +110,21 @@ def test_token_step_exact_ties_keep_lowest_indices():
                  dtype="bf16", seed=4242, t_cap=3072)
     inp = synth.make_inputs(w, device="cuda", tail_fill=float("nan"))
     inp["K"][:, :, :3000] = inp["K"][:, :, :1].clone()
+    idx, out, sc = run_token(w, inp, 300)
+    want = torch.arange(300, dtype=torch.int32, device="cuda").expand(2, 2, 300)
+    assert torch.equal(idx, want)
+    check(w, inp, 300, idx, out, sc, [0, 1], certify=False)
+
+
+def test_token_tile_candidates_exact_ties_keep_lowest_indices():
+    """Few pairs and many tiles per pair, so every score tile selects its own
+    candidates: every key equal, all scores tie in every tile and across
+    them, and the k lowest token indices (all of the first tile's) are
+    kept."""
+    w = Workload("tok-ties-tiles", batch=2, hq=8, hkv=2, ctx_len=20000, block=1, topk=300,
+                 dtype="bf16", seed=4245, t_cap=20000)
+    inp = synth.make_inputs(w, device="cuda", tail_fill=float("nan"))
+    inp["K"][:, :, :20000] = inp["K"][:, :, :1].clone()
     idx, out, sc = run_token(w, inp, 300)
     want = torch.arange(300, dtype=torch.int32, device="cuda").expand(2, 2, 300)
     assert torch.equal(idx, want)
@@ -185,23 +201,27 @@ def _plant_near_tie(inp, w, b, g, k, exact, above=False):
     inp["K"][b, g, c] = row.cuda()
 
 
-@pytest.mark.parametrize("batch", [64, 2], ids=["one-kernel", "two-kernel"])
-def test_token_near_ties_below_the_top_word(batch):
+@pytest.mark.parametrize("batch,k", [(64, 100), (2, 100), (2, 200)],
+                         ids=["one-kernel", "two-kernel-tile-candidates", "two-kernel-all-words"])
+def test_token_near_ties_below_the_top_word(batch, k):
     """Planted keys whose scores equal the k-th score in the top 32 bits of
     the order key (near ties: they differ below; exact ties: they do not):
     the recomputed low words must order them as the oracle does, in the
     one-kernel step (256 pairs: the top words in LDS) and in the two-kernel
-    step (8 pairs: the top words handed over in memory)."""
-    w = Workload(f"tok-near-b{batch}", batch=batch, hq=16, hkv=4, ctx_len=2000, block=1,
-                 topk=100, dtype="bf16", seed=4244, t_cap=2048)
+    step (8 pairs): with k = 100 each of the 16 score tiles selects its own
+    100 candidates first (their top words handed over in memory), with k =
+    200 the tiles' candidates would outnumber the 2000 tokens, so every
+    token's top word is handed over."""
+    w = Workload(f"tok-near-b{batch}-k{k}", batch=batch, hq=16, hkv=4, ctx_len=2000, block=1,
+                 topk=k, dtype="bf16", seed=4244, t_cap=2048)
     inp = synth.make_inputs(w, device="cuda", tail_fill=float("nan"))
     last = batch - 1
     # (sequence, KV head, exact tie, planted key just above the k-th)
     planted = [(0, 0, False, False), (0, 1, True, False), (last, 2, False, True),
                (last, 3, True, False), (last, 0, False, True)]
     for b, g, exact, above in planted:
-        _plant_near_tie(inp, w, b, g, 100, exact, above)
-    idx, out, sc = run_token(w, inp, 100)
-    check(w, inp, 100, idx, out, sc, sorted({p[0] for p in planted}), certify=False)
-    idx2, out2, _ = run_token(w, inp, 100, scores=False)
+        _plant_near_tie(inp, w, b, g, k, exact, above)
+    idx, out, sc = run_token(w, inp, k)
+    check(w, inp, k, idx, out, sc, sorted({p[0] for p in planted}), certify=False)
+    idx2, out2, _ = run_token(w, inp, k, scores=False)
     assert torch.equal(idx2, idx)
