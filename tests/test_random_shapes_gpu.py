@@ -94,7 +94,21 @@ def _draw_token_case(rng, i):
     return (f"tok{i}-b{batch}-g{gqa}-kv{hkv}-L{ctx}-k{k}", batch, gqa * hkv, hkv, ctx, k, cap)
 
 
-TOKEN_CASES = [_draw_token_case(random.Random(9100 + i), i) for i in range(10)]
+def _draw_token_tile_case(rng, i):
+    """Few pairs, long contexts and k below a score tile's length: the
+    shapes for which each score tile first keeps its own k best tokens."""
+    hkv = rng.choice([2, 4, 8])
+    batch = max(1, rng.choice([16, 32, 64, 128]) // hkv + rng.randint(-1, 1))
+    ctx = rng.randint(8000, 100000)
+    rows = ctx * batch * hkv // 256  # about one tile's tokens
+    k = rng.randint(1, max(1, min(8192, rows // 2)))
+    gqa = rng.choice([1, 2, 4, 8])
+    cap = ctx + rng.randint(0, 100)
+    return (f"toktile{i}-b{batch}-g{gqa}-kv{hkv}-L{ctx}-k{k}", batch, gqa * hkv, hkv, ctx, k, cap)
+
+
+TOKEN_CASES = [_draw_token_case(random.Random(9100 + i), i) for i in range(10)] + \
+    [_draw_token_tile_case(random.Random(9200 + i), i) for i in range(4)]
 
 
 def _run_token(w, inp, k, scores):
