@@ -5,15 +5,19 @@
 //   kernel 1 (k_tok_score): the group score of every key, fp64, streamed
 //            straight from K in tiles spread over the chip (the scoring loop
 //            of scoring.h); the top 32 bits of each score's order key
-//            written out, and each tile's sign/exponent counts;
+//            written out, and each tile's sign/exponent counts.  When the
+//            tiles fit in LDS and their k best together are fewer than the
+//            tokens, each tile instead keeps its words in LDS, selects its
+//            own k best (a superset of the pair's top k) and writes out only
+//            those candidates;
 //   kernel 2 (k_tok_select_attend): the k best tokens (select_key32.h over
-//            those words, read from memory, low words recomputed from K
-//            only where they decide), then attention over those tokens' K/V
-//            (MFMA, online softmax), split over several workgroups when
-//            there are fewer pairs than CUs, the splits combined in-kernel;
-//            the splits of a pair share the selection's sweeps (each sweeps
-//            its own range of the keys, the counts summed through the
-//            workspace).
+//            those words or candidates, read from memory, low words
+//            recomputed from K only where they decide), then attention over
+//            those tokens' K/V (MFMA, online softmax), split over several
+//            workgroups when there are fewer pairs than CUs, the splits
+//            combined in-kernel; over every token's word, the splits of a
+//            pair share the selection's sweeps (each sweeps its own range of
+//            the keys, the counts summed through the workspace).
 //
 // With at least as many pairs as CUs, a context of at most 32768 tokens and
 // at most 2048 kept, the whole step runs in one kernel (k_tok_step), one
