@@ -84,12 +84,14 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step_f32(AttnArgs a, St
     __syncthreads();
 
     // 1. scores.  Rows of blocks below the newest one, 16 per wave and
-    // round (4 rows per 16-lane group load), the next round's loads issued
-    // before this round's math; past the range a load re-reads the last
-    // scored row and its score is dropped.  The newest row is never loaded
-    // here: wave 0 rewrites it during this phase.  The first round's loads
-    // go out before the query rows are summed (they do not need the sum),
-    // so their round trip overlaps the query's and the newest row's.
+    // round (4 rows per 16-lane group load), two rounds in flight: round
+    // it + 2's loads are issued as soon as round it's math has read its
+    // registers; past the range a load re-reads the last scored row and
+    // its score is dropped.  The newest row is never loaded here: wave 0
+    // rewrites it during this phase.  The first two rounds' loads go out
+    // before the query rows are summed (they do not need the sum), so
+    // their round trips overlap the query's and the newest row's (a pair
+    // of 256 blocks is two rounds: one round trip for the whole scan).
     const int sub = lane & 15, grp = lane >> 4;
     const int n_rows = nb - 1;
     constexpr int kRound = NW * 16;
@@ -103,6 +105,7 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step_f32(AttnArgs a, St
     };
     u32x4 wa[2][4], wb[2][4];
     if (n_it > 0) load_round(0, wa[0], wb[0]);
+    if (n_it > 1) load_round(1, wa[1], wb[1]);
     double qs[8];
     group_query_sum<KIN_F32>(a.q, b, g, a.hkv, a.gqa, sub, qs);
     if (wave == 0)
@@ -112,11 +115,11 @@ __global__ __launch_bounds__(kStepThreads) void k_decode_step_f32(AttnArgs a, St
     if (n_it > 0) {
         for (int it = 0; it < n_it; ++it) {
             const int cur = it & 1;
-            // the next round (or a harmless repeat of the last one)
-            load_round(min(it + 1, n_it - 1), wa[cur ^ 1], wb[cur ^ 1]);
             double part[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) part[v] = slice_dot<KIN_F32>(qs, wa[cur][v], wb[cur][v]);
+            // this round's registers are read: they take round it + 2
+            if (it + 2 < n_it) load_round(it + 2, wa[cur], wb[cur]);
             const double xv = fold4(part, lane);
             const int slot = ((lane & 8) ? 2 : 0) + ((lane & 4) ? 1 : 0);
             const int j = wave * 16 + it * kRound + 4 * slot + grp;
