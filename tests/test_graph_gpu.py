@@ -87,16 +87,20 @@ def test_block_step_replayed_from_a_graph(case):
     _check_replays(call, inp["q"], lambda: (bufs.idx, bufs.out), w.seed)
 
 
-def test_token_step_replayed_from_a_graph():
-    w = Workload("graph-token", batch=2, hq=8, hkv=2, ctx_len=20000, block=1, topk=500,
+@pytest.mark.parametrize("k", [500, 100], ids=["all-words", "tile-candidates"])
+def test_token_step_replayed_from_a_graph(k):
+    """4 pairs over 53 score tiles: with k = 500 the splits share a
+    selection over every token's word, with k = 100 each tile first keeps
+    its own 100 best."""
+    w = Workload("graph-token", batch=2, hq=8, hkv=2, ctx_len=20000, block=1, topk=k,
                  dtype="bf16", seed=915, t_cap=20000)
     inp = synth.make_inputs(w, device="cuda")
     desc = kb.make_desc(w.batch, w.hkv, w.gqa, w.cap, w.ctx_len, 1, torch.bfloat16)
-    idx = torch.empty((w.batch, w.hkv, 500), dtype=torch.int32, device="cuda")
+    idx = torch.empty((w.batch, w.hkv, k), dtype=torch.int32, device="cuda")
     out = torch.empty((w.batch, w.hq, 128), dtype=torch.bfloat16, device="cuda")
-    ws = torch.zeros(kb.kin_token_ws_bytes(desc, 500), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(kb.kin_token_ws_bytes(desc, k), dtype=torch.uint8, device="cuda")
     _check_replays(lambda: kb.kin_token_decode_step(desc, inp["q"], inp["K"], inp["V"], None,
-                                                    500, idx, out, ws),
+                                                    k, idx, out, ws),
                    inp["q"], lambda: (idx, out), 915)
 
 

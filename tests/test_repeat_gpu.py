@@ -74,15 +74,17 @@ def test_block_step_repeated_on_one_workspace(case):
     _repeat(call, lambda: (bufs.idx, bufs.out))
 
 
-def test_token_step_repeated_on_one_workspace():
-    w = Workload("rep-token", batch=2, hq=8, hkv=2, ctx_len=20000, block=1, topk=500,
-                 dtype="bf16", seed=913, t_cap=20000)  # 4 pairs: the two-kernel form
+@pytest.mark.parametrize("k", [500, 100], ids=["all-words", "tile-candidates"])
+def test_token_step_repeated_on_one_workspace(k):
+    # 4 pairs: the two-kernel form; k = 100: the score tiles pick candidates
+    w = Workload("rep-token", batch=2, hq=8, hkv=2, ctx_len=20000, block=1, topk=k,
+                 dtype="bf16", seed=913, t_cap=20000)
     inp = synth.make_inputs(w, device="cuda")
     desc = kb.make_desc(w.batch, w.hkv, w.gqa, w.cap, w.ctx_len, 1, torch.bfloat16)
-    idx = torch.empty((w.batch, w.hkv, 500), dtype=torch.int32, device="cuda")
+    idx = torch.empty((w.batch, w.hkv, k), dtype=torch.int32, device="cuda")
     out = torch.empty((w.batch, w.hq, 128), dtype=torch.bfloat16, device="cuda")
-    ws = torch.zeros(kb.kin_token_ws_bytes(desc, 500), dtype=torch.uint8, device="cuda")
-    _repeat(lambda: kb.kin_token_decode_step(desc, inp["q"], inp["K"], inp["V"], None, 500, idx,
+    ws = torch.zeros(kb.kin_token_ws_bytes(desc, k), dtype=torch.uint8, device="cuda")
+    _repeat(lambda: kb.kin_token_decode_step(desc, inp["q"], inp["K"], inp["V"], None, k, idx,
                                              out, ws),
             lambda: (idx, out))
 
@@ -146,7 +148,9 @@ def test_one_workspace_zeroed_once_serves_every_split_form():
     shapes and entry points: the keep-all one-launch step, the bf16 two-kernel
     step (its first kernel clears the second's words), the standalone
     second half (kin_decode_select_attend), the fp32 two-kernel step, the
-    standalone split attention, the token-level and Quest two-kernel steps.
+    standalone split attention, the token-level two-kernel step (over every
+    token's word, and with the score tiles' candidates) and the Quest
+    two-kernel step.
     After every call the first 8 KiB (the arrival words) are zero again, and
     every result equals the same call's on a fresh zeroed workspace."""
     calls = []
@@ -191,12 +195,13 @@ def test_one_workspace_zeroed_once_serves_every_split_form():
                   dtype="bf16", seed=915, t_cap=20000)
     it = synth.make_inputs(wt, device="cuda")
     dt_ = kb.make_desc(wt.batch, wt.hkv, wt.gqa, wt.cap, wt.ctx_len, 1, torch.bfloat16)
-    tidx = torch.empty((wt.batch, wt.hkv, 500), dtype=torch.int32, device="cuda")
-    tout = torch.empty((wt.batch, wt.hq, 128), dtype=torch.bfloat16, device="cuda")
-    calls.append(("ws-token",
-                  lambda ws: kb.kin_token_decode_step(dt_, it["q"], it["K"], it["V"], None, 500,
-                                                      tidx, tout, ws),
-                  kb.kin_token_ws_bytes(dt_, 500), lambda: (tidx, tout)))
+    for tk, tname in ((500, "ws-token"), (100, "ws-token-tiles")):
+        tidx = torch.empty((wt.batch, wt.hkv, tk), dtype=torch.int32, device="cuda")
+        tout = torch.empty((wt.batch, wt.hq, 128), dtype=torch.bfloat16, device="cuda")
+        calls.append((tname,
+                      lambda ws, tk=tk, tidx=tidx, tout=tout: kb.kin_token_decode_step(
+                          dt_, it["q"], it["K"], it["V"], None, tk, tidx, tout, ws),
+                      kb.kin_token_ws_bytes(dt_, tk), lambda tidx=tidx, tout=tout: (tidx, tout)))
 
     wq = Workload("ws-quest", batch=3, hq=16, hkv=2, ctx_len=4000, block=16, topk=60,
                   dtype="bf16", seed=916, t_cap=4096)
