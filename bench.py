@@ -658,10 +658,10 @@ def main():
         res["calib_copy_bytes"] = 2**30
         del src, dst
 
+    # the oracle is timed last, after every GPU measurement: a GPU left idle
+    # for its ~15 s would start the next measurements from a lower clock
     cpu_layer = layers[0]
-    if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(w, cpu_layer, args.cpu_seqs)
-    del layers, cpu_layer
+    del layers
     torch.cuda.empty_cache()
 
     # the other configurations, same protocol, one entry each
@@ -692,6 +692,9 @@ def main():
                             "gbs": round(best, 1), "source": src,
                             "frac_of_published": round(best / PEAK_HBM_GBS, 4),
                             "step_frac": round(gbs / best, 4)}
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, cpu_layer, args.cpu_seqs)
+    del cpu_layer
     print(json.dumps(res), flush=True)
 
 
