@@ -96,7 +96,7 @@ __device__ __noinline__ double exact_score_mapped(const uint16_t *row0, const in
 // workgroup (each thread scans a contiguous segment); ta, tb: the totals.
 // Ends with a barrier.
 template <int NT>
-__device__ void block_exclusive_scan2(uint32_t *a, uint32_t *b, int n,
+__device__ __forceinline__ void block_exclusive_scan2(uint32_t *a, uint32_t *b, int n,
                                       uint32_t (&wsum)[2][NT / 64], uint32_t &ta,
                                       uint32_t &tb) {
     const int tid = threadIdx.x, lane = tid & 63;
