@@ -35,6 +35,8 @@
 // the launch's start order).
 #pragma once
 
+#include <type_traits>
+
 #include "attn_impl.h"
 
 namespace kin {
@@ -135,10 +137,17 @@ __device__ __forceinline__ void block_exclusive_scan2(uint32_t *a, uint32_t *b, 
 }
 
 // Top words of keys j0 + u * NT + threadIdx.x, u < B (slots past n re-read
-// key 0; callers ignore them).
+// key 0; callers ignore them).  A whole batch inside the keys (every batch
+// but the last) reads from one base address at constant offsets.
 template <int NT, int B>
 __device__ __forceinline__ void key32_batch(const uint32_t *key, int n, int j0,
                                             uint32_t (&x)[B]) {
+    if (j0 + B * NT <= n) {  // uniform
+        const uint32_t *p = key + j0 + (int)threadIdx.x;
+#pragma unroll
+        for (int u = 0; u < B; ++u) x[u] = p[u * NT];
+        return;
+    }
 #pragma unroll
     for (int u = 0; u < B; ++u) {
         const int j = j0 + u * NT + (int)threadIdx.x;
@@ -334,10 +343,24 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
         const int nbuf = buf == 2 ? 0 : buf + 1;
         const uint32_t dmask = (1u << width) - 1u;
         key32_sweep<NT, B>(key, n, lo, hi, [&](int j0, const uint32_t (&x)[B]) {
+            // past the first digit few keys match: most batches of a wave
+            // count nothing and skip the atomics altogether
+            auto count = [&](auto whole) {
+                auto match = [&](int u) {
+                    return (whole.value || j0 + u * NT + tid < n) && (x[u] & pmask) == prefix;
+                };
+                uint64_t hit = 0;
 #pragma unroll
-            for (int u = 0; u < B; ++u)
-                if (j0 + u * NT + tid < n && (x[u] & pmask) == prefix)
-                    atomicAdd(&h[(x[u] >> lo_bit) & dmask], 1u);
+                for (int u = 0; u < B; ++u) hit |= __builtin_amdgcn_ballot_w64(match(u));
+                if (hit == 0ull) return;
+#pragma unroll
+                for (int u = 0; u < B; ++u)
+                    if (match(u)) atomicAdd(&h[(x[u] >> lo_bit) & dmask], 1u);
+            };
+            if (j0 + B * NT <= n)  // uniform: a whole batch, no bound checks
+                count(std::true_type());
+            else
+                count(std::false_type());
         });
         for (int i = tid; i < 256; i += NT) sc.hist[nbuf][i] = 0u;
         __syncthreads();
@@ -425,14 +448,19 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
         static_assert(B <= 64, "one lane per round of a batch");
         key32_sweep<NT, B>(key, n, lo, hi, [&](int j0, const uint32_t (&x)[B]) {
             const int r0 = j0 / NT;
-            const bool full = j0 + B * NT <= n;  // uniform: no bound checks
-            uint32_t mine = 0;
+            auto counts = [&](auto whole) {
+                uint32_t mine = 0;
 #pragma unroll
-            for (int u = 0; u < B; ++u) {
-                const bool keep = (full || j0 + u * NT + tid < n) && x[u] >= prefix;
-                const uint32_t c = (uint32_t)__popcll(__ballot(keep));
-                mine = lane == u ? c : mine;
-            }
+                for (int u = 0; u < B; ++u) {
+                    const bool keep = (whole.value || j0 + u * NT + tid < n) && x[u] >= prefix;
+                    const uint32_t c = (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(keep));
+                    mine = lane == u ? c : mine;
+                }
+                return mine;
+            };
+            // uniform: a whole batch needs no bound checks
+            const uint32_t mine = j0 + B * NT <= n ? counts(std::true_type())
+                                                   : counts(std::false_type());
             if (lane < B && r0 + lane < R) {
                 sc.cnt[(r0 + lane) * NW + wave] = mine;
                 sc.cnt_tie[(r0 + lane) * NW + wave] = 0u;
@@ -445,18 +473,25 @@ __device__ void select_key32(const uint32_t *key, int n, int k, int32_t *out,
         share_totals<NT>(sc.hist[buf], tot, 0u, sh, round, before, before_tie);
         key32_sweep<NT, B>(key, n, lo, hi, [&](int j0, const uint32_t (&x)[B]) {
             const int r0 = j0 / NT;
-            const bool full = j0 + B * NT <= n;
             const uint32_t base = lane < B && r0 + lane < R ? sc.cnt[(r0 + lane) * NW + wave] : 0u;
+            auto write = [&](auto whole) {
 #pragma unroll
-            for (int u = 0; u < B; ++u) {
-                const int j = j0 + u * NT + tid;
-                const bool keep = (full || j < n) && x[u] >= prefix;
-                const uint32_t pos = before + lane_value(base, u) + rank_below(__ballot(keep));
-                if (keep) {
-                    out[pos] = tok0 + j;
-                    if (out_key) out_key[pos] = x[u];
+                for (int u = 0; u < B; ++u) {
+                    const int j = j0 + u * NT + tid;
+                    const bool keep = (whole.value || j < n) && x[u] >= prefix;
+                    const uint64_t kb = __builtin_amdgcn_ballot_w64(keep);
+                    if (kb == 0ull) continue;  // uniform: nothing kept in this round
+                    const uint32_t pos = before + lane_value(base, u) + rank_below(kb);
+                    if (keep) {
+                        out[pos] = tok0 + j;
+                        if (out_key) out_key[pos] = x[u];
+                    }
                 }
-            }
+            };
+            if (j0 + B * NT <= n)  // uniform: a whole batch, no bound checks
+                write(std::true_type());
+            else
+                write(std::false_type());
         });
         __syncthreads();
         gather(before, tot);
