@@ -84,11 +84,17 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_f32(AttnArgs a) {
 // (pair, split); every split of a pair repeats the same selection)
 // ---------------------------------------------------------------------------
 
+// cand (bf16, tile candidates): the pair's n_cand candidates, in block
+// order, their scores at scores + pair * n_cand and their block numbers at
+// cand + pair * n_cand; the selection keeps k of them (places ascending,
+// ties to the lower place, hence the lower block) and turns the places into
+// block numbers.  Otherwise scores holds every block's score (stride nb_cap).
 template <int DT, int KPT, int MODE>
 __global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a0,
                                                                 const double *__restrict__ scores,
                                                                 int nb_cap, int32_t *idx_out,
-                                                                uint64_t *ctrl, void *S_newest) {
+                                                                uint64_t *ctrl, void *S_newest,
+                                                                const int32_t *cand, int n_cand) {
     constexpr int NW = kStepThreads / 64;
     __shared__ int32_t sel[kStepIdxCap];
     __shared__ union {
@@ -105,7 +111,18 @@ __global__ __launch_bounds__(kStepThreads) void k_select_attend(AttnArgs a0,
     if constexpr (DT == KIN_F32) load_q_f32(a, pair, qf32);
     select_clear(u.s);
     __syncthreads();
-    select_topk<KPT, kStepThreads, false>(scores + (size_t)pair * nb_cap, a.nb, a.k, sel, u.s);
+    if (cand) {
+        select_topk<KPT, kStepThreads, false>(scores + (size_t)pair * n_cand, n_cand, a.k, sel,
+                                              u.s);
+        __syncthreads();
+        // k < n_cand and at least k candidates are real blocks (every tile
+        // hands over min(k, its blocks)): every kept place holds a block
+        const int32_t *cp = cand + (size_t)pair * n_cand;
+        for (int i = threadIdx.x; i < a.k; i += kStepThreads) sel[i] = cp[sel[i]];
+    } else {
+        select_topk<KPT, kStepThreads, false>(scores + (size_t)pair * nb_cap, a.nb, a.k, sel,
+                                              u.s);
+    }
     __syncthreads();
     if (split == 0)
         for (int i = threadIdx.x; i < a.k; i += kStepThreads) idx_out[(size_t)pair * a.k + i] = sel[i];
@@ -242,9 +259,26 @@ double *step_scores_in_ws(const Geo &g, const AttnPlan &p, void *ws) {
     return reinterpret_cast<double *>(ws_body(ws) + align256(ws_for(g, p.nsplit)));
 }
 
-size_t step_ws_with_scores(const Geo &g, const AttnPlan &p) {
-    return kCtrlBytes + align256(ws_for(g, p.nsplit)) +
-           (size_t)g.pairs * (size_t)g.nb_cap * sizeof(double);
+// tile candidates: their scores, then (256-byte aligned) their block numbers
+static size_t cand_idx_offset(const Geo &g, const TileCands &tc) {
+    return align256((size_t)g.pairs * tc.n * sizeof(double));
+}
+
+int32_t *step_cands_in_ws(const Geo &g, const AttnPlan &p, const TileCands &tc, void *ws) {
+    return reinterpret_cast<int32_t *>(reinterpret_cast<char *>(step_scores_in_ws(g, p, ws)) +
+                                       cand_idx_offset(g, tc));
+}
+
+size_t step_ws_with_scores(const Geo &g, const AttnPlan &p, int k, int num_cu) {
+    size_t area = (size_t)g.pairs * (size_t)g.nb_cap * sizeof(double);
+    if (k > 0) {
+        const TileCands tc = step_tile_cands(g, k, num_cu);
+        if (tc.tiles) {
+            const size_t c = cand_idx_offset(g, tc) + (size_t)g.pairs * tc.n * sizeof(int32_t);
+            area = c > area ? c : area;
+        }
+    }
+    return kCtrlBytes + align256(ws_for(g, p.nsplit)) + area;
 }
 
 static hipError_t launch_combine(const Geo &g, const AttnArgs &a, void *out, int nsplit,
@@ -281,16 +315,17 @@ hipError_t launch_attention(const Geo &g, const AttnPlan &p, const void *q, cons
 
 template <int DT>
 static void launch_sa(const Geo &g, const AttnArgs &a, dim3 grid, const double *scores,
-                      int32_t *idx, uint64_t *ctrl, void *S_newest, hipStream_t s) {
+                      int32_t *idx, uint64_t *ctrl, void *S_newest, hipStream_t s,
+                      const int32_t *cand, int n_cand) {
 #define KIN_SA_MODE(KPT, MODE)                                                                 \
     k_select_attend<DT, KPT, MODE><<<grid, kStepThreads, 0, s>>>(a, scores, g.nb_cap, idx, ctrl, \
-                                                                 S_newest)
+                                                                 S_newest, cand, n_cand)
 #define KIN_SA(KPT)                                                                            \
     (DT != KIN_BF16 ? KIN_SA_MODE(KPT, kContig)                                                \
      : g.pages      ? KIN_SA_MODE(KPT, (DT == KIN_BF16 ? kPaged : kContig))                    \
      : g.share_n    ? KIN_SA_MODE(KPT, (DT == KIN_BF16 ? kShared : kContig))                   \
                     : KIN_SA_MODE(KPT, kContig))
-    switch (select_kpt(g.nb, kStepThreads)) {
+    switch (select_kpt(cand ? n_cand : g.nb, kStepThreads)) {
     case 1: KIN_SA(1); break;
     case 2: KIN_SA(2); break;
     case 4: KIN_SA(4); break;
@@ -310,7 +345,8 @@ uint64_t *step_ctrl(const AttnPlan &p, void *ws) {
 
 hipError_t launch_select_attend(const Geo &g, const AttnPlan &p, const void *q, const void *K,
                                 const void *V, const double *scores, int k, int32_t *idx,
-                                void *out, void *ws, hipStream_t s, void *S_newest) {
+                                void *out, void *ws, hipStream_t s, void *S_newest,
+                                const int32_t *cand, int n_cand) {
     if (!p.fused) {
         hipError_t e = launch_block_topk(g, scores, k, idx, s);
         if (e != hipSuccess) return e;
@@ -321,9 +357,9 @@ hipError_t launch_select_attend(const Geo &g, const AttnPlan &p, const void *q, 
     uint64_t *ctrl = step_ctrl(p, ws);
     dim3 grid(p.nsplit, g.pairs);
     if (g.dtype == KIN_BF16)
-        launch_sa<KIN_BF16>(g, a, grid, scores, idx, ctrl, S_newest, s);
+        launch_sa<KIN_BF16>(g, a, grid, scores, idx, ctrl, S_newest, s, cand, n_cand);
     else
-        launch_sa<KIN_F32>(g, a, grid, scores, idx, ctrl, nullptr, s);
+        launch_sa<KIN_F32>(g, a, grid, scores, idx, ctrl, nullptr, s, nullptr, 0);
     return hipGetLastError();
 }
 

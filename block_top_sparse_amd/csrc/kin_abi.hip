@@ -290,7 +290,7 @@ static size_t step_ws_need(const kin::Geo &g, int32_t k, int cu, bool scores) {
     if (!g.pages && !g.share_n && kin::step_f32_single_kernel(g, k))
         return kin::step_f32_ws_bytes(g, k);
     const kin::AttnPlan p = kin::plan_step(g, k, cu);
-    return scores ? p.ws_bytes : kin::step_ws_with_scores(g, p);
+    return scores ? p.ws_bytes : kin::step_ws_with_scores(g, p, k, cu);
 }
 
 // The decode step for a checked geometry (contiguous or paged).
@@ -332,10 +332,18 @@ static kin_status decode_step(const kin::Geo &g, const void *q, const void *K, c
     if (newest_only && p.fused)
         return launched(kin::launch_select_attend(g, p, q, K, V, sc, k, idx, out, ws, s, S),
                         "kin_sparse_decode_step");
+    // no scores wanted, few pairs: the score tiles may hand over only their
+    // own k best (kin::step_tile_cands)
+    const kin::TileCands tc = scores || newest_only || !p.fused ? kin::TileCands{0, 0, 0}
+                                                                : kin::step_tile_cands(g, k, cu);
+    int32_t *cand = tc.tiles ? kin::step_cands_in_ws(g, p, tc, ws) : nullptr;
     // the scoring kernel also clears the second kernel's arrival words
     hipError_t e = kin::launch_update_and_score(g, q, K, S, sc, cu, s, newest_only,
-                                                kin::step_ctrl(p, ws));
-    if (e == hipSuccess) e = kin::launch_select_attend(g, p, q, K, V, sc, k, idx, out, ws, s);
+                                                kin::step_ctrl(p, ws), cand ? &tc : nullptr,
+                                                cand, k);
+    if (e == hipSuccess)
+        e = kin::launch_select_attend(g, p, q, K, V, sc, k, idx, out, ws, s, nullptr, cand,
+                                      tc.n);
     return launched(e, "kin_sparse_decode_step");
 }
 
@@ -592,7 +600,7 @@ size_t kin_sparse_ws_bytes(const kin_desc *desc, int32_t k) {
     // the step's two-kernel form, with room for the scores (scores == NULL)
     const size_t b = kin::step_single_kernel(g, k, cu)      ? 0
                      : kin::step_f32_single_kernel(g, k) ? kin::step_f32_ws_bytes(g, k)
-                                                         : kin::step_ws_with_scores(g, kin::plan_step(g, k, cu));
+                                                         : kin::step_ws_with_scores(g, kin::plan_step(g, k, cu), k, cu);
     return a > b ? a : b;
 }
 

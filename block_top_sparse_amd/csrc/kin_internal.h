@@ -63,12 +63,25 @@ hipError_t launch_block_summary_paged(const Geo &g, const void *K, void *S, int 
                                       int t_end, hipStream_t s);
 hipError_t launch_block_score(const Geo &g, const void *q, const void *S, double *scores,
                               int num_cu, hipStream_t s);
+// Tile candidates of the few-pair two-kernel step (bf16, one length for
+// every sequence): when the score tiles of a pair fit in LDS and their k
+// best together are fewer than the pair's blocks, each tile keeps its own
+// k best (a superset of the pair's top k) and hands over only those.
+// tiles == 0: not used; n = tiles * k candidates per pair.
+struct TileCands {
+    int tiles, rows, n;
+};
+TileCands step_tile_cands(const Geo &g, int k, int num_cu);
 // decode step, first half: newest-block summary update + all block scores
 // (bf16: newest_only skips the scores, for a step that keeps every block;
-// ctrl_zero: arrival words, one per pair, to clear for the second half)
+// ctrl_zero: arrival words, one per pair, to clear for the second half;
+// tc: tile candidates instead of all scores, their scores to `scores` and
+// their block numbers to cand_idx, [pair][tc->n] each)
 hipError_t launch_update_and_score(const Geo &g, const void *q, const void *K, void *S,
                                    double *scores, int num_cu, hipStream_t s,
-                                   bool newest_only = false, uint64_t *ctrl_zero = nullptr);
+                                   bool newest_only = false, uint64_t *ctrl_zero = nullptr,
+                                   const TileCands *tc = nullptr, int32_t *cand_idx = nullptr,
+                                   int k = 0);
 hipError_t launch_block_topk(const Geo &g, const double *scores, int k, int32_t *idx,
                              hipStream_t s);
 hipError_t launch_attention(const Geo &g, const AttnPlan &p, const void *q, const void *K,
@@ -82,9 +95,13 @@ AttnPlan plan_step(const Geo &g, int k, int num_cu);
 // step or left at zero by the previous call; S_newest: with a fused plan
 // that keeps every block, bf16, the summaries whose newest row the kernel
 // rebuilds, so that no first half is needed)
+// cand: the tile candidates' block numbers ([pair][n_cand]; scores then
+// holds their scores in the same layout), or nullptr: scores holds every
+// block's score ([pair][nb_cap])
 hipError_t launch_select_attend(const Geo &g, const AttnPlan &p, const void *q, const void *K,
                                 const void *V, const double *scores, int k, int32_t *idx,
-                                void *out, void *ws, hipStream_t s, void *S_newest = nullptr);
+                                void *out, void *ws, hipStream_t s, void *S_newest = nullptr,
+                                const int32_t *cand = nullptr, int n_cand = 0);
 // the whole decode step in one kernel (one workgroup per pair); usable when
 // step_single_kernel() says so (bf16, enough pairs to cover the chip)
 bool step_single_kernel(const Geo &g, int k, int num_cu);
@@ -99,9 +116,12 @@ hipError_t launch_decode_step_f32(const Geo &g, const void *q, const void *K, co
 // nullptr: the plan has none)
 uint64_t *step_ctrl(const AttnPlan &p, void *ws);
 // where a two-kernel step keeps its fp64 scores in ws when the caller
-// passes no scores buffer, and the workspace bytes that form needs
+// passes no scores buffer (or, with tile candidates, their scores, then
+// their block numbers: step_cands_in_ws), and the workspace bytes that form
+// needs (k > 0: room for the tile candidates of step_tile_cands(g, k, cu))
 double *step_scores_in_ws(const Geo &g, const AttnPlan &p, void *ws);
-size_t step_ws_with_scores(const Geo &g, const AttnPlan &p);
+int32_t *step_cands_in_ws(const Geo &g, const AttnPlan &p, const TileCands &tc, void *ws);
+size_t step_ws_with_scores(const Geo &g, const AttnPlan &p, int k = 0, int num_cu = 0);
 // Quest-style summaries ([pair][nb_cap][2][head_dim]: minimum, maximum) of
 // blocks [j0, j1), and the decode step's first kernel with the Quest bound
 // (update: the newest block's rows rebuilt first); bf16

@@ -38,14 +38,56 @@ namespace kin {
 // block rebuilds that block's summary first.  About one tile per CU, so a
 // few pairs still spread over the whole chip.
 constexpr int kTileThreads = 512;
+// blocks of a score tile whose scores stay in LDS for the tile's own
+// selection (tile candidates)
+constexpr int kTileCandRows = 2048;
 
-template <bool UPDATE, bool SHARED>
+// Score tiles per pair and blocks per tile: about one workgroup per CU,
+// rows a multiple of one round of the 8 waves.
+static void tile_geometry(const Geo &g, int num_cu, int &tiles, int &rows) {
+    constexpr int kRows = (kTileThreads / 64) * kScoreBatch;
+    const int cu = num_cu > 0 ? num_cu : 256;
+    tiles = g.pairs >= cu ? 1 : (cu + g.pairs - 1) / g.pairs;
+    rows = (g.nb + tiles - 1) / tiles;
+    rows = (rows + kRows - 1) / kRows * kRows;
+    tiles = (g.nb + rows - 1) / rows;
+}
+
+TileCands step_tile_cands(const Geo &g, int k, int num_cu) {
+    TileCands t{0, 0, 0};
+    // every sequence of one length (a shorter one could keep all its blocks,
+    // fewer than k), and the tiles' k best together fewer than the blocks.
+    // Only for more than 8 blocks per thread of the selecting workgroup:
+    // below that its selection is short, and the tiles' own selections cost
+    // more than they save (measured: 2048 blocks per pair +1.7%, 4096 even,
+    // 8192 -4 to -7%)
+    if (g.dtype != KIN_BF16 || g.ctx_lens || k < 1 || k >= g.nb || k > kStepIdxCap ||
+        g.nb <= 8 * kStepThreads)
+        return t;
+    int tiles, rows;
+    tile_geometry(g, num_cu, tiles, rows);
+    if (tiles < 2 || rows > kTileCandRows || (long long)tiles * k >= g.nb) return t;
+    t.tiles = tiles;
+    t.rows = rows;
+    t.n = tiles * k;
+    return t;
+}
+
+// CKPT > 0 (tile candidates): the tile's scores stay in LDS, counted into
+// its own sign/exponent tables, and the tile selects its k best (ties to
+// the lower block) with select.h, CKPT keys per thread.  A block among the
+// pair's top k has fewer than k blocks of the pair ahead of it, so fewer
+// than k of its tile: it is among its tile's k best.  The tile writes only
+// those: their scores to `scores` and their block numbers to cand_idx
+// ([pair][tile][k], ascending; past the tile's blocks -inf and -1).
+template <bool UPDATE, bool SHARED, int CKPT>
 __global__ __launch_bounds__(kTileThreads) void k_score_tiles(AttnArgs a0, void *S,
                                                              double *scores, int nb_cap,
                                                              int tile_rows, uint64_t *ctrl_zero,
-                                                             int newest_only) {
+                                                             int newest_only, int32_t *cand_idx) {
     constexpr int NW = kTileThreads / 64;
     static_assert(NewestLds<NW>::kMaxBlock >= 128, "every block size");
+    static_assert(CKPT * kTileThreads <= kTileCandRows || CKPT == 0, "tile scores in LDS");
     __shared__ NewestLds<NW> nl;
     const int pair = blockIdx.y;
     // the pair's arrival word for the next kernel's in-kernel combine starts
@@ -53,6 +95,37 @@ __global__ __launch_bounds__(kTileThreads) void k_score_tiles(AttnArgs a0, void 
     if (ctrl_zero && blockIdx.x == 0 && threadIdx.x == 0) ctrl_zero[pair] = 0ull;
     const AttnArgs a = for_pair(a0, pair);  // this sequence's own length
     const int nb = a.nb;
+    if constexpr (CKPT > 0) {
+        __shared__ double tsc[kTileCandRows];
+        __shared__ SelectLds<CKPT, kTileThreads> sl;
+        __shared__ int32_t tsel[kStepIdxCap];
+        const int k = a.k;
+        const int j_beg = blockIdx.x * tile_rows;  // every tile holds blocks
+        const int j_end = min(nb, j_beg + tile_rows);
+        select_clear(sl);
+        if (threadIdx.x == 0) nl.ready = 0u;
+        __syncthreads();
+        auto emit = [&](int j, double v) {
+            tsc[j - j_beg] = v;
+            select_count(sl, v);
+        };
+        if (UPDATE && j_end == nb)
+            score_blocks<NW, true, decltype(emit), false, SHARED>(a, S, nb_cap, pair, j_beg, nb,
+                                                                  nl, emit);
+        else
+            score_blocks<NW, false, decltype(emit), false, SHARED>(a, S, nb_cap, pair, j_beg,
+                                                                   j_end, nl, emit);
+        __syncthreads();
+        select_topk<CKPT, kTileThreads, true>(tsc, j_end - j_beg, k, tsel, sl);
+        __syncthreads();
+        const size_t c0 = ((size_t)pair * gridDim.x + blockIdx.x) * k;
+        for (int i = threadIdx.x; i < k; i += kTileThreads) {
+            const int l = tsel[i];
+            scores[c0 + i] = l >= 0 ? tsc[l] : -__builtin_huge_val();
+            cand_idx[c0 + i] = l >= 0 ? j_beg + l : -1;
+        }
+        return;
+    }
     // newest_only: every block is kept and no scores are wanted, so only the
     // newest block's summary is rebuilt (by tile 0)
     const int j_beg = newest_only ? (blockIdx.x == 0 ? nb - 1 : nb) : blockIdx.x * tile_rows;
@@ -73,7 +146,8 @@ __global__ __launch_bounds__(kTileThreads) void k_score_tiles(AttnArgs a0, void 
 
 static hipError_t launch_tiles(const Geo &g, bool update, const void *q, const void *K, void *S,
                                double *scores, int num_cu, hipStream_t s, bool newest_only,
-                               uint64_t *ctrl_zero) {
+                               uint64_t *ctrl_zero, const TileCands *tc, int32_t *cand_idx,
+                               int k) {
     AttnArgs a{};
     a.q = q;
     a.K = K;
@@ -84,7 +158,7 @@ static hipError_t launch_tiles(const Geo &g, bool update, const void *q, const v
     a.block = g.block;
     a.block_shift = __builtin_ctz((unsigned)g.block);
     a.nb = g.nb;
-    a.k = 1;  // unused here (for_pair's chunk count)
+    a.k = tc ? k : 1;  // the tiles' own selection (else unused)
     a.ctx_lens = g.ctx_lens;
     a.Sp = g.Sp;
     a.share_n = g.share_n;
@@ -94,22 +168,38 @@ static hipError_t launch_tiles(const Geo &g, bool update, const void *q, const v
     a.page_shift = g.page_shift;
     a.max_pages = g.max_pages;
     a.num_pages = g.num_pages;
-    constexpr int kRows = (kTileThreads / 64) * kScoreBatch;  // one round of the 8 waves
-    const int cu = num_cu > 0 ? num_cu : 256;
-    const int tiles = g.pairs >= cu ? 1 : (cu + g.pairs - 1) / g.pairs;
-    int rows = (g.nb + tiles - 1) / tiles;
-    rows = (rows + kRows - 1) / kRows * kRows;
-    const dim3 grid(newest_only ? 1 : (g.nb + rows - 1) / rows, g.pairs);
+    int tiles, rows;
+    tile_geometry(g, num_cu, tiles, rows);
+    const dim3 grid(newest_only ? 1 : tiles, g.pairs);
     const int no = newest_only ? 1 : 0;
-    if (update && g.share_n)
-        k_score_tiles<true, true><<<grid, kTileThreads, 0, s>>>(a, S, scores, g.nb_cap, rows,
-                                                                ctrl_zero, no);
-    else if (update)
-        k_score_tiles<true, false><<<grid, kTileThreads, 0, s>>>(a, S, scores, g.nb_cap, rows,
-                                                                 ctrl_zero, no);
-    else
-        k_score_tiles<false, false><<<grid, kTileThreads, 0, s>>>(a, S, scores, g.nb_cap, rows,
-                                                                  ctrl_zero, 0);
+    if (tc) {  // tile candidates: the first kernel of the decode step
+#define KIN_TILES_CAND(SH, C)                                                                  \
+    k_score_tiles<true, SH, C><<<grid, kTileThreads, 0, s>>>(a, S, scores, g.nb_cap, rows,     \
+                                                             ctrl_zero, 0, cand_idx)
+#define KIN_TILES_CAND_KPT(SH)                                                                 \
+    do {                                                                                       \
+        switch (select_kpt(rows, kTileThreads)) {                                              \
+        case 1: KIN_TILES_CAND(SH, 1); break;                                                  \
+        case 2: KIN_TILES_CAND(SH, 2); break;                                                  \
+        default: KIN_TILES_CAND(SH, 4); break;                                                 \
+        }                                                                                      \
+    } while (0)
+        if (g.share_n)
+            KIN_TILES_CAND_KPT(true);
+        else
+            KIN_TILES_CAND_KPT(false);
+#undef KIN_TILES_CAND_KPT
+#undef KIN_TILES_CAND
+    } else if (update && g.share_n) {
+        k_score_tiles<true, true, 0><<<grid, kTileThreads, 0, s>>>(a, S, scores, g.nb_cap, rows,
+                                                                   ctrl_zero, no, nullptr);
+    } else if (update) {
+        k_score_tiles<true, false, 0><<<grid, kTileThreads, 0, s>>>(a, S, scores, g.nb_cap, rows,
+                                                                    ctrl_zero, no, nullptr);
+    } else {
+        k_score_tiles<false, false, 0><<<grid, kTileThreads, 0, s>>>(a, S, scores, g.nb_cap,
+                                                                     rows, ctrl_zero, 0, nullptr);
+    }
     return hipGetLastError();
 }
 
@@ -212,15 +302,17 @@ hipError_t launch_block_score(const Geo &g, const void *q, const void *S, double
                               int num_cu, hipStream_t s) {
     void *Sm = const_cast<void *>(S);  // not written without UPDATE
     return g.dtype == KIN_BF16
-               ? launch_tiles(g, false, q, nullptr, Sm, scores, num_cu, s, false, nullptr)
-                               : launch_dt<KIN_F32, false>(g, q, nullptr, Sm, scores, s, nullptr);
+               ? launch_tiles(g, false, q, nullptr, Sm, scores, num_cu, s, false, nullptr,
+                              nullptr, nullptr, 0)
+               : launch_dt<KIN_F32, false>(g, q, nullptr, Sm, scores, s, nullptr);
 }
 
 hipError_t launch_update_and_score(const Geo &g, const void *q, const void *K, void *S,
                                    double *scores, int num_cu, hipStream_t s, bool newest_only,
-                                   uint64_t *ctrl_zero) {
+                                   uint64_t *ctrl_zero, const TileCands *tc, int32_t *cand_idx,
+                                   int k) {
     return g.dtype == KIN_BF16 ? launch_tiles(g, true, q, K, S, scores, num_cu, s, newest_only,
-                                              ctrl_zero)
+                                              ctrl_zero, tc, cand_idx, k)
                                : launch_dt<KIN_F32, true>(g, q, K, S, scores, s, ctrl_zero);
 }
 

@@ -63,6 +63,7 @@ BLOCK = [
     ("graph-one-kernel", 64, 16, 4, 2000, 16, 20, "bf16", 2048, False),   # 256 pairs
     ("graph-two-kernel", 3, 16, 2, 5000, 16, 100, "bf16", 5120, True),
     ("graph-two-kernel-nosc", 1, 8, 2, 40000, 32, 64, "bf16", 40000, False),  # scores in ws
+    ("graph-two-kernel-cand", 2, 16, 4, 100000, 16, 120, "bf16", 100096, False),  # tile candidates
     ("graph-keepall", 2, 16, 4, 2000, 16, 125, "bf16", 2048, False),       # one launch, splits
     ("graph-f32-split", 3, 2, 2, 4730, 16, 292, "f32", 4793, True),        # fp32 split step
     ("graph-f32-one", 1, 8, 2, 4096, 16, 32, "f32", 4096, False),          # fp32 one kernel

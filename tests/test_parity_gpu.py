@@ -136,6 +136,10 @@ FEW_PAIRS = [
     ("few-g8-b64-k1", 2, 64, 8, 3000, 64, 1, "bf16", 3072),         # one split
     ("few-g5-b32-kpast", 4, 20, 4, 700, 32, 40, "bf16", 704),       # k > nb
     ("few-g1-b16-nb8192", 1, 2, 2, 131072, 16, 512, "bf16", 131072),
+    # more than 4096 blocks per pair, k below a tile's length: the score
+    # tiles hand over their own k best (a tail tile shorter than k pads)
+    ("few-g4-b16-cand", 2, 16, 4, 100000, 16, 120, "bf16", 100096),
+    ("few-g2-b32-cand-ragged", 4, 8, 4, 150000, 32, 200, "bf16", 150016),
     ("few-g16-b128", 2, 64, 4, 20000, 128, 10, "bf16", 20096),
 ]
 
@@ -469,12 +473,16 @@ TIES = [
     ("ties-one-kernel-nb2048", 32, 8, 4, 32768, 16, 64, [1.0] * 6, True),
     ("ties-few-pairs", 2, 4, 8, 8192, 16, 100, [1.0] * 5, True),
     ("ties-few-pairs-nb8192", 1, 2, 4, 131072, 16, 300, [1.0] * 5, True),
+    # the score tiles' own candidates (6250 blocks per pair, 25 tiles)
+    ("ties-few-pairs-cand", 2, 4, 8, 100000, 16, 120, [1.0] * 5, True),
     # exponents far apart (scores spread over ~400 binades of both signs)
     ("wide-one-kernel-8w", 32, 8, 4, 4096, 16, 40, [2.0**-100, 2.0**-40, 1.0, 2.0**40, 2.0**100],
      False),
     ("wide-one-kernel-4w", 64, 8, 5, 2048, 32, 20, [2.0**-90, 1.0, 2.0**90], False),
     ("wide-few-pairs", 2, 4, 8, 8192, 16, 100, [2.0**-100, 2.0**-40, 1.0, 2.0**40, 2.0**100],
      False),
+    ("wide-few-pairs-cand", 2, 4, 8, 100000, 16, 120,
+     [2.0**-100, 2.0**-40, 1.0, 2.0**40, 2.0**100], False),
 ]
 
 

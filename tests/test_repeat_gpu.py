@@ -49,6 +49,7 @@ BLOCK = [
     ("rep-two-kernel", 3, 16, 2, 5000, 16, 100, "bf16", 5120, True),     # kernel 1 clears words
     ("rep-two-kernel-nosc", 3, 16, 2, 5000, 16, 100, "bf16", 5120, False),
     ("rep-two-kernel-one-split", 2, 64, 8, 3000, 64, 1, "bf16", 3072, False),  # one split per pair
+    ("rep-two-kernel-cand", 2, 16, 4, 100000, 16, 120, "bf16", 100096, False),  # tile candidates
     ("rep-keepall", 2, 16, 4, 2000, 16, 125, "bf16", 2048, False),       # one launch
     ("rep-f32-split", 3, 2, 2, 4730, 16, 292, "f32", 4793, True),        # fp32 kernel 1 clears
     ("rep-f32-one", 1, 8, 2, 4096, 16, 32, "f32", 4096, False),          # fp32 one kernel, splits
