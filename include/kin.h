@@ -209,12 +209,15 @@ KIN_API kin_status kin_decode_select_attend(const kin_desc *desc, const void *q,
  * updated in place; scores and idx receive the step's intermediate
  * results.  scores may be NULL: the scores are then not written (the
  * single-kernel form keeps them in LDS; the two-kernel form keeps them in
- * ws, which must then hold kin_sparse_ws_bytes(desc, k) bytes).  With bf16 data and at least as many (sequence, KV head) pairs
- * as the device has compute units it is ONE kernel (a workgroup per pair
- * runs all four steps, the scores never leave LDS before the selection);
- * otherwise it is kin_decode_update_score then kin_decode_select_attend
- * (two kernels, plus a combine pass when a pair's kept blocks are split
- * over several workgroups). */
+ * ws, which must then hold kin_sparse_ws_bytes(desc, k) bytes, or, with
+ * more than 4096 blocks per pair and one length for every sequence, keeps
+ * there only each score tile's own k best blocks, a superset of the
+ * pair's top k).  With bf16 data and at least as many (sequence, KV head)
+ * pairs as the device has compute units it is ONE kernel (a workgroup per
+ * pair runs all four steps, the scores never leave LDS before the
+ * selection); otherwise it is kin_decode_update_score then
+ * kin_decode_select_attend (two kernels, plus a combine pass when a pair's
+ * kept blocks are split over several workgroups). */
 KIN_API kin_status kin_sparse_decode_step(const kin_desc *desc, const void *q, const void *K,
                                   const void *V, void *S, double *scores, int32_t k,
                                   int32_t *idx, void *out, void *ws, size_t ws_bytes,
