@@ -215,9 +215,10 @@ KIN_API kin_status kin_decode_select_attend(const kin_desc *desc, const void *q,
  * pair's top k).  With bf16 data and at least as many (sequence, KV head)
  * pairs as the device has compute units it is ONE kernel (a workgroup per
  * pair runs all four steps, the scores never leave LDS before the
- * selection); otherwise it is kin_decode_update_score then
- * kin_decode_select_attend (two kernels, plus a combine pass when a pair's
- * kept blocks are split over several workgroups). */
+ * selection); otherwise it is two kernels, those of kin_decode_update_score
+ * then kin_decode_select_attend (handing over the tiles' candidates instead
+ * of every score when it does), plus a combine pass when a pair's kept
+ * blocks are split over several workgroups. */
 KIN_API kin_status kin_sparse_decode_step(const kin_desc *desc, const void *q, const void *K,
                                   const void *V, void *S, double *scores, int32_t k,
                                   int32_t *idx, void *out, void *ws, size_t ws_bytes,
